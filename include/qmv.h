@@ -1,0 +1,191 @@
+/*
+ * qmv.h -- C ABI of libqmv: quantized matrix-vector products (MMVQ) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Weights are K-quant blocks (Q6_K, Q4_K, Q5_K), the
+ * activations are Q8_1 blocks, and for every activation column n and weight
+ * row r
+ *     out[n][r] = sum over 32-weight sub-blocks b of
+ *                 d_w * scale * d_a(n, b) * (integer dot of the unpacked
+ *                 weight quants of sub-block b with the Q8_1 quants)
+ * (minus the Q4_K/Q5_K min term), the per-sub-block value of PR #1774
+ * ("sycl opt-in: STRATA_IQ3S_WIDE=1, a wide mmvq kernel for the dense IQ3_S
+ * matrices", section "What changed"), for 1 to 8 activation columns with the
+ * weights read once for all columns (PR #2207, "Issue: #1545, #1606 (Arc
+ * A-series decode)", section "Summary").  Integer dots are exact int32; the
+ * scaling and accumulation are fp32, so results agree with the exact value to
+ * within fp32 rounding of a sum whose order differs from any other
+ * implementation's (PR #1774, "What changed", notes the same for its kernel).
+ *
+ * Block formats (little-endian; the pages name the GGUF-layout blocks, PR
+ * #2340 "sycl mmvq: Q6_K decode kernels no longer ALU-bound; Q6_K output
+ * heads as aligned planes; int4 activation loads", section "What it
+ * changes"; the bit layout is the GGUF K-quant convention):
+ *   Q6_K, 210 B per 256 weights: ql[128] @0, qh[64] @128, int8 scales[16]
+ *     @192, fp16 d @208.  Weight i: h = i/128, c = (i%128)/32, l = i%32,
+ *     q6 = ((ql[64h+32(c%2)+l] >> 4(c/2)) & 15) | ((qh[32h+l] >> 2c) & 3) << 4,
+ *     w = d * scales[i/16] * (q6 - 32).
+ *   Q4_K, 144 B: fp16 d @0, fp16 dmin @2, scales[12] @4, qs[128] @16.
+ *     Sub-block j = i/32: q4 = (qs[32(j/2)+i%32] >> 4(j%2)) & 15,
+ *     w = d*sc_j*q4 - dmin*m_j with 6-bit sc_j, m_j packed in scales[12]
+ *     (j<4: low six bits of bytes j and j+4; j>=4: the nibbles of byte j+4
+ *     joined with the top two bits of bytes j-4 and j).
+ *   Q5_K, 176 B: as Q4_K with qh[32] @16 and qs[128] @48;
+ *     q5 = q4 | ((qh[i%32] >> j) & 1) << 4.
+ *   Q8_1, 36 B per 32 values: fp16 d @0, fp16 s @2, int8 q[32] @4.
+ *   A matrix of R rows and K columns is R*K/256 blocks, row-major (row r
+ *   holds blocks r*K/256 .. (r+1)*K/256-1).  A Q8_1 activation of ncols
+ *   columns is [ncols][K/32] blocks.  Outputs are fp32 [ncols][R].
+ *
+ * Planar Q6_K layout (QMV_LAYOUT_PLANAR), produced by repack_q6k_planar: the
+ * same number of bytes as the GGUF matrix, split into planes whose every
+ * lane-load is an aligned 16-byte load (the load-time conversion of PR #2340,
+ * "What it changes").  With NB = R*K/256 blocks, block t = r*(K/256) + s,
+ * v_i = (q6_i - 32) mod 64 for weight i of the block:
+ *   plane A at byte 0, 128 B per block, 16 B per sub-block j (0..7):
+ *     byte k (0..15) = v[32j+k] << 2 | spare_A(k);
+ *   plane B at byte 128*NB, 64 B per block, 8 B per sub-block:
+ *     byte k (0..7) = v[32j+16+k] << 2 | spare_B(k);
+ *   the two spare bits of every byte hold weights 32j+24 .. 32j+31: for
+ *     k = 0..3, weight 32j+24+k keeps bits 0-1 of v in spare_A(k), bits 2-3
+ *     in spare_A(4+k), bits 4-5 in spare_A(8+k); weight 32j+28+k keeps bits
+ *     0-1 in spare_A(12+k), bits 2-3 in spare_B(k), bits 4-5 in spare_B(4+k);
+ *   plane SC at byte 192*NB, 16 B per block: the int8 scales, unchanged;
+ *   plane D at byte 208*NB, 2 B per block: fp16 d, unchanged.
+ * Read as int8, a plane byte with its spare bits cleared is 4*(q6-32), so the
+ * six-bit offset costs no instruction.  Planar and GGUF inputs give
+ * bit-identical outputs.
+ *
+ * Conventions for every entry point.
+ *   Memory: all data pointers are device pointers owned by the caller; the
+ *   library never allocates, frees or synchronizes.  `stream` is a
+ *   hipStream_t (NULL: the default stream).  Work is enqueued on `stream` and
+ *   returns at once; calls are safe to capture in a HIP graph and are
+ *   thread-safe across streams.  Outputs are overwritten, never accumulated.
+ *   Errors: 0 on success, a negative QMV_ERR_* code otherwise.  Every argument
+ *   check runs on the host before any HIP call, so a rejected call has no
+ *   effect.  QMV_ERR_HIP means a launch failed; qmv_last_hip_error() returns
+ *   the hipError_t of that failure (per calling thread).
+ *   Preconditions the host cannot check: buffers are as large as stated and
+ *   do not overlap outputs; activations are finite.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    QMV_OK = 0,
+    QMV_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size */
+    QMV_ERR_UNSUPPORTED = -2,   /* K % 256 != 0, ncols not in 1..8, bad layout, too large */
+    QMV_ERR_ALIGNMENT = -3,     /* a pointer below its required alignment */
+    QMV_ERR_WORKSPACE = -4,     /* workspace missing or too small */
+    QMV_ERR_HIP = -5            /* a HIP launch failed */
+};
+
+enum { QMV_LAYOUT_GGUF = 0, QMV_LAYOUT_PLANAR = 1 };
+
+/* Largest supported sizes: rows <= 2^31-1, K <= 2^20, and every weight,
+ * activation and output buffer below 2^40 bytes. */
+
+/* Quantize fp32 activations to Q8_1 (PR #2340 "What it changes" names the
+ * Q8_1 activation quants).  Per block of 32 values of one column:
+ * amax = max|x|, d = amax/127 (fp32 division), q = round-half-away-from-zero
+ * of x/d (fp32 division; all zero when d == 0), stored d = fp16(d) and
+ * s = fp16(d * sum q), both rounded to nearest even.
+ * x: fp32 [ncols][K], 4-byte aligned.  xq: [ncols][K/32] blocks of 36 B,
+ * 4-byte aligned.  K % 32 == 0, 1 <= ncols <= 65535. */
+int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream);
+
+/* Q6_K weights x Q8_1 activations (the Q6_K dense decode product of PR
+ * #2340 "What it changes" and PR #2207 "How it was checked").
+ * w: rows x K Q6_K matrix in `layout` (QMV_LAYOUT_GGUF: 210-byte blocks,
+ * 4-byte aligned; QMV_LAYOUT_PLANAR: the planar layout above, 16-byte
+ * aligned).  xq: Q8_1 [ncols][K/32], 4-byte aligned.  out: fp32
+ * [ncols][rows], 4-byte aligned.  K % 256 == 0, 1 <= ncols <= 8. */
+int mmvq_q6k(const void *w, int layout, const void *xq, float *out,
+             int64_t rows, int64_t K, int ncols, void *stream);
+
+/* Q4_K / Q5_K weights (GGUF blocks, 16-byte aligned; 144 and 176 B blocks
+ * keep every field aligned, so no planar form is needed) x Q8_1 activations
+ * (PR #2340 "What it changes" and PR #2207 "How it was checked" measure
+ * these types).  The min term uses the exact integer sum of each Q8_1
+ * block's quants.  Arguments as for mmvq_q6k. */
+int mmvq_q4k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
+             int ncols, void *stream);
+int mmvq_q5k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
+             int ncols, void *stream);
+
+/* Load-time conversion of a GGUF Q6_K matrix into the planar layout above
+ * (PR #2340 "What it changes").  Out of place; src (2-byte aligned) and dst
+ * (16-byte aligned) are rows*K/256*210 bytes and must not overlap.  The
+ * caller may free src afterwards. */
+int repack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
+/* Inverse conversion, planar -> GGUF (for tests and for exporting). */
+int unpack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
+
+/* Per-sub-block integer sums of the same kernels (for verification):
+ * isums int32 [ncols][rows][K/32].  Q6_K: sum over the sub-block's two
+ * 16-weight groups of scale * sum (q6-32)*q8.  Q4_K/Q5_K: sum q*q8 of the
+ * sub-block, unscaled.  Same arguments and checks as the products. */
+int mmvq_q6k_isums(const void *w, int layout, const void *xq, int32_t *isums,
+                   int64_t rows, int64_t K, int ncols, void *stream);
+int mmvq_q4k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows,
+                   int64_t K, int ncols, void *stream);
+int mmvq_q5k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows,
+                   int64_t K, int ncols, void *stream);
+
+/* Grouped MoE-expert product over a window of T routed tokens (the
+ * routed-expert gate/up and down kernels of issue #2801 "[Feature]: SYCL:
+ * cheaper IQ weight decodes in the grouped expert kernels"; the token windows
+ * and empty expert groups of PR #2746 "B70 validation").  For every token t
+ * and slot k (slot = t*topk + k), e = ids[t][k]:
+ *   g = gate_e . xq_t, u = up_e . xq_t           (Q4_K MMVQ, d_ff rows)
+ *   h = silu(g) * u, silu(g) = g / (1 + exp(-g))  (fp32)
+ *   hq = quantize_q8_1(h)                         (d_ff/32 blocks)
+ *   y = down_e . hq                               (Q6_K MMVQ, d_model rows)
+ *   out[t] = sum over k = 0..topk-1, in that order, of route_w[t][k] * y.
+ * Each expert's weights are read once for all tokens routed to it; experts
+ * with no token are not read.
+ *   w_gate, w_up: Q4_K [E][d_ff][d_model/256] blocks, 16-byte aligned.
+ *   w_down: Q6_K [E][d_model][d_ff/256] in down_layout (GGUF: 4-byte
+ *     aligned; planar: 16-byte aligned, the repack_q6k_planar of the whole
+ *     tensor taken as E*d_model rows).
+ *   xq: Q8_1 [T][d_model/32] (4-byte aligned); ids: int32 [T][topk] in
+ *   [0, E), distinct within a token; route_w: fp32 [T][topk];
+ *   out: fp32 [T][d_model], overwritten.
+ *   1 <= T <= 8, 1 <= topk <= 8, d_model and d_ff multiples of 256.
+ *   ws: device workspace of at least grouped_expert_mmvq_workspace() bytes,
+ *   256-byte aligned.  Layout (all offsets from ws, S = T*topk):
+ *     int32 hdr[64]: hdr[0] = number of distinct experts hit, hdr[1] = number
+ *       of ids outside [0, E) (such slots contribute nothing);
+ *     int32 expert[S], count[S], first[S] @256: per hit expert (ascending id)
+ *       its id, its number of slots and its first position in slot_list;
+ *     int32 slot_list[S] @256+12*S: slots grouped by expert, ascending slot
+ *       order inside a group;
+ *     fp32 h[S][d_ff] @H = align256(256+16*S);
+ *     Q8_1 hq[S][d_ff/32] @HQ = align256(H + 4*S*d_ff);
+ *     fp32 y[S][d_model] @Y = align256(HQ + 36*S*d_ff/32).
+ *   The workspace is overwritten; ids that repeat within a token are handled
+ *   (their slots are processed like any other) but break the "read once"
+ *   property. */
+int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down,
+                        int down_layout, const void *xq, const int32_t *ids,
+                        const float *route_w, float *out, int E, int T, int topk,
+                        int64_t d_model, int64_t d_ff, void *ws, size_t ws_bytes,
+                        void *stream);
+size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff);
+
+/* Diagnostics. */
+const char *qmv_strerror(int code);
+int qmv_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMV_H */

@@ -1,0 +1,197 @@
+// api.hip -- the C ABI of libqmv (declared in include/qmv.h): argument
+// checks on the host, then the launches.  No entry point allocates, frees or
+// synchronizes; every check runs before the first HIP call.
+#include <stdint.h>
+
+#include "../../include/qmv.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxRows = 2147483647LL;
+constexpr int64_t kMaxK = 1LL << 20;
+constexpr int64_t kMaxBytes = 1LL << 40;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int from_hip(hipError_t e) {
+    if (e == hipSuccess) return QMV_OK;
+    g_last_hip_error = (int)e;
+    return QMV_ERR_HIP;
+}
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Checks shared by the MMVQ entry points.
+int check_mmvq(const void *w, const void *xq, const void *out, int64_t rows, int64_t K, int ncols,
+               int64_t block_bytes, uintptr_t w_align) {
+    if (!w || !xq || !out) return QMV_ERR_INVALID_ARG;
+    if (rows <= 0 || K <= 0) return QMV_ERR_INVALID_ARG;
+    if (K % 256 != 0 || K > kMaxK || rows > kMaxRows) return QMV_ERR_UNSUPPORTED;
+    if (ncols < 1 || ncols > 8) return QMV_ERR_UNSUPPORTED;
+    if (rows * (K / 256) * block_bytes >= kMaxBytes || rows * ncols * 4 >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(w, w_align) || !aligned(xq, 4) || !aligned(out, 4)) return QMV_ERR_ALIGNMENT;
+    return QMV_OK;
+}
+
+int q6_dispatch(const void *w, int layout, const void *xq, float *out, int32_t *dump, int64_t rows,
+                int64_t K, int ncols, void *stream) {
+    if (layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR) {
+        if (!w || !xq || !(out || dump)) return QMV_ERR_INVALID_ARG;
+        return QMV_ERR_UNSUPPORTED;
+    }
+    const void *o = out ? static_cast<const void *>(out) : static_cast<const void *>(dump);
+    int rc = check_mmvq(w, xq, o, rows, K, ncols, 210, layout == QMV_LAYOUT_PLANAR ? 16 : 4);
+    if (rc) return rc;
+    hipError_t e = layout == QMV_LAYOUT_PLANAR
+                       ? qmv::launch_mmvq_q6_planar(w, xq, out, dump, rows, K, ncols, as_stream(stream))
+                       : qmv::launch_mmvq_q6_gguf(w, xq, out, dump, rows, K, ncols, as_stream(stream));
+    return from_hip(e);
+}
+
+int q45_dispatch(bool five, const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                 int ncols, void *stream) {
+    const void *o = out ? static_cast<const void *>(out) : static_cast<const void *>(dump);
+    int rc = check_mmvq(w, xq, o, rows, K, ncols, five ? 176 : 144, 16);
+    if (rc) return rc;
+    hipError_t e = five ? qmv::launch_mmvq_q5(w, xq, out, dump, rows, K, ncols, as_stream(stream))
+                        : qmv::launch_mmvq_q4(w, xq, out, dump, rows, K, ncols, as_stream(stream));
+    return from_hip(e);
+}
+
+int check_repack(const void *src, const void *dst, int64_t rows, int64_t K, uintptr_t src_align,
+                 uintptr_t dst_align) {
+    if (!src || !dst) return QMV_ERR_INVALID_ARG;
+    if (rows <= 0 || K <= 0) return QMV_ERR_INVALID_ARG;
+    if (K % 256 != 0 || K > kMaxK || rows > kMaxRows) return QMV_ERR_UNSUPPORTED;
+    const int64_t bytes = rows * (K / 256) * 210;
+    if (bytes >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(src, src_align) || !aligned(dst, dst_align)) return QMV_ERR_ALIGNMENT;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    if (s < d + (uintptr_t)bytes && d < s + (uintptr_t)bytes) return QMV_ERR_INVALID_ARG;   // overlap
+    return QMV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream) {
+    if (!x || !xq) return QMV_ERR_INVALID_ARG;
+    if (K <= 0 || ncols <= 0) return QMV_ERR_INVALID_ARG;
+    if (K % 32 != 0 || K > kMaxK || ncols > 65535) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(x, 4) || !aligned(xq, 4)) return QMV_ERR_ALIGNMENT;
+    return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, as_stream(stream)));
+}
+
+int mmvq_q6k(const void *w, int layout, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
+             void *stream) {
+    if (!out) return QMV_ERR_INVALID_ARG;
+    return q6_dispatch(w, layout, xq, out, nullptr, rows, K, ncols, stream);
+}
+
+int mmvq_q4k(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols, void *stream) {
+    if (!out) return QMV_ERR_INVALID_ARG;
+    return q45_dispatch(false, w, xq, out, nullptr, rows, K, ncols, stream);
+}
+
+int mmvq_q5k(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols, void *stream) {
+    if (!out) return QMV_ERR_INVALID_ARG;
+    return q45_dispatch(true, w, xq, out, nullptr, rows, K, ncols, stream);
+}
+
+int mmvq_q6k_isums(const void *w, int layout, const void *xq, int32_t *isums, int64_t rows, int64_t K,
+                   int ncols, void *stream) {
+    if (!isums) return QMV_ERR_INVALID_ARG;
+    return q6_dispatch(w, layout, xq, nullptr, isums, rows, K, ncols, stream);
+}
+
+int mmvq_q4k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows, int64_t K, int ncols,
+                   void *stream) {
+    if (!isums) return QMV_ERR_INVALID_ARG;
+    return q45_dispatch(false, w, xq, nullptr, isums, rows, K, ncols, stream);
+}
+
+int mmvq_q5k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows, int64_t K, int ncols,
+                   void *stream) {
+    if (!isums) return QMV_ERR_INVALID_ARG;
+    return q45_dispatch(true, w, xq, nullptr, isums, rows, K, ncols, stream);
+}
+
+int repack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream) {
+    int rc = check_repack(src, dst, rows, K, 2, 16);
+    if (rc) return rc;
+    return from_hip(qmv::launch_repack(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst),
+                                       rows * (K / 256), as_stream(stream)));
+}
+
+int unpack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream) {
+    int rc = check_repack(src, dst, rows, K, 16, 2);
+    if (rc) return rc;
+    return from_hip(qmv::launch_unpack(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst),
+                                       rows * (K / 256), as_stream(stream)));
+}
+
+size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff) {
+    if (E < 1 || T < 1 || T > 8 || topk < 1 || topk > 8 || d_model < 256 || d_ff < 256 || d_model % 256 ||
+        d_ff % 256 || d_model > kMaxK || d_ff > kMaxK)
+        return 0;
+    return (size_t)qmv::moe_layout(T, topk, d_model, d_ff).total;
+}
+
+int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down, int down_layout,
+                        const void *xq, const int32_t *ids, const float *route_w, float *out, int E, int T,
+                        int topk, int64_t d_model, int64_t d_ff, void *ws, size_t ws_bytes, void *stream) {
+    if (!w_gate || !w_up || !w_down || !xq || !ids || !route_w || !out) return QMV_ERR_INVALID_ARG;
+    if (E < 1 || T < 1 || topk < 1 || d_model <= 0 || d_ff <= 0) return QMV_ERR_INVALID_ARG;
+    if (T > 8 || topk > 8 || d_model % 256 || d_ff % 256 || d_model > kMaxK || d_ff > kMaxK)
+        return QMV_ERR_UNSUPPORTED;
+    if (down_layout != QMV_LAYOUT_GGUF && down_layout != QMV_LAYOUT_PLANAR) return QMV_ERR_UNSUPPORTED;
+    const int64_t gu_bytes = (int64_t)E * d_ff * (d_model / 256) * 144;
+    const int64_t dn_bytes = (int64_t)E * d_model * (d_ff / 256) * 210;
+    if (gu_bytes >= kMaxBytes || dn_bytes >= kMaxBytes || (int64_t)E * d_model > kMaxRows)
+        return QMV_ERR_UNSUPPORTED;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, down_layout == QMV_LAYOUT_PLANAR ? 16 : 4) ||
+        !aligned(xq, 4) || !aligned(ids, 4) || !aligned(route_w, 4) || !aligned(out, 4))
+        return QMV_ERR_ALIGNMENT;
+    const qmv::MoeLayout L = qmv::moe_layout(T, topk, d_model, d_ff);
+    if (!ws || ws_bytes < (size_t)L.total) return QMV_ERR_WORKSPACE;
+    if (!aligned(ws, 256)) return QMV_ERR_ALIGNMENT;
+    qmv::MoeArgs m;
+    m.w_gate = reinterpret_cast<const uint8_t *>(w_gate);
+    m.w_up = reinterpret_cast<const uint8_t *>(w_up);
+    m.w_down = reinterpret_cast<const uint8_t *>(w_down);
+    m.xq = reinterpret_cast<const uint8_t *>(xq);
+    m.ids = ids;
+    m.route_w = route_w;
+    m.out = out;
+    m.ws = reinterpret_cast<uint8_t *>(ws);
+    m.E = E;
+    m.T = T;
+    m.topk = topk;
+    m.S = T * topk;
+    m.d_model = d_model;
+    m.d_ff = d_ff;
+    m.off_h = L.off_h;
+    m.off_hq = L.off_hq;
+    m.off_y = L.off_y;
+    return from_hip(qmv::launch_moe(m, down_layout, as_stream(stream)));
+}
+
+const char *qmv_strerror(int code) {
+    switch (code) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or overlapping buffers)";
+    case QMV_ERR_UNSUPPORTED: return "unsupported shape or option (K % 256, ncols 1..8, T/topk 1..8, layout, size)";
+    case QMV_ERR_ALIGNMENT: return "pointer below its required alignment";
+    case QMV_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMV_ERR_HIP: return "HIP launch failed (see qmv_last_hip_error)";
+    default: return "unknown error code";
+    }
+}
+
+int qmv_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,564 @@
+// device.hpp -- gfx950 device building blocks of libqmv: integer dot
+// products, fp16 decode, wave64 DPP reductions, the K-quant block loaders and
+// the MMVQ kernel template shared by the dense and grouped products.
+//
+// Work mapping (a design for CDNA4 wave64, not the 32-lane sub-group
+// mapping of the SYCL kernels on the pages):
+//   * a "unit" is the piece of a weight row one lane handles per step:
+//     one 32-weight sub-block for Q6_K, a pair of sub-blocks (one 32-byte
+//     qs chunk) for Q4_K/Q5_K;
+//   * U lanes (8, 16, 32 or 64; a function of K only) share a row; lane u
+//     of the group takes units u, u+U, u+2U, ...; a wave holds 64/U rows;
+//   * a lane keeps N fp32 accumulators (one per activation column), so the
+//     weights are read once for all N columns;
+//   * the Q8_1 activation tile is staged once per workgroup in LDS and read
+//     by every row of the workgroup;
+//   * the U partial sums of a row are combined by a fixed DPP butterfly, so
+//     results do not depend on N, on the weight layout or on the launch
+//     shape, only on K.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+constexpr int kWave = 64;
+constexpr int kQ6Bytes = 210, kQ4Bytes = 144, kQ5Bytes = 176, kQ81Bytes = 36;
+
+// ---------------------------------------------------------------- basics
+__device__ __forceinline__ int sdot4(int a, int b, int c) {
+    return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+__device__ __forceinline__ float half_to_float(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
+}
+
+__device__ __forceinline__ int sext8(uint32_t v, int byte) {
+    return __builtin_amdgcn_sbfe((int)v, 8 * byte, 8);
+}
+
+__device__ __forceinline__ uint32_t ubyte(uint32_t v, int byte) {
+    return __builtin_amdgcn_ubfe(v, 8 * byte, 8);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum of v over each aligned group of U lanes; every lane of a group ends
+// with the same bits (each step adds a lane's value to its partner's, and
+// fp32 addition is commutative).  All 64 lanes must be active.
+template <int U>
+__device__ __forceinline__ float group_sum(float v) {
+    v = dpp_add<0xB1>(v);                       // quad_perm [1,0,3,2]: lane ^ 1
+    v = dpp_add<0x4E>(v);                       // quad_perm [2,3,0,1]: lane ^ 2
+    v = dpp_add<0x141>(v);                      // row_half_mirror: i <-> 7-i
+    if constexpr (U >= 16) v = dpp_add<0x140>(v);   // row_mirror: i <-> 15-i
+    if constexpr (U >= 32) v += __shfl_xor(v, 16);
+    if constexpr (U >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Workgroup barrier that orders LDS only: weight loads still in flight are
+// not waited for.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// --------------------------------------------------------- LDS act tile
+// One staged Q8_1 block of one column: quants 0-15 and 16-31 in two
+// 16-byte arrays (conflict-free ds_read_b128 for consecutive blocks) and a
+// float pair: (d * dscale, d * sum(q)) where dscale is 1/4 for the Q6_K
+// 4x codes.
+struct ActTile {
+    uint4 *x0;
+    uint4 *x1;
+    float2 *f;
+    int nb;            // blocks per column in the tile
+};
+
+__device__ __forceinline__ ActTile act_tile(void *lds, int ncols, int nb) {
+    ActTile t;
+    t.x0 = reinterpret_cast<uint4 *>(lds);
+    t.x1 = t.x0 + ncols * nb;
+    t.f = reinterpret_cast<float2 *>(t.x1 + ncols * nb);
+    t.nb = nb;
+    return t;
+}
+
+constexpr int kActBytesPerBlock = 40;
+
+struct ActRaw {
+    uint32_t w[9];
+};
+
+__device__ __forceinline__ void act_load(ActRaw &r, const uint8_t *xq, int64_t blk) {
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(xq + blk * kQ81Bytes);
+#pragma unroll
+    for (int i = 0; i < 9; i++) r.w[i] = p[i];
+}
+
+__device__ __forceinline__ void act_store(const ActTile &t, int idx, const ActRaw &r, float dscale) {
+    uint4 a = make_uint4(r.w[1], r.w[2], r.w[3], r.w[4]);
+    uint4 b = make_uint4(r.w[5], r.w[6], r.w[7], r.w[8]);
+    float d = half_to_float(r.w[0]);
+    int s = 0;
+#pragma unroll
+    for (int i = 1; i < 9; i++) s = sdot4((int)r.w[i], 0x01010101, s);
+    t.x0[idx] = a;
+    t.x1[idx] = b;
+    t.f[idx] = make_float2(d * dscale, d * (float)s);
+}
+
+// ------------------------------------------------------- format policies
+// Each policy defines:
+//   SBPU     sub-blocks per unit;   IT  units held in registers per lane
+//   Raw      registers of one unit; load(); dot<N>() accumulating into acc[N]
+//   DSCALE   scale applied to d_a when staged.
+
+// Q6_K, planar layout (see qmv.h).  Codes are 4*(q6-32) as int8.
+struct Q6Planar {
+    static constexpr int SBPU = 1, IT = 5;
+    static constexpr float DSCALE = 0.25f;
+    struct Raw {
+        uint4 a;
+        uint2 b;
+        uint32_t sc, d;
+    };
+    const uint4 *A;
+    const uint2 *B;
+    const uint16_t *SC;
+    const uint16_t *D;
+    int64_t nsb;   // sub-blocks per row
+
+    __device__ __forceinline__ void init(const void *w, int64_t rows, int64_t K) {
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(w);
+        int64_t NB = rows * (K / 256);
+        A = reinterpret_cast<const uint4 *>(base);
+        B = reinterpret_cast<const uint2 *>(base + 128 * NB);
+        SC = reinterpret_cast<const uint16_t *>(base + 192 * NB);
+        D = reinterpret_cast<const uint16_t *>(base + 208 * NB);
+        nsb = K / 32;
+    }
+    __device__ __forceinline__ void load(Raw &r, int64_t row, int unit) const {
+        int64_t i = row * nsb + unit;
+        r.a = A[i];
+        r.b = B[i];
+        r.sc = SC[i];
+        r.d = D[i >> 3];
+    }
+    __device__ __forceinline__ static void codes(const Raw &r, int v[8]) {
+        const uint32_t m3 = 0x03030303u, mfc = 0xFCFCFCFCu;
+        v[0] = (int)(r.a.x & mfc);
+        v[1] = (int)(r.a.y & mfc);
+        v[2] = (int)(r.a.z & mfc);
+        v[3] = (int)(r.a.w & mfc);
+        v[4] = (int)(r.b.x & mfc);
+        v[5] = (int)(r.b.y & mfc);
+        v[6] = (int)(((r.a.z & m3) << 6) | ((r.a.y & m3) << 4) | ((r.a.x & m3) << 2));
+        v[7] = (int)(((r.b.y & m3) << 6) | ((r.b.x & m3) << 4) | ((r.a.w & m3) << 2));
+    }
+};
+
+// Q6_K, GGUF layout: 210-byte blocks, only 2-byte aligned; read as aligned
+// dwords and realigned with alignbit, then turned into the same 4x codes.
+struct Q6Gguf {
+    static constexpr int SBPU = 1, IT = 2;
+    static constexpr float DSCALE = 0.25f;
+    struct Raw {
+        uint32_t l[9], h[9];
+        uint32_t sc, d, shift;   // shift: bit 0-4 realign shift, 8-9: c
+    };
+    const uint8_t *W;
+    int64_t nbk;   // blocks per row
+
+    __device__ __forceinline__ void init(const void *w, int64_t, int64_t K) {
+        W = reinterpret_cast<const uint8_t *>(w);
+        nbk = K / 256;
+    }
+    __device__ __forceinline__ void load(Raw &r, int64_t row, int unit) const {
+        int j = unit & 7, h = j >> 2, c = j & 3;
+        const uint8_t *blk = W + (row * nbk + (unit >> 3)) * kQ6Bytes;
+        uintptr_t pl = reinterpret_cast<uintptr_t>(blk) + 64 * h + 32 * (c & 1);
+        uintptr_t ph = reinterpret_cast<uintptr_t>(blk) + 128 + 32 * h;
+        const uint32_t *al = reinterpret_cast<const uint32_t *>(pl & ~uintptr_t(3));
+        const uint32_t *ah = reinterpret_cast<const uint32_t *>(ph & ~uintptr_t(3));
+#pragma unroll
+        for (int i = 0; i < 9; i++) {
+            r.l[i] = al[i];
+            r.h[i] = ah[i];
+        }
+        r.sc = *reinterpret_cast<const uint16_t *>(blk + 192 + 2 * j);
+        r.d = *reinterpret_cast<const uint16_t *>(blk + 208);
+        r.shift = (uint32_t)((pl & 3) * 8) | ((uint32_t)c << 8);
+    }
+    __device__ __forceinline__ static void codes(const Raw &r, int v[8]) {
+        uint32_t sh = r.shift & 31, c = r.shift >> 8;
+        uint32_t nsh = 4 * (c >> 1), hsh = 2 * c;
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            uint32_t L = __builtin_amdgcn_alignbit(r.l[m + 1], r.l[m], sh);
+            uint32_t H = __builtin_amdgcn_alignbit(r.h[m + 1], r.h[m], sh);
+            uint32_t q6 = ((L >> nsh) & 0x0F0F0F0Fu) | (((H >> hsh) & 0x03030303u) << 4);
+            v[m] = (int)((q6 ^ 0x20202020u) << 2);
+        }
+    }
+};
+
+// Shared dot product of the two Q6_K layouts for one unit and N columns.
+template <class F, int N, bool DUMP>
+__device__ __forceinline__ void q6_dot(const typename F::Raw &r, const ActTile &t, int tb,
+                                       float acc[N], int32_t *dump, int64_t dstride) {
+    int v[8];
+    F::codes(r, v);
+    int sc0 = sext8(r.sc, 0), sc1 = sext8(r.sc, 1);
+    float dw = half_to_float(r.d);
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+        uint4 x0 = t.x0[n * t.nb + tb];
+        uint4 x1 = t.x1[n * t.nb + tb];
+        int d0 = sdot4(v[0], (int)x0.x, 0);
+        d0 = sdot4(v[1], (int)x0.y, d0);
+        d0 = sdot4(v[2], (int)x0.z, d0);
+        d0 = sdot4(v[3], (int)x0.w, d0);
+        int d1 = sdot4(v[4], (int)x1.x, 0);
+        d1 = sdot4(v[5], (int)x1.y, d1);
+        d1 = sdot4(v[6], (int)x1.z, d1);
+        d1 = sdot4(v[7], (int)x1.w, d1);
+        int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact (|operands| < 2^23)
+        if constexpr (DUMP) {
+            dump[n * dstride] = isum4 >> 2;
+        } else {
+            float da = t.f[n * t.nb + tb].x;           // d_a / 4
+            acc[n] = __builtin_fmaf(dw * da, (float)isum4, acc[n]);
+        }
+    }
+}
+
+// Q4_K / Q5_K (GGUF blocks, 16-byte aligned).  Unit = pair p of sub-blocks
+// (2p', 2p'+1) of superblock p/4, p' = p%4, i.e. the 32-byte qs chunk whose
+// low nibbles are sub-block 2p' and high nibbles sub-block 2p'+1.
+template <bool FIVE>
+struct Q45 {
+    static constexpr int SBPU = 2, IT = FIVE ? 3 : 4;
+    static constexpr float DSCALE = 1.0f;
+    static constexpr int BYTES = FIVE ? kQ5Bytes : kQ4Bytes;
+    struct Raw {
+        uint4 hdr, q0, q1;
+        uint4 h0, h1;   // Q5_K only
+    };
+    const uint8_t *W;
+    int64_t nbk;
+
+    __device__ __forceinline__ void init(const void *w, int64_t, int64_t K) {
+        W = reinterpret_cast<const uint8_t *>(w);
+        nbk = K / 256;
+    }
+    __device__ __forceinline__ void load(Raw &r, int64_t row, int unit) const {
+        const uint8_t *blk = W + (row * nbk + (unit >> 2)) * BYTES;
+        int pp = unit & 3;
+        r.hdr = *reinterpret_cast<const uint4 *>(blk);
+        const uint8_t *qs = blk + (FIVE ? 48 : 16) + 32 * pp;
+        r.q0 = *reinterpret_cast<const uint4 *>(qs);
+        r.q1 = *reinterpret_cast<const uint4 *>(qs + 16);
+        if constexpr (FIVE) {
+            r.h0 = *reinterpret_cast<const uint4 *>(blk + 16);
+            r.h1 = *reinterpret_cast<const uint4 *>(blk + 32);
+        }
+    }
+};
+
+// 6-bit scale and min of sub-block j (0..7) from the 12 packed bytes held in
+// hdr.y (bytes 0-3), hdr.z (4-7), hdr.w (8-11).
+__device__ __forceinline__ void q45_scale_min(const uint4 &hdr, int j, int &sc, int &m) {
+    int jj = j & 3;
+    uint32_t Y = ubyte(hdr.y, jj), Z = ubyte(hdr.z, jj), Wb = ubyte(hdr.w, jj);
+    int sl = (int)(Y & 63), ml = (int)(Z & 63);
+    int sh = (int)((Wb & 15) | ((Y >> 6) << 4)), mh = (int)((Wb >> 4) | ((Z >> 6) << 4));
+    sc = j < 4 ? sl : sh;
+    m = j < 4 ? ml : mh;
+}
+
+template <bool FIVE, int N, bool DUMP>
+__device__ __forceinline__ void q45_dot(const typename Q45<FIVE>::Raw &r, int unit, const ActTile &t,
+                                        int tb, float acc[N], int32_t *dump, int64_t dstride) {
+    int pp = unit & 3, j0 = 2 * pp, j1 = 2 * pp + 1;
+    uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
+    int lo[8], hi[8];
+    if constexpr (FIVE) {
+        uint32_t h[8] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w};
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            lo[m] = (int)((q[m] & 0x0F0F0F0Fu) | (((h[m] >> j0) & 0x01010101u) << 4));
+            hi[m] = (int)(((q[m] >> 4) & 0x0F0F0F0Fu) | (((h[m] >> j1) & 0x01010101u) << 4));
+        }
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            lo[m] = (int)(q[m] & 0x0F0F0F0Fu);
+            hi[m] = (int)((q[m] >> 4) & 0x0F0F0F0Fu);
+        }
+    }
+    int sc0, m0, sc1, m1;
+    q45_scale_min(r.hdr, j0, sc0, m0);
+    q45_scale_min(r.hdr, j1, sc1, m1);
+    float d = half_to_float(r.hdr.x), dmin = half_to_float(r.hdr.x >> 16);
+    float m0f = (float)m0, m1f = (float)m1;
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+        const uint4 a0 = t.x0[n * t.nb + tb], a1 = t.x1[n * t.nb + tb];
+        const uint4 b0 = t.x0[n * t.nb + tb + 1], b1 = t.x1[n * t.nb + tb + 1];
+        int da = sdot4(lo[0], (int)a0.x, 0);
+        da = sdot4(lo[1], (int)a0.y, da);
+        da = sdot4(lo[2], (int)a0.z, da);
+        da = sdot4(lo[3], (int)a0.w, da);
+        da = sdot4(lo[4], (int)a1.x, da);
+        da = sdot4(lo[5], (int)a1.y, da);
+        da = sdot4(lo[6], (int)a1.z, da);
+        da = sdot4(lo[7], (int)a1.w, da);
+        int db = sdot4(hi[0], (int)b0.x, 0);
+        db = sdot4(hi[1], (int)b0.y, db);
+        db = sdot4(hi[2], (int)b0.z, db);
+        db = sdot4(hi[3], (int)b0.w, db);
+        db = sdot4(hi[4], (int)b1.x, db);
+        db = sdot4(hi[5], (int)b1.y, db);
+        db = sdot4(hi[6], (int)b1.z, db);
+        db = sdot4(hi[7], (int)b1.w, db);
+        if constexpr (DUMP) {
+            dump[n * dstride] = da;
+            dump[n * dstride + 1] = db;
+        } else {
+            float2 fa = t.f[n * t.nb + tb], fb = t.f[n * t.nb + tb + 1];
+            float s = fa.x * (float)__mul24(sc0, da);
+            s = __builtin_fmaf(fb.x, (float)__mul24(sc1, db), s);
+            float mm = m0f * fa.y;
+            mm = __builtin_fmaf(m1f, fb.y, mm);
+            acc[n] = __builtin_fmaf(d, s, acc[n]);
+            acc[n] = __builtin_fmaf(-dmin, mm, acc[n]);
+        }
+    }
+}
+
+template <class F>
+struct Dot;
+template <>
+struct Dot<Q6Planar> {
+    template <int N, bool DUMP>
+    __device__ __forceinline__ static void run(const Q6Planar::Raw &r, int, const ActTile &t, int tb,
+                                               float acc[N], int32_t *dump, int64_t ds) {
+        q6_dot<Q6Planar, N, DUMP>(r, t, tb, acc, dump, ds);
+    }
+};
+template <>
+struct Dot<Q6Gguf> {
+    template <int N, bool DUMP>
+    __device__ __forceinline__ static void run(const Q6Gguf::Raw &r, int, const ActTile &t, int tb,
+                                               float acc[N], int32_t *dump, int64_t ds) {
+        q6_dot<Q6Gguf, N, DUMP>(r, t, tb, acc, dump, ds);
+    }
+};
+template <bool FIVE>
+struct Dot<Q45<FIVE>> {
+    template <int N, bool DUMP>
+    __device__ __forceinline__ static void run(const typename Q45<FIVE>::Raw &r, int unit, const ActTile &t,
+                                               int tb, float acc[N], int32_t *dump, int64_t ds) {
+        q45_dot<FIVE, N, DUMP>(r, unit, t, tb, acc, dump, ds);
+    }
+};
+
+// Gate and up matrices of one expert read as one matrix of interleaved
+// virtual rows: virtual row 2r is gate row r, 2r+1 is up row r.  A wave then
+// holds gate and up of the same rows side by side.
+struct Q4GateUp {
+    static constexpr int SBPU = Q45<false>::SBPU, IT = Q45<false>::IT;
+    static constexpr float DSCALE = 1.0f;
+    using Raw = Q45<false>::Raw;
+    Q45<false> g, u;
+    int64_t base_row;   // first row of the expert in both tensors
+
+    __device__ __forceinline__ void load(Raw &r, int64_t vrow, int unit) const {
+        const Q45<false> &m = (vrow & 1) ? u : g;
+        m.load(r, base_row + (vrow >> 1), unit);
+    }
+};
+template <>
+struct Dot<Q4GateUp> {
+    template <int N, bool DUMP>
+    __device__ __forceinline__ static void run(const Q4GateUp::Raw &r, int unit, const ActTile &t, int tb,
+                                               float acc[N], int32_t *dump, int64_t ds) {
+        q45_dot<false, N, DUMP>(r, unit, t, tb, acc, dump, ds);
+    }
+};
+
+// ------------------------------------------------------- Q8_1 quantizer
+// Quantizes one block of 32 values held one per lane by an aligned group of
+// 32 lanes (all 32 lanes active).  Returns the lane's int8 quant; the block's
+// fp16 d and s bits are returned in every lane.  d = amax/127 and x/d are
+// IEEE fp32 divisions, rounding is half away from zero, the fp16 stores
+// round to nearest even.
+__device__ __forceinline__ int q8_1_quantize32(float x, uint32_t &dbits, uint32_t &sbits) {
+    float a = fabsf(x);
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
+    float d = a / 127.0f;
+    int q = 0;
+    if (d != 0.0f) {
+        float r = roundf(x / d);
+        r = fminf(fmaxf(r, -127.0f), 127.0f);
+        q = (int)r;
+    }
+    int s = q;
+#pragma unroll
+    for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m, 32);
+    dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
+    sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+    return q;
+}
+
+// Stores the quant of lane i (0..31) of a 32-lane group as one Q8_1 block at
+// blk (4-byte aligned): lanes 0, 4, .. write a dword of four quants each,
+// lane 0 also the (d, s) header.  All 32 lanes must be active; `store`
+// masks the writes.
+__device__ __forceinline__ void q8_1_store32(uint8_t *blk, int i, int q, uint32_t dbits, uint32_t sbits,
+                                             bool store) {
+    uint32_t b = (uint32_t)q & 0xFFu;
+    uint32_t b1 = __shfl_down(b, 1, 32), b2 = __shfl_down(b, 2, 32), b3 = __shfl_down(b, 3, 32);
+    if (store) {
+        uint32_t *p = reinterpret_cast<uint32_t *>(blk);
+        if ((i & 3) == 0) p[1 + (i >> 2)] = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        if (i == 0) p[0] = dbits | (sbits << 16);
+    }
+}
+
+// ------------------------------------------------------------- the core
+// Parameters of one MMVQ call as the kernel sees them.  Column n of the
+// activation starts at Q8_1 block ((colpack >> 8n) & 255) * xstride of xq
+// (a packed index rather than an array: a runtime-indexed array would be
+// read from memory); dumps go to dump[n * rows * K/32 + row * K/32 + b].
+struct MmvqArgs {
+    const uint8_t *xq;
+    int32_t *dump;
+    int64_t rows, K;
+    uint64_t colpack;
+    int64_t xstride;
+    int its;              // register steps staged per LDS sub-tile
+};
+
+// First Q8_1 block of column n.
+template <int N>
+__device__ __forceinline__ int64_t xcol_of(const MmvqArgs &a, int n) {
+    return (int64_t)((a.colpack >> (8 * n)) & 255u) * a.xstride;
+}
+
+// Row of the calling lane inside a workgroup that starts at row0.
+template <int U>
+__device__ __forceinline__ int64_t lane_row(int64_t row0) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    return row0 + (int64_t)wave * (kWave / U) + lane / U;
+}
+
+// Computes N dot products for the rows of one workgroup (rows row0 ..;
+// lane_row<U>() names the calling lane's row) and leaves in acc[n] the full
+// sum for (lane's row, column n), identical in every lane of the row's
+// group.  lds holds at least N * its * U * SBPU * kActBytesPerBlock bytes.
+// Every thread of the workgroup must call it (it has barriers); it starts
+// with no barrier, so a caller that reuses lds must place one before.
+template <class F, int N, int U, bool DUMP>
+__device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
+                                          float acc[N]) {
+    constexpr int IT = F::IT;
+    constexpr int SBPU = F::SBPU;
+    constexpr int SI = 3;   // activation blocks per thread loaded ahead of the weights
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int u = (tid & (kWave - 1)) % U;
+    const int64_t row = lane_row<U>(row0);
+    const bool row_ok = row < a.rows;
+    const int64_t nsb = a.K / 32;
+    const int units = (int)(nsb / SBPU);
+
+#pragma unroll
+    for (int n = 0; n < N; n++) acc[n] = 0.0f;
+
+    for (int c0 = 0; c0 < units; c0 += U * IT) {            // register chunk
+        typename F::Raw r[IT];
+        bool ok[IT];
+        int sub_sb0 = c0 * SBPU;
+        int sub_nsb = min(a.its * U * SBPU, (int)nsb - sub_sb0);
+        int items = N * sub_nsb;
+        if (c0 > 0) lds_barrier();
+        // activation loads are issued before the weight loads: loads retire
+        // in order, so waiting for them does not wait for the weights
+        ActRaw ar[SI];
+#pragma unroll
+        for (int s = 0; s < SI; s++) {
+            // unconditional (clamped) so the loads stay ahead of the weights
+            int i = min(tid + s * nthr, items - 1);
+            int n = i / sub_nsb, b = i - n * sub_nsb;
+            act_load(ar[s], a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
+        }
+        // keep every activation load ahead of the weight loads
+        __builtin_amdgcn_sched_barrier(0);
+        // unconditional loads (out-of-range lanes read a clamped, valid
+        // address and ignore it): branches here would make the wait counts
+        // conservative and serialize the weight stream behind the tile
+#pragma unroll
+        for (int it = 0; it < IT; it++) {
+            int unit = c0 + u + U * it;
+            ok[it] = row_ok && unit < units;
+            fmt.load(r[it], row_ok ? row : a.rows - 1, min(unit, units - 1));
+        }
+        ActTile t = act_tile(lds, N, sub_nsb);
+#pragma unroll
+        for (int s = 0; s < SI; s++) {
+            int i = tid + s * nthr;
+            if (i < items) act_store(t, i, ar[s], F::DSCALE);
+        }
+        for (int i = tid + SI * nthr; i < items; i += nthr) {
+            int n = i / sub_nsb, b = i - n * sub_nsb;
+            ActRaw x;
+            act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
+            act_store(t, i, x, F::DSCALE);
+        }
+        lds_barrier();
+
+        int it_lo = 0;
+        while (true) {
+            int it_hi = min(it_lo + a.its, IT);
+#pragma unroll
+            for (int it = 0; it < IT; it++) {
+                if (it < it_lo || it >= it_hi) continue;
+                if (ok[it]) {
+                    int unit = c0 + u + U * it;
+                    int tb = (u + U * (it - it_lo)) * SBPU;
+                    int32_t *dp = nullptr;
+                    if constexpr (DUMP) dp = a.dump + row * nsb + (int64_t)unit * SBPU;
+                    Dot<F>::template run<N, DUMP>(r[it], unit, t, tb, acc, dp, a.rows * nsb);
+                }
+            }
+            it_lo = it_hi;
+            if (it_lo >= IT || c0 + it_lo * U >= units) break;
+            // next LDS sub-tile of the same register chunk
+            lds_barrier();
+            sub_sb0 = (c0 + it_lo * U) * SBPU;
+            sub_nsb = min(a.its * U * SBPU, (int)nsb - sub_sb0);
+            items = N * sub_nsb;
+            t = act_tile(lds, N, sub_nsb);
+            for (int i = tid; i < items; i += nthr) {
+                int n = i / sub_nsb, b = i - n * sub_nsb;
+                ActRaw x;
+                act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
+                act_store(t, i, x, F::DSCALE);
+            }
+            lds_barrier();
+        }
+    }
+#pragma unroll
+    for (int n = 0; n < N; n++) acc[n] = group_sum<U>(acc[n]);
+}
+
+}  // namespace qmv

@@ -1,0 +1,62 @@
+// launch.hpp -- internal host-side launchers of libqmv (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmv {
+
+enum Fmt { FMT_Q6_PLANAR = 0, FMT_Q6_GGUF = 1, FMT_Q4 = 2, FMT_Q5 = 3 };
+
+// Lanes sharing a row: the largest of 64, 32, 16 (not above cap) that
+// divides the row's units with at least three units per lane, else 8.  A
+// function of the row length only, so every launch of a given K sums a row
+// in the same order.
+__host__ __device__ constexpr int choose_u(int units, int cap = 64) {
+    for (int U = 64; U >= 16; U /= 2)
+        if (U <= cap && units % U == 0 && units / U >= 3) return U;
+    return 8;
+}
+
+// Register steps staged per LDS sub-tile: the first sub-tile's activation
+// blocks must fit three per thread.
+__host__ __device__ constexpr int its_for(int IT, int N, int U, int SBPU, int nthr) {
+    int its = IT;
+    while (its > 1 && N * its * U * SBPU > 3 * nthr) its--;
+    return its;
+}
+
+hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t nblocks, hipStream_t s);
+hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t nblocks, hipStream_t s);
+
+hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int32_t *dump,
+                                 int64_t rows, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_mmvq_q6_gguf(const void *w, const void *xq, float *out, int32_t *dump,
+                               int64_t rows, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_mmvq_q4(const void *w, const void *xq, float *out, int32_t *dump,
+                          int64_t rows, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_mmvq_q5(const void *w, const void *xq, float *out, int32_t *dump,
+                          int64_t rows, int64_t K, int ncols, hipStream_t s);
+
+struct MoeArgs {
+    const uint8_t *w_gate, *w_up, *w_down;
+    const uint8_t *xq;
+    const int32_t *ids;
+    const float *route_w;
+    float *out;
+    uint8_t *ws;
+    int E, T, topk, S;
+    int64_t d_model, d_ff;
+    int64_t off_h, off_hq, off_y;   // byte offsets of h, hq, y in ws
+};
+
+// Byte offsets of the workspace regions (see qmv.h) and its total size.
+struct MoeLayout {
+    int64_t off_h, off_hq, off_y, total;
+};
+MoeLayout moe_layout(int T, int topk, int64_t d_model, int64_t d_ff);
+
+hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s);
+
+}  // namespace qmv

@@ -1,0 +1,126 @@
+// misc.hip -- Q8_1 activation quantizer and the load-time Q6_K planar
+// conversion (and its inverse).
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qmv {
+
+// One 32-lane group per Q8_1 block; x is [ncols][K], xq [ncols][K/32].
+__global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__ x, uint8_t *__restrict__ xq,
+                                                       int64_t K, int64_t nblocks) {
+    const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
+    const int i = threadIdx.x & 31;
+    const bool ok = g < nblocks;
+    const int64_t nb = K / 32;
+    float v = 0.0f;
+    if (ok) {
+        const int64_t col = g / nb, b = g - col * nb;
+        v = x[col * K + b * 32 + i];
+    }
+    uint32_t db, sb;
+    int q = q8_1_quantize32(v, db, sb);
+    q8_1_store32(xq + g * kQ81Bytes, i, q, db, sb, ok);
+}
+
+hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s) {
+    const int64_t nblocks = (int64_t)ncols * (K / 32);
+    const int64_t threads = nblocks * 32;
+    const int64_t grid = (threads + 255) / 256;
+    hipLaunchKernelGGL(k_quantize_q8_1, dim3((unsigned)grid), dim3(256), 0, s, x, xq, K, nblocks);
+    return hipGetLastError();
+}
+
+// GGUF Q6_K -> planar.  One thread per (block, sub-block j): it decodes the
+// 32 six-bit values of sub-block j, writes its 16-byte plane-A and 8-byte
+// plane-B pieces, and sub-block 0's thread copies the scales and d.
+__global__ __launch_bounds__(256) void k_repack_q6k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                    int64_t NB) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= NB * 8) return;
+    const int64_t t = gid >> 3;
+    const int j = (int)(gid & 7), h = j >> 2, c = j & 3;
+    const uint8_t *blk = src + t * kQ6Bytes;
+    uint32_t v[32];
+#pragma unroll
+    for (int l = 0; l < 32; l++) {
+        uint32_t lo = (blk[64 * h + 32 * (c & 1) + l] >> (4 * (c >> 1))) & 15u;
+        uint32_t hi = (blk[128 + 32 * h + l] >> (2 * c)) & 3u;
+        v[l] = (lo | (hi << 4)) ^ 32u;                 // (q6 - 32) mod 64
+    }
+    uint32_t A[4], B[2];
+#pragma unroll
+    for (int m = 0; m < 4; m++)
+        A[m] = (v[4 * m] << 2) | (v[4 * m + 1] << 10) | (v[4 * m + 2] << 18) | (v[4 * m + 3] << 26);
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+        B[m] = (v[16 + 4 * m] << 2) | (v[17 + 4 * m] << 10) | (v[18 + 4 * m] << 18) | (v[19 + 4 * m] << 26);
+    // spare bit pairs: weight 24+k -> bits 0-1 of A0, A1, A2 byte k (its
+    // bits 0-1, 2-3, 4-5); weight 28+k -> A3, B0, B1 byte k
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        uint32_t w24 = v[24 + k], w28 = v[28 + k];
+        A[0] |= (w24 & 3u) << (8 * k);
+        A[1] |= ((w24 >> 2) & 3u) << (8 * k);
+        A[2] |= ((w24 >> 4) & 3u) << (8 * k);
+        A[3] |= (w28 & 3u) << (8 * k);
+        B[0] |= ((w28 >> 2) & 3u) << (8 * k);
+        B[1] |= ((w28 >> 4) & 3u) << (8 * k);
+    }
+    reinterpret_cast<uint4 *>(dst)[t * 8 + j] = make_uint4(A[0], A[1], A[2], A[3]);
+    reinterpret_cast<uint2 *>(dst + 128 * NB)[t * 8 + j] = make_uint2(B[0], B[1]);
+    if (j == 0) {
+        uint8_t *sc = dst + 192 * NB + 16 * t;
+#pragma unroll
+        for (int k = 0; k < 16; k++) sc[k] = blk[192 + k];
+        dst[208 * NB + 2 * t] = blk[208];
+        dst[208 * NB + 2 * t + 1] = blk[209];
+    }
+}
+
+// planar -> GGUF Q6_K, one thread per block.
+__global__ __launch_bounds__(256) void k_unpack_q6k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                    int64_t NB) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= NB) return;
+    uint8_t *blk = dst + t * kQ6Bytes;
+    uint8_t ql[128] = {}, qh[64] = {};
+    for (int j = 0; j < 8; j++) {
+        const uint4 a = reinterpret_cast<const uint4 *>(src)[t * 8 + j];
+        const uint2 b = reinterpret_cast<const uint2 *>(src + 128 * NB)[t * 8 + j];
+        const uint32_t A[4] = {a.x, a.y, a.z, a.w}, B[2] = {b.x, b.y};
+        uint32_t v[32];
+        for (int k = 0; k < 16; k++) v[k] = (A[k >> 2] >> (8 * (k & 3) + 2)) & 63u;
+        for (int k = 0; k < 8; k++) v[16 + k] = (B[k >> 2] >> (8 * (k & 3) + 2)) & 63u;
+        for (int k = 0; k < 4; k++) {
+            const int sh = 8 * k;
+            v[24 + k] = ((A[0] >> sh) & 3u) | (((A[1] >> sh) & 3u) << 2) | (((A[2] >> sh) & 3u) << 4);
+            v[28 + k] = ((A[3] >> sh) & 3u) | (((B[0] >> sh) & 3u) << 2) | (((B[1] >> sh) & 3u) << 4);
+        }
+        const int h = j >> 2, c = j & 3;
+        for (int l = 0; l < 32; l++) {
+            uint32_t q6 = v[l] ^ 32u;
+            ql[64 * h + 32 * (c & 1) + l] |= (uint8_t)((q6 & 15u) << (4 * (c >> 1)));
+            qh[32 * h + l] |= (uint8_t)((q6 >> 4) << (2 * c));
+        }
+    }
+    for (int k = 0; k < 128; k++) blk[k] = ql[k];
+    for (int k = 0; k < 64; k++) blk[128 + k] = qh[k];
+    const uint8_t *sc = src + 192 * NB + 16 * t;
+    for (int k = 0; k < 16; k++) blk[192 + k] = sc[k];
+    blk[208] = src[208 * NB + 2 * t];
+    blk[209] = src[208 * NB + 2 * t + 1];
+}
+
+hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t NB, hipStream_t s) {
+    const int64_t grid = (NB * 8 + 255) / 256;
+    hipLaunchKernelGGL(k_repack_q6k, dim3((unsigned)grid), dim3(256), 0, s, src, dst, NB);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t NB, hipStream_t s) {
+    const int64_t grid = (NB + 255) / 256;
+    hipLaunchKernelGGL(k_unpack_q6k, dim3((unsigned)grid), dim3(256), 0, s, src, dst, NB);
+    return hipGetLastError();
+}
+
+}  // namespace qmv

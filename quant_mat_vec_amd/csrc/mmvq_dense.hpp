@@ -1,0 +1,89 @@
+// mmvq_dense.hpp -- the dense MMVQ kernel and its compile-time dispatch on
+// (lanes per row U, columns N, dump flag).  Included by one source file per
+// weight format so the instantiations compile in parallel.
+#pragma once
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qmv {
+
+constexpr int kDenseWaves = 4;
+
+template <class F, int N, int U, bool DUMP>
+__global__ __launch_bounds__(kDenseWaves * kWave) void k_mmvq_dense(const void *__restrict__ w, MmvqArgs a,
+                                                                  float *__restrict__ out) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    F fmt;
+    fmt.init(w, a.rows, a.K);
+    const int64_t row0 = (int64_t)blockIdx.x * kDenseWaves * (kWave / U);
+    float acc[N];
+    mmvq_rows<F, N, U, DUMP>(fmt, a, row0, lds, acc);
+    if constexpr (!DUMP) {
+        const int64_t row = lane_row<U>(row0);
+        const int u = (threadIdx.x & (kWave - 1)) % U;
+        if (row < a.rows) {
+#pragma unroll
+            for (int n = 0; n < N; n++)
+                if (u == n % U) out[(int64_t)n * a.rows + row] = acc[n];
+        }
+    }
+}
+
+template <class F, int N, int U, bool DUMP>
+hipError_t launch_dense_nu(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                           hipStream_t s) {
+    constexpr int threads = kDenseWaves * kWave;
+    constexpr int its = its_for(F::IT, N, U, F::SBPU, threads);
+    MmvqArgs a;
+    a.xq = reinterpret_cast<const uint8_t *>(xq);
+    a.dump = dump;
+    a.rows = rows;
+    a.K = K;
+    a.colpack = 0x0706050403020100ull;
+    a.xstride = K / 32;
+    a.its = its;
+    const size_t lds = (size_t)N * its * U * F::SBPU * kActBytesPerBlock;
+    const int64_t rpb = kDenseWaves * (kWave / U);
+    const int64_t grid = (rows + rpb - 1) / rpb;
+    hipLaunchKernelGGL((k_mmvq_dense<F, N, U, DUMP>), dim3((unsigned)grid), dim3(threads), lds, s, w, a, out);
+    return hipGetLastError();
+}
+
+template <class F, int U, bool DUMP>
+hipError_t launch_dense_u(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                          int ncols, hipStream_t s) {
+    switch (ncols) {
+    case 1: return launch_dense_nu<F, 1, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 2: return launch_dense_nu<F, 2, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 3: return launch_dense_nu<F, 3, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 4: return launch_dense_nu<F, 4, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 5: return launch_dense_nu<F, 5, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 6: return launch_dense_nu<F, 6, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 7: return launch_dense_nu<F, 7, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 8: return launch_dense_nu<F, 8, U, DUMP>(w, xq, out, dump, rows, K, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class F, bool DUMP>
+hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                        int ncols, hipStream_t s) {
+    const int units = (int)(K / 32 / F::SBPU);
+    switch (choose_u(units)) {
+    case 8: return launch_dense_u<F, 8, DUMP>(w, xq, out, dump, rows, K, ncols, s);
+    case 16: return launch_dense_u<F, 16, DUMP>(w, xq, out, dump, rows, K, ncols, s);
+    case 32: return launch_dense_u<F, 32, DUMP>(w, xq, out, dump, rows, K, ncols, s);
+    case 64: return launch_dense_u<F, 64, DUMP>(w, xq, out, dump, rows, K, ncols, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class F>
+hipError_t launch_dense_any(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                            int ncols, hipStream_t s) {
+    return dump ? launch_dense<F, true>(w, xq, out, dump, rows, K, ncols, s)
+                : launch_dense<F, false>(w, xq, out, dump, rows, K, ncols, s);
+}
+
+}  // namespace qmv

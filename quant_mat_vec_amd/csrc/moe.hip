@@ -1,0 +1,315 @@
+// moe.hip -- grouped MoE-expert product over a window of routed tokens.
+//
+// Four launches on one stream, none needing a host synchronization:
+//   route   : one workgroup groups the T*topk slots by expert (ascending id,
+//             ascending slot inside a group) into the workspace tables;
+//   gate/up : workgroup (i, tile) takes the i-th hit expert and 32 rows of
+//             d_ff; gate and up are read once for all of the expert's tokens
+//             (the token count is the MMVQ column count, 1..8), then
+//             h = silu(g)*u and its Q8_1 block are written per slot;
+//   down    : workgroup (i, tile) takes the i-th hit expert and a row tile of
+//             d_model, Q6_K MMVQ over the expert's requantized slots;
+//   combine : out[t] = sum over k, ascending, of route_w[t][k] * y[t][k].
+// Workgroups of experts that were not hit exit at once, so unrouted expert
+// weights are never read.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qmv {
+
+namespace {
+__host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+}  // namespace
+
+MoeLayout moe_layout(int T, int topk, int64_t d_model, int64_t d_ff) {
+    const int64_t S = (int64_t)T * topk;
+    MoeLayout L;
+    L.off_h = align256(256 + 16 * S);
+    L.off_hq = align256(L.off_h + 4 * S * d_ff);
+    L.off_y = align256(L.off_hq + (int64_t)kQ81Bytes * S * (d_ff / 32));
+    L.total = align256(L.off_y + 4 * S * d_model);
+    return L;
+}
+
+struct MoeTables {
+    const int32_t *expert, *count, *first, *slot_list;
+};
+
+__device__ __forceinline__ MoeTables moe_tables(const MoeArgs &m) {
+    const int32_t *wsi = reinterpret_cast<const int32_t *>(m.ws);
+    MoeTables t;
+    t.expert = wsi + 64;
+    t.count = t.expert + m.S;
+    t.first = t.count + m.S;
+    t.slot_list = t.first + m.S;
+    return t;
+}
+
+// S <= 64 slots, one thread per slot.
+__global__ __launch_bounds__(64) void k_moe_route(MoeArgs m) {
+    __shared__ int es[64];
+    __shared__ int fo[64];
+    const int s = threadIdx.x;
+    int e = -1;
+    if (s < m.S) {
+        e = m.ids[s];
+        if (e < 0 || e >= m.E) e = -1;
+    }
+    es[s] = e;
+    __syncthreads();
+    bool first_occ = e >= 0;
+    for (int t = 0; t < s; t++)
+        if (es[t] == e) first_occ = false;
+    fo[s] = first_occ ? 1 : 0;
+    __syncthreads();
+    int32_t *wsi = reinterpret_cast<int32_t *>(m.ws);
+    int32_t *expert = wsi + 64, *count = expert + m.S, *first = count + m.S, *slot_list = first + m.S;
+    if (e >= 0) {
+        int before = 0, pos = 0, cnt = 0, rank = 0;
+        for (int t = 0; t < m.S; t++) {
+            const int et = es[t];
+            if (et < 0) continue;
+            if (et < e) {
+                before++;
+                rank += fo[t];
+            } else if (et == e) {
+                cnt++;
+                if (t < s) pos++;
+            }
+        }
+        slot_list[before + pos] = s;
+        if (first_occ) {
+            expert[rank] = e;
+            count[rank] = cnt;
+            first[rank] = before;
+        }
+    }
+    if (s == 0) {
+        int nd = 0, bad = 0;
+        for (int t = 0; t < m.S; t++) {
+            nd += fo[t];
+            bad += es[t] < 0 ? 1 : 0;
+        }
+        wsi[0] = nd;
+        wsi[1] = bad;
+    }
+}
+
+// ------------------------------------------------------------- gate / up
+constexpr int kGuRows = 32;   // real rows per workgroup: one Q8_1 block of h
+
+template <int N, int U>
+__device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t *slots, int tile,
+                                         uint8_t *lds) {
+    constexpr int nthr = U * kWave;
+    constexpr int its = its_for(Q4GateUp::IT, N, U, Q4GateUp::SBPU, nthr);
+    float *H = reinterpret_cast<float *>(lds);                 // [N][32]
+    uint8_t *act = lds + 8 * kGuRows * sizeof(float);
+    int sl[N];
+#pragma unroll
+    for (int n = 0; n < N; n++) sl[n] = slots[n];
+
+    Q4GateUp f;
+    f.g.init(m.w_gate, 0, m.d_model);
+    f.u.init(m.w_up, 0, m.d_model);
+    f.base_row = (int64_t)e * m.d_ff;
+    MmvqArgs a;
+    a.xq = m.xq;
+    a.dump = nullptr;
+    a.rows = 2 * m.d_ff;
+    a.K = m.d_model;
+    a.colpack = 0;
+#pragma unroll
+    for (int n = 0; n < N; n++) a.colpack |= (uint64_t)(sl[n] / m.topk) << (8 * n);
+    a.xstride = m.d_model / 32;
+    a.its = its;
+    const int64_t row0 = (int64_t)tile * 2 * kGuRows;
+    float acc[N];
+    mmvq_rows<Q4GateUp, N, U, false>(f, a, row0, act, acc);
+
+    const int lane = threadIdx.x & (kWave - 1), u = lane % U;
+    const int64_t vrow = lane_row<U>(row0);
+    float *hg = reinterpret_cast<float *>(m.ws + m.off_h);
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+        const float up = __shfl_down(acc[n], U);
+        if ((vrow & 1) == 0 && vrow < a.rows && u == n % U) {
+            const float g = acc[n];
+            const float h = g / (1.0f + expf(-g)) * up;
+            const int r = (int)((vrow - row0) >> 1);
+            H[n * kGuRows + r] = h;
+            hg[(int64_t)sl[n] * m.d_ff + (int64_t)tile * kGuRows + r] = h;
+        }
+    }
+    lds_barrier();
+    const int t = threadIdx.x;
+    if (t < N * 32) {
+        const int n = t >> 5, i = t & 31;
+        int slot = sl[0];
+#pragma unroll
+        for (int k = 1; k < N; k++)
+            if (n == k) slot = sl[k];
+        uint32_t db, sb;
+        const int q = q8_1_quantize32(H[n * kGuRows + i], db, sb);
+        uint8_t *hq = m.ws + m.off_hq + ((int64_t)slot * (m.d_ff / 32) + tile) * kQ81Bytes;
+        q8_1_store32(hq, i, q, db, sb, true);
+    }
+}
+
+template <int U>
+__global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int32_t *wsi = reinterpret_cast<const int32_t *>(m.ws);
+    const int i = blockIdx.x;
+    if (i >= wsi[0]) return;
+    const MoeTables tb = moe_tables(m);
+    const int e = tb.expert[i], c = tb.count[i], f = tb.first[i];
+    for (int c0 = 0; c0 < c; c0 += 8) {
+        if (c0 > 0) lds_barrier();
+        const int nc = min(8, c - c0);
+        const int32_t *sl = tb.slot_list + f + c0;
+        switch (nc) {
+        case 1: gateup_n<1, U>(m, e, sl, blockIdx.y, lds); break;
+        case 2: gateup_n<2, U>(m, e, sl, blockIdx.y, lds); break;
+        case 3: gateup_n<3, U>(m, e, sl, blockIdx.y, lds); break;
+        case 4: gateup_n<4, U>(m, e, sl, blockIdx.y, lds); break;
+        case 5: gateup_n<5, U>(m, e, sl, blockIdx.y, lds); break;
+        case 6: gateup_n<6, U>(m, e, sl, blockIdx.y, lds); break;
+        case 7: gateup_n<7, U>(m, e, sl, blockIdx.y, lds); break;
+        default: gateup_n<8, U>(m, e, sl, blockIdx.y, lds); break;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ down
+constexpr int kDnWaves = 4;
+
+template <class F, int N, int U>
+__device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t *slots, int tile, uint8_t *lds) {
+    constexpr int nthr = kDnWaves * kWave;
+    constexpr int its = its_for(F::IT, N, U, F::SBPU, nthr);
+    int sl[N];
+#pragma unroll
+    for (int n = 0; n < N; n++) sl[n] = slots[n];
+    F f;
+    f.init(m.w_down, (int64_t)m.E * m.d_model, m.d_ff);
+    MmvqArgs a;
+    a.xq = m.ws + m.off_hq;
+    a.dump = nullptr;
+    a.rows = (int64_t)(e + 1) * m.d_model;
+    a.K = m.d_ff;
+    a.colpack = 0;
+#pragma unroll
+    for (int n = 0; n < N; n++) a.colpack |= (uint64_t)sl[n] << (8 * n);
+    a.xstride = m.d_ff / 32;
+    a.its = its;
+    const int64_t row0 = (int64_t)e * m.d_model + (int64_t)tile * kDnWaves * (kWave / U);
+    float acc[N];
+    mmvq_rows<F, N, U, false>(f, a, row0, lds, acc);
+    const int64_t row = lane_row<U>(row0);
+    const int u = (threadIdx.x & (kWave - 1)) % U;
+    float *y = reinterpret_cast<float *>(m.ws + m.off_y);
+    if (row < a.rows) {
+#pragma unroll
+        for (int n = 0; n < N; n++)
+            if (u == n % U) y[(int64_t)sl[n] * m.d_model + (row - (int64_t)e * m.d_model)] = acc[n];
+    }
+}
+
+template <class F, int U>
+__global__ __launch_bounds__(kDnWaves *kWave) void k_moe_down(MoeArgs m) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int32_t *wsi = reinterpret_cast<const int32_t *>(m.ws);
+    const int i = blockIdx.x;
+    if (i >= wsi[0]) return;
+    const MoeTables tb = moe_tables(m);
+    const int e = tb.expert[i], c = tb.count[i], f = tb.first[i];
+    for (int c0 = 0; c0 < c; c0 += 8) {
+        if (c0 > 0) lds_barrier();
+        const int nc = min(8, c - c0);
+        const int32_t *sl = tb.slot_list + f + c0;
+        switch (nc) {
+        case 1: down_n<F, 1, U>(m, e, sl, blockIdx.y, lds); break;
+        case 2: down_n<F, 2, U>(m, e, sl, blockIdx.y, lds); break;
+        case 3: down_n<F, 3, U>(m, e, sl, blockIdx.y, lds); break;
+        case 4: down_n<F, 4, U>(m, e, sl, blockIdx.y, lds); break;
+        case 5: down_n<F, 5, U>(m, e, sl, blockIdx.y, lds); break;
+        case 6: down_n<F, 6, U>(m, e, sl, blockIdx.y, lds); break;
+        case 7: down_n<F, 7, U>(m, e, sl, blockIdx.y, lds); break;
+        default: down_n<F, 8, U>(m, e, sl, blockIdx.y, lds); break;
+        }
+    }
+}
+
+// --------------------------------------------------------------- combine
+__global__ __launch_bounds__(256) void k_moe_combine(MoeArgs m) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int t = blockIdx.y;
+    if (i >= m.d_model) return;
+    const float *y = reinterpret_cast<const float *>(m.ws + m.off_y);
+    float acc = 0.0f;
+    for (int k = 0; k < m.topk; k++) {
+        const int s = t * m.topk + k;
+        const int e = m.ids[s];
+        if (e < 0 || e >= m.E) continue;
+        acc = __builtin_fmaf(m.route_w[s], y[(int64_t)s * m.d_model + i], acc);
+    }
+    m.out[(int64_t)t * m.d_model + i] = acc;
+}
+
+// ------------------------------------------------------------------ host
+template <int U>
+static hipError_t launch_gateup(const MoeArgs &m, int smax, hipStream_t s) {
+    constexpr int nthr = U * kWave;
+    size_t act = 0;
+    // largest tile over the column counts a workgroup may meet
+    for (int n = 1; n <= 8; n++) {
+        size_t b = (size_t)n * its_for(Q4GateUp::IT, n, U, Q4GateUp::SBPU, nthr) * U * Q4GateUp::SBPU *
+                   kActBytesPerBlock;
+        if (b > act) act = b;
+    }
+    const size_t lds = 8 * kGuRows * sizeof(float) + act;
+    hipLaunchKernelGGL((k_moe_gateup<U>), dim3(smax, (unsigned)(m.d_ff / kGuRows)), dim3(nthr), lds, s, m);
+    return hipGetLastError();
+}
+
+template <class F, int U>
+static hipError_t launch_down_u(const MoeArgs &m, int smax, hipStream_t s) {
+    constexpr int nthr = kDnWaves * kWave;
+    size_t lds = 0;
+    // largest tile over the column counts a workgroup may meet
+    for (int n = 1; n <= 8; n++) {
+        int its = its_for(F::IT, n, U, F::SBPU, nthr);
+        size_t b = (size_t)n * its * U * F::SBPU * kActBytesPerBlock;
+        if (b > lds) lds = b;
+    }
+    const int64_t rpb = kDnWaves * (kWave / U);
+    hipLaunchKernelGGL((k_moe_down<F, U>), dim3(smax, (unsigned)((m.d_model + rpb - 1) / rpb)), dim3(nthr), lds,
+                       s, m);
+    return hipGetLastError();
+}
+
+template <class F>
+static hipError_t launch_down(const MoeArgs &m, int smax, hipStream_t s) {
+    switch (choose_u((int)(m.d_ff / 32))) {
+    case 8: return launch_down_u<F, 8>(m, smax, s);
+    case 16: return launch_down_u<F, 16>(m, smax, s);
+    case 32: return launch_down_u<F, 32>(m, smax, s);
+    default: return launch_down_u<F, 64>(m, smax, s);
+    }
+}
+
+hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s) {
+    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(64), 0, s, m);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int smax = m.S < m.E ? m.S : m.E;
+    err = choose_u((int)(m.d_model / 64), 16) == 8 ? launch_gateup<8>(m, smax, s) : launch_gateup<16>(m, smax, s);
+    if (err != hipSuccess) return err;
+    err = down_layout == 1 ? launch_down<Q6Planar>(m, smax, s) : launch_down<Q6Gguf>(m, smax, s);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((m.d_model + 255) / 256), m.T), dim3(256), 0, s, m);
+    return hipGetLastError();
+}
+
+}  // namespace qmv

@@ -1,0 +1,143 @@
+"""C-ABI library checks that need no GPU: the library loads, exports every
+symbol include/qmv.h declares, and rejects every invalid argument on the host
+(the checks run before any HIP call, so fake pointer values are safe here)."""
+import ctypes
+import os
+
+import pytest
+
+from quant_mat_vec_amd import qmv
+
+E_INV, E_UNS, E_ALN, E_WS = (qmv.QMV_ERR_INVALID_ARG, qmv.QMV_ERR_UNSUPPORTED,
+                             qmv.QMV_ERR_ALIGNMENT, qmv.QMV_ERR_WORKSPACE)
+P = 0x7F0000000000          # a fake, 256-byte aligned "device address"; never dereferenced
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qmv.LIB_PATH):
+        from quant_mat_vec_amd import build
+        build.build(verbose=False)
+    return qmv.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = qmv.declared_symbols()
+    expected = {"quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
+                "unpack_q6k_planar", "mmvq_q6k_isums", "mmvq_q4k_isums", "mmvq_q5k_isums",
+                "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "qmv_strerror",
+                "qmv_last_hip_error"}
+    assert expected <= set(names), set(names) ^ expected
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_strerror_names_every_code(L):
+    for c in (0, -1, -2, -3, -4, -5):
+        assert qmv.strerror(c) and "unknown" not in qmv.strerror(c)
+    assert "unknown" in qmv.strerror(-99)
+    assert L.qmv_last_hip_error() == 0
+
+
+def test_quantize_rejects(L):
+    q = L.quantize_q8_1
+    assert q(None, P, 256, 1, None) == E_INV
+    assert q(P, None, 256, 1, None) == E_INV
+    assert q(P, P, 0, 1, None) == E_INV
+    assert q(P, P, 256, 0, None) == E_INV
+    assert q(P, P, 100, 1, None) == E_UNS
+    assert q(P, P, (1 << 20) + 32, 1, None) == E_UNS
+    assert q(P, P, 256, 65536, None) == E_UNS
+    assert q(P + 2, P, 256, 1, None) == E_ALN
+    assert q(P, P + 1, 256, 1, None) == E_ALN
+
+
+@pytest.mark.parametrize("name", ["mmvq_q6k", "mmvq_q4k", "mmvq_q5k",
+                                  "mmvq_q6k_isums", "mmvq_q4k_isums", "mmvq_q5k_isums"])
+def test_mmvq_rejects(L, name):
+    fn = getattr(L, name)
+    q6 = "q6k" in name
+
+    def call(w=P, xq=P, out=P, rows=16, K=512, ncols=1, layout=qmv.LAYOUT_PLANAR):
+        if q6:
+            return fn(w, layout, xq, out, rows, K, ncols, None)
+        return fn(w, xq, out, rows, K, ncols, None)
+
+    assert call(w=None) == E_INV
+    assert call(xq=None) == E_INV
+    assert call(out=None) == E_INV
+    assert call(rows=0) == E_INV
+    assert call(rows=-3) == E_INV
+    assert call(K=0) == E_INV
+    assert call(K=300) == E_UNS
+    assert call(K=1 << 21) == E_UNS
+    assert call(rows=1 << 31) == E_UNS
+    assert call(ncols=0) == E_UNS
+    assert call(ncols=9) == E_UNS
+    assert call(xq=P + 2) == E_ALN
+    assert call(out=P + 2) == E_ALN
+    if q6:
+        assert call(layout=2) == E_UNS
+        assert call(layout=-1) == E_UNS
+        assert call(w=P + 8, layout=qmv.LAYOUT_PLANAR) == E_ALN
+        assert call(w=P + 2, layout=qmv.LAYOUT_GGUF) == E_ALN
+    else:
+        assert call(w=P + 8) == E_ALN
+
+
+def test_repack_rejects(L):
+    for fn, a_src, a_dst in ((L.repack_q6k_planar, 2, 16), (L.unpack_q6k_planar, 16, 2)):
+        assert fn(None, P, 4, 256, None) == E_INV
+        assert fn(P, None, 4, 256, None) == E_INV
+        assert fn(P, P + 4096, 0, 256, None) == E_INV
+        assert fn(P, P + 4096, 4, 100, None) == E_UNS
+        assert fn(P, P + 832, 4, 256, None) == E_INV            # overlapping buffers
+        if a_src > 1:
+            assert fn(P + a_src // 2, P + 4096, 4, 256, None) == E_ALN
+        assert fn(P, P + 4096 + a_dst // 2, 4, 256, None) == E_ALN
+
+
+def test_moe_rejects_and_workspace(L):
+    ws_size = L.grouped_expert_mmvq_workspace(128, 8, 8, 2560, 768)
+    lay = qmv.moe_workspace_layout(8, 8, 2560, 768)
+    assert ws_size == lay["total"] and ws_size % 256 == 0
+    assert lay["h"] >= lay["slot_list"] + 4 * 64
+    assert L.grouped_expert_mmvq_workspace(128, 9, 8, 2560, 768) == 0
+    assert L.grouped_expert_mmvq_workspace(128, 8, 8, 2500, 768) == 0
+
+    def call(**kw):
+        a = dict(wg=P, wu=P, wd=P, lay=1, xq=P, ids=P, rw=P, out=P, E=128, T=8, topk=8, dm=2560,
+                 dff=768, ws=P, wsb=ws_size)
+        a.update(kw)
+        return L.grouped_expert_mmvq(a["wg"], a["wu"], a["wd"], a["lay"], a["xq"], a["ids"], a["rw"],
+                                     a["out"], a["E"], a["T"], a["topk"], a["dm"], a["dff"], a["ws"],
+                                     a["wsb"], None)
+
+    assert call(wg=None) == E_INV
+    assert call(ids=None) == E_INV
+    assert call(E=0) == E_INV
+    assert call(T=0) == E_INV
+    assert call(T=9) == E_UNS
+    assert call(topk=9) == E_UNS
+    assert call(dm=2500) == E_UNS
+    assert call(dff=700) == E_UNS
+    assert call(lay=5) == E_UNS
+    assert call(ws=None) == E_WS
+    assert call(wsb=ws_size - 1) == E_WS
+    assert call(ws=P + 64) == E_ALN
+    assert call(wg=P + 8) == E_ALN
+    assert call(wd=P + 2, lay=0) == E_ALN
+    assert call(wd=P + 8, lay=1) == E_ALN
+
+
+def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(qmv, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(qmv, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        qmv.lib()
+
+
+def test_binding_raises_qmv_error(L):
+    with pytest.raises(qmv.QmvError) as ei:
+        qmv.mmvq_q6k(P, 1, P, P, 16, 300, 1, stream=0)
+    assert ei.value.code == E_UNS
