@@ -182,6 +182,13 @@ int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down
 size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff);
 
 /* Diagnostics. */
+/* Streaming-read calibration: reads `bytes` (a multiple of 16) from src
+ * (16-byte aligned) with 16-byte loads over `blocks` (1..65535) workgroups of
+ * 256 threads and writes one XOR word per workgroup to sink (uint32
+ * [blocks]).  Its duration at a given size is the achievable read time the
+ * MMVQ kernels are measured against. */
+int qmv_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, void *stream);
+
 const char *qmv_strerror(int code);
 int qmv_last_hip_error(void);
 

@@ -26,9 +26,42 @@ namespace qmv {
 constexpr int kWave = 64;
 constexpr int kQ6Bytes = 210, kQ4Bytes = 144, kQ5Bytes = 176, kQ81Bytes = 36;
 
+// Lanes sharing a row: the largest of 64, 32, 16 (not above cap) that
+// divides the row's units with at least three units per lane, else 8.  A
+// function of the row length only, so every launch of a given K sums a row
+// in the same order.
+__host__ __device__ constexpr int choose_u(int units, int cap = 64) {
+    for (int U = 64; U >= 16; U /= 2)
+        if (U <= cap && units % U == 0 && units / U >= 3) return U;
+    return 8;
+}
+
+// Register steps staged per LDS sub-tile: the first sub-tile's activation
+// blocks must fit three per thread.
+__host__ __device__ constexpr int its_for(int IT, int N, int U, int SBPU, int nthr) {
+    int its = IT;
+    while (its > 1 && N * its * U * SBPU > 3 * nthr) its--;
+    return its;
+}
+
 // ---------------------------------------------------------------- basics
 __device__ __forceinline__ int sdot4(int a, int b, int c) {
     return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+#ifndef QMV_DOT_HEAD_ASM
+#define QMV_DOT_HEAD_ASM 1
+#endif
+// First dot of a chain (accumulator 0).  The compiler emits v_mov 0 +
+// v_dot4c for sdot4(a, b, 0); the three-operand form takes the 0 inline.
+__device__ __forceinline__ int sdot4_head(int a, int b) {
+#if QMV_DOT_HEAD_ASM
+    int d;
+    asm("v_dot4_i32_i8 %0, %1, %2, 0" : "=v"(d) : "v"(a), "v"(b));
+    return d;
+#else
+    return __builtin_amdgcn_sdot4(a, b, 0, false);
+#endif
 }
 
 __device__ __forceinline__ float half_to_float(uint32_t bits) {
@@ -75,19 +108,22 @@ __device__ __forceinline__ void lds_barrier() {
 // 16-byte arrays (conflict-free ds_read_b128 for consecutive blocks) and a
 // float pair: (d * dscale, d * sum(q)) where dscale is 1/4 for the Q6_K
 // 4x codes.
+// nb (blocks per column) is the tile's compile-time column stride, so every
+// read of column n is a constant offset from one per-lane address.
+template <int NB>
 struct ActTile {
+    static constexpr int nb = NB;
     uint4 *x0;
     uint4 *x1;
     float2 *f;
-    int nb;            // blocks per column in the tile
 };
 
-__device__ __forceinline__ ActTile act_tile(void *lds, int ncols, int nb) {
-    ActTile t;
+template <int NB>
+__device__ __forceinline__ ActTile<NB> act_tile(void *lds, int ncols) {
+    ActTile<NB> t;
     t.x0 = reinterpret_cast<uint4 *>(lds);
-    t.x1 = t.x0 + ncols * nb;
-    t.f = reinterpret_cast<float2 *>(t.x1 + ncols * nb);
-    t.nb = nb;
+    t.x1 = t.x0 + ncols * NB;
+    t.f = reinterpret_cast<float2 *>(t.x1 + ncols * NB);
     return t;
 }
 
@@ -103,28 +139,39 @@ __device__ __forceinline__ void act_load(ActRaw &r, const uint8_t *xq, int64_t b
     for (int i = 0; i < 9; i++) r.w[i] = p[i];
 }
 
-__device__ __forceinline__ void act_store(const ActTile &t, int idx, const ActRaw &r, float dscale) {
+// Stores one Q8_1 block into the tile; the exact quant sum (times d) is only
+// formed for the formats whose min term needs it.
+template <bool NEED_SUM, int NB>
+__device__ __forceinline__ void act_store(const ActTile<NB> &t, int idx, const ActRaw &r, float dscale) {
     uint4 a = make_uint4(r.w[1], r.w[2], r.w[3], r.w[4]);
     uint4 b = make_uint4(r.w[5], r.w[6], r.w[7], r.w[8]);
     float d = half_to_float(r.w[0]);
-    int s = 0;
+    float ds = 0.0f;
+    if constexpr (NEED_SUM) {
+        int s = 0;
 #pragma unroll
-    for (int i = 1; i < 9; i++) s = sdot4((int)r.w[i], 0x01010101, s);
+        for (int i = 1; i < 9; i++) s = sdot4((int)r.w[i], 0x01010101, s);
+        ds = d * (float)s;
+    }
     t.x0[idx] = a;
     t.x1[idx] = b;
-    t.f[idx] = make_float2(d * dscale, d * (float)s);
+    t.f[idx] = make_float2(d * dscale, ds);
 }
 
 // ------------------------------------------------------- format policies
 // Each policy defines:
 //   SBPU     sub-blocks per unit;   IT  units held in registers per lane
 //   Raw      registers of one unit; load(); dot<N>() accumulating into acc[N]
-//   DSCALE   scale applied to d_a when staged.
+//   DSCALE   scale applied to d_a when staged;  NEED_SUM  stage d_a * sum(q8).
 
 // Q6_K, planar layout (see qmv.h).  Codes are 4*(q6-32) as int8.
+#ifndef QMV_Q6P_IT
+#define QMV_Q6P_IT 5
+#endif
 struct Q6Planar {
-    static constexpr int SBPU = 1, IT = 5;
+    static constexpr int SBPU = 1, IT = QMV_Q6P_IT;
     static constexpr float DSCALE = 0.25f;
+    static constexpr bool NEED_SUM = false;
     struct Raw {
         uint4 a;
         uint2 b;
@@ -170,6 +217,7 @@ struct Q6Planar {
 struct Q6Gguf {
     static constexpr int SBPU = 1, IT = 2;
     static constexpr float DSCALE = 0.25f;
+    static constexpr bool NEED_SUM = false;
     struct Raw {
         uint32_t l[9], h[9];
         uint32_t sc, d, shift;   // shift: bit 0-4 realign shift, 8-9: c
@@ -210,32 +258,51 @@ struct Q6Gguf {
     }
 };
 
-// Shared dot product of the two Q6_K layouts for one unit and N columns.
-template <class F, int N, bool DUMP>
-__device__ __forceinline__ void q6_dot(const typename F::Raw &r, const ActTile &t, int tb,
-                                       float acc[N], int32_t *dump, int64_t dstride) {
-    int v[8];
-    F::codes(r, v);
-    int sc0 = sext8(r.sc, 0), sc1 = sext8(r.sc, 1);
-    float dw = half_to_float(r.d);
+// Q6_K dot products of one unit for P rows and N columns; each LDS read of
+// the activation serves all P rows, and column n+1 is read while column n is
+// computed.  Shared by the two Q6_K layouts.
+template <class F, int N, int P, bool DUMP, int NB>
+__device__ __forceinline__ void q6_dot(const typename F::Raw (&r)[P], const ActTile<NB> &t, int tb,
+                                       float (&acc)[P][N], int32_t *const (&dump)[P], const bool (&rok)[P],
+                                       int64_t dstride) {
+    int v[P][8], sc0[P], sc1[P];
+    float dw[P];
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+        F::codes(r[p], v[p]);
+        sc0[p] = sext8(r[p].sc, 0);
+        sc1[p] = sext8(r[p].sc, 1);
+        dw[p] = half_to_float(r[p].d);
+    }
+    uint4 nx0 = t.x0[tb], nx1 = t.x1[tb];
+    float nda = 0.0f;
+    if constexpr (!DUMP) nda = t.f[tb].x;
 #pragma unroll
     for (int n = 0; n < N; n++) {
-        uint4 x0 = t.x0[n * t.nb + tb];
-        uint4 x1 = t.x1[n * t.nb + tb];
-        int d0 = sdot4(v[0], (int)x0.x, 0);
-        d0 = sdot4(v[1], (int)x0.y, d0);
-        d0 = sdot4(v[2], (int)x0.z, d0);
-        d0 = sdot4(v[3], (int)x0.w, d0);
-        int d1 = sdot4(v[4], (int)x1.x, 0);
-        d1 = sdot4(v[5], (int)x1.y, d1);
-        d1 = sdot4(v[6], (int)x1.z, d1);
-        d1 = sdot4(v[7], (int)x1.w, d1);
-        int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact (|operands| < 2^23)
-        if constexpr (DUMP) {
-            dump[n * dstride] = isum4 >> 2;
-        } else {
-            float da = t.f[n * t.nb + tb].x;           // d_a / 4
-            acc[n] = __builtin_fmaf(dw * da, (float)isum4, acc[n]);
+        const uint4 x0 = nx0, x1 = nx1;
+        const float da = nda;                                     // d_a / 4
+        if (n + 1 < N) {
+            nx0 = t.x0[(n + 1) * NB + tb];
+            nx1 = t.x1[(n + 1) * NB + tb];
+            if constexpr (!DUMP) nda = t.f[(n + 1) * NB + tb].x;
+        }
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int d0 = sdot4_head(v[p][0], (int)x0.x);
+            d0 = sdot4(v[p][1], (int)x0.y, d0);
+            d0 = sdot4(v[p][2], (int)x0.z, d0);
+            d0 = sdot4(v[p][3], (int)x0.w, d0);
+            int d1 = sdot4_head(v[p][4], (int)x1.x);
+            d1 = sdot4(v[p][5], (int)x1.y, d1);
+            d1 = sdot4(v[p][6], (int)x1.z, d1);
+            d1 = sdot4(v[p][7], (int)x1.w, d1);
+            // 4 * isum, exact (|operands| < 2^23)
+            const int isum4 = __mul24(sc0[p], d0) + __mul24(sc1[p], d1);
+            if constexpr (DUMP) {
+                if (rok[p]) dump[p][n * dstride] = isum4 >> 2;
+            } else {
+                acc[p][n] = __builtin_fmaf(dw[p] * da, (float)isum4, acc[p][n]);
+            }
         }
     }
 }
@@ -247,6 +314,7 @@ template <bool FIVE>
 struct Q45 {
     static constexpr int SBPU = 2, IT = FIVE ? 3 : 4;
     static constexpr float DSCALE = 1.0f;
+    static constexpr bool NEED_SUM = true;
     static constexpr int BYTES = FIVE ? kQ5Bytes : kQ4Bytes;
     struct Raw {
         uint4 hdr, q0, q1;
@@ -284,62 +352,92 @@ __device__ __forceinline__ void q45_scale_min(const uint4 &hdr, int j, int &sc, 
     m = j < 4 ? ml : mh;
 }
 
-template <bool FIVE, int N, bool DUMP>
-__device__ __forceinline__ void q45_dot(const typename Q45<FIVE>::Raw &r, int unit, const ActTile &t,
-                                        int tb, float acc[N], int32_t *dump, int64_t dstride) {
-    int pp = unit & 3, j0 = 2 * pp, j1 = 2 * pp + 1;
-    uint32_t q[8] = {r.q0.x, r.q0.y, r.q0.z, r.q0.w, r.q1.x, r.q1.y, r.q1.z, r.q1.w};
-    int lo[8], hi[8];
-    if constexpr (FIVE) {
-        uint32_t h[8] = {r.h0.x, r.h0.y, r.h0.z, r.h0.w, r.h1.x, r.h1.y, r.h1.z, r.h1.w};
+template <bool FIVE, int N, int P, bool DUMP, int NB>
+__device__ __forceinline__ void q45_dot(const typename Q45<FIVE>::Raw (&r)[P], int unit, const ActTile<NB> &t,
+                                        int tb, float (&acc)[P][N], int32_t *const (&dump)[P],
+                                        const bool (&rok)[P], int64_t dstride) {
+    const int pp = unit & 3, j0 = 2 * pp, j1 = 2 * pp + 1;
+    int lo[P][8], hi[P][8], sc0[P], sc1[P];
+    float d[P], dmin[P], m0f[P], m1f[P];
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            lo[m] = (int)((q[m] & 0x0F0F0F0Fu) | (((h[m] >> j0) & 0x01010101u) << 4));
-            hi[m] = (int)(((q[m] >> 4) & 0x0F0F0F0Fu) | (((h[m] >> j1) & 0x01010101u) << 4));
-        }
-    } else {
+    for (int p = 0; p < P; p++) {
+        const uint32_t q[8] = {r[p].q0.x, r[p].q0.y, r[p].q0.z, r[p].q0.w,
+                               r[p].q1.x, r[p].q1.y, r[p].q1.z, r[p].q1.w};
+        if constexpr (FIVE) {
+            const uint32_t h[8] = {r[p].h0.x, r[p].h0.y, r[p].h0.z, r[p].h0.w,
+                                   r[p].h1.x, r[p].h1.y, r[p].h1.z, r[p].h1.w};
 #pragma unroll
-        for (int m = 0; m < 8; m++) {
-            lo[m] = (int)(q[m] & 0x0F0F0F0Fu);
-            hi[m] = (int)((q[m] >> 4) & 0x0F0F0F0Fu);
+            for (int m = 0; m < 8; m++) {
+                lo[p][m] = (int)((q[m] & 0x0F0F0F0Fu) | (((h[m] >> j0) & 0x01010101u) << 4));
+                hi[p][m] = (int)(((q[m] >> 4) & 0x0F0F0F0Fu) | (((h[m] >> j1) & 0x01010101u) << 4));
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; m++) {
+                lo[p][m] = (int)(q[m] & 0x0F0F0F0Fu);
+                hi[p][m] = (int)((q[m] >> 4) & 0x0F0F0F0Fu);
+            }
         }
+        int m0, m1;
+        q45_scale_min(r[p].hdr, j0, sc0[p], m0);
+        q45_scale_min(r[p].hdr, j1, sc1[p], m1);
+        d[p] = half_to_float(r[p].hdr.x);
+        dmin[p] = half_to_float(r[p].hdr.x >> 16);
+        m0f[p] = (float)m0;
+        m1f[p] = (float)m1;
     }
-    int sc0, m0, sc1, m1;
-    q45_scale_min(r.hdr, j0, sc0, m0);
-    q45_scale_min(r.hdr, j1, sc1, m1);
-    float d = half_to_float(r.hdr.x), dmin = half_to_float(r.hdr.x >> 16);
-    float m0f = (float)m0, m1f = (float)m1;
+    uint4 na0 = t.x0[tb], na1 = t.x1[tb], nb0 = t.x0[tb + 1], nb1 = t.x1[tb + 1];
+    float2 nfa = make_float2(0.0f, 0.0f), nfb = nfa;
+    if constexpr (!DUMP) {
+        nfa = t.f[tb];
+        nfb = t.f[tb + 1];
+    }
 #pragma unroll
     for (int n = 0; n < N; n++) {
-        const uint4 a0 = t.x0[n * t.nb + tb], a1 = t.x1[n * t.nb + tb];
-        const uint4 b0 = t.x0[n * t.nb + tb + 1], b1 = t.x1[n * t.nb + tb + 1];
-        int da = sdot4(lo[0], (int)a0.x, 0);
-        da = sdot4(lo[1], (int)a0.y, da);
-        da = sdot4(lo[2], (int)a0.z, da);
-        da = sdot4(lo[3], (int)a0.w, da);
-        da = sdot4(lo[4], (int)a1.x, da);
-        da = sdot4(lo[5], (int)a1.y, da);
-        da = sdot4(lo[6], (int)a1.z, da);
-        da = sdot4(lo[7], (int)a1.w, da);
-        int db = sdot4(hi[0], (int)b0.x, 0);
-        db = sdot4(hi[1], (int)b0.y, db);
-        db = sdot4(hi[2], (int)b0.z, db);
-        db = sdot4(hi[3], (int)b0.w, db);
-        db = sdot4(hi[4], (int)b1.x, db);
-        db = sdot4(hi[5], (int)b1.y, db);
-        db = sdot4(hi[6], (int)b1.z, db);
-        db = sdot4(hi[7], (int)b1.w, db);
-        if constexpr (DUMP) {
-            dump[n * dstride] = da;
-            dump[n * dstride + 1] = db;
-        } else {
-            float2 fa = t.f[n * t.nb + tb], fb = t.f[n * t.nb + tb + 1];
-            float s = fa.x * (float)__mul24(sc0, da);
-            s = __builtin_fmaf(fb.x, (float)__mul24(sc1, db), s);
-            float mm = m0f * fa.y;
-            mm = __builtin_fmaf(m1f, fb.y, mm);
-            acc[n] = __builtin_fmaf(d, s, acc[n]);
-            acc[n] = __builtin_fmaf(-dmin, mm, acc[n]);
+        const uint4 a0 = na0, a1 = na1, b0 = nb0, b1 = nb1;
+        const float2 fa = nfa, fb = nfb;
+        if (n + 1 < N) {                          // read column n+1 while computing n
+            const int o = (n + 1) * NB + tb;
+            na0 = t.x0[o];
+            na1 = t.x1[o];
+            nb0 = t.x0[o + 1];
+            nb1 = t.x1[o + 1];
+            if constexpr (!DUMP) {
+                nfa = t.f[o];
+                nfb = t.f[o + 1];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int da = sdot4_head(lo[p][0], (int)a0.x);
+            da = sdot4(lo[p][1], (int)a0.y, da);
+            da = sdot4(lo[p][2], (int)a0.z, da);
+            da = sdot4(lo[p][3], (int)a0.w, da);
+            da = sdot4(lo[p][4], (int)a1.x, da);
+            da = sdot4(lo[p][5], (int)a1.y, da);
+            da = sdot4(lo[p][6], (int)a1.z, da);
+            da = sdot4(lo[p][7], (int)a1.w, da);
+            int db = sdot4_head(hi[p][0], (int)b0.x);
+            db = sdot4(hi[p][1], (int)b0.y, db);
+            db = sdot4(hi[p][2], (int)b0.z, db);
+            db = sdot4(hi[p][3], (int)b0.w, db);
+            db = sdot4(hi[p][4], (int)b1.x, db);
+            db = sdot4(hi[p][5], (int)b1.y, db);
+            db = sdot4(hi[p][6], (int)b1.z, db);
+            db = sdot4(hi[p][7], (int)b1.w, db);
+            if constexpr (DUMP) {
+                if (rok[p]) {
+                    dump[p][n * dstride] = da;
+                    dump[p][n * dstride + 1] = db;
+                }
+            } else {
+                float s2 = fa.x * (float)__mul24(sc0[p], da);
+                s2 = __builtin_fmaf(fb.x, (float)__mul24(sc1[p], db), s2);
+                float mm = m0f[p] * fa.y;
+                mm = __builtin_fmaf(m1f[p], fb.y, mm);
+                acc[p][n] = __builtin_fmaf(d[p], s2, acc[p][n]);
+                acc[p][n] = __builtin_fmaf(-dmin[p], mm, acc[p][n]);
+            }
         }
     }
 }
@@ -348,26 +446,29 @@ template <class F>
 struct Dot;
 template <>
 struct Dot<Q6Planar> {
-    template <int N, bool DUMP>
-    __device__ __forceinline__ static void run(const Q6Planar::Raw &r, int, const ActTile &t, int tb,
-                                               float acc[N], int32_t *dump, int64_t ds) {
-        q6_dot<Q6Planar, N, DUMP>(r, t, tb, acc, dump, ds);
+    template <int N, int P, bool DUMP, int NB>
+    __device__ __forceinline__ static void run(const Q6Planar::Raw (&r)[P], int, const ActTile<NB> &t, int tb,
+                                               float (&acc)[P][N], int32_t *const (&dp)[P],
+                                               const bool (&rok)[P], int64_t ds) {
+        q6_dot<Q6Planar, N, P, DUMP, NB>(r, t, tb, acc, dp, rok, ds);
     }
 };
 template <>
 struct Dot<Q6Gguf> {
-    template <int N, bool DUMP>
-    __device__ __forceinline__ static void run(const Q6Gguf::Raw &r, int, const ActTile &t, int tb,
-                                               float acc[N], int32_t *dump, int64_t ds) {
-        q6_dot<Q6Gguf, N, DUMP>(r, t, tb, acc, dump, ds);
+    template <int N, int P, bool DUMP, int NB>
+    __device__ __forceinline__ static void run(const Q6Gguf::Raw (&r)[P], int, const ActTile<NB> &t, int tb,
+                                               float (&acc)[P][N], int32_t *const (&dp)[P],
+                                               const bool (&rok)[P], int64_t ds) {
+        q6_dot<Q6Gguf, N, P, DUMP, NB>(r, t, tb, acc, dp, rok, ds);
     }
 };
 template <bool FIVE>
 struct Dot<Q45<FIVE>> {
-    template <int N, bool DUMP>
-    __device__ __forceinline__ static void run(const typename Q45<FIVE>::Raw &r, int unit, const ActTile &t,
-                                               int tb, float acc[N], int32_t *dump, int64_t ds) {
-        q45_dot<FIVE, N, DUMP>(r, unit, t, tb, acc, dump, ds);
+    template <int N, int P, bool DUMP, int NB>
+    __device__ __forceinline__ static void run(const typename Q45<FIVE>::Raw (&r)[P], int unit,
+                                               const ActTile<NB> &t, int tb, float (&acc)[P][N],
+                                               int32_t *const (&dp)[P], const bool (&rok)[P], int64_t ds) {
+        q45_dot<FIVE, N, P, DUMP, NB>(r, unit, t, tb, acc, dp, rok, ds);
     }
 };
 
@@ -377,6 +478,7 @@ struct Dot<Q45<FIVE>> {
 struct Q4GateUp {
     static constexpr int SBPU = Q45<false>::SBPU, IT = Q45<false>::IT;
     static constexpr float DSCALE = 1.0f;
+    static constexpr bool NEED_SUM = true;
     using Raw = Q45<false>::Raw;
     Q45<false> g, u;
     int64_t base_row;   // first row of the expert in both tensors
@@ -388,10 +490,11 @@ struct Q4GateUp {
 };
 template <>
 struct Dot<Q4GateUp> {
-    template <int N, bool DUMP>
-    __device__ __forceinline__ static void run(const Q4GateUp::Raw &r, int unit, const ActTile &t, int tb,
-                                               float acc[N], int32_t *dump, int64_t ds) {
-        q45_dot<false, N, DUMP>(r, unit, t, tb, acc, dump, ds);
+    template <int N, int P, bool DUMP, int NB>
+    __device__ __forceinline__ static void run(const Q4GateUp::Raw (&r)[P], int unit, const ActTile<NB> &t,
+                                               int tb, float (&acc)[P][N], int32_t *const (&dp)[P],
+                                               const bool (&rok)[P], int64_t ds) {
+        q45_dot<false, N, P, DUMP, NB>(r, unit, t, tb, acc, dp, rok, ds);
     }
 };
 
@@ -455,110 +558,142 @@ __device__ __forceinline__ int64_t xcol_of(const MmvqArgs &a, int n) {
     return (int64_t)((a.colpack >> (8 * n)) & 255u) * a.xstride;
 }
 
-// Row of the calling lane inside a workgroup that starts at row0.
-template <int U>
-__device__ __forceinline__ int64_t lane_row(int64_t row0) {
+// p-th row of the calling lane in a workgroup that starts at row0: a wave
+// holds P groups of 64/U consecutive rows, lane l takes row l/U of each.
+template <int U, int P>
+__device__ __forceinline__ int64_t lane_row(int64_t row0, int p) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    return row0 + (int64_t)wave * (kWave / U) + lane / U;
+    return row0 + ((int64_t)wave * P + p) * (kWave / U) + lane / U;
 }
 
-// Computes N dot products for the rows of one workgroup (rows row0 ..;
-// lane_row<U>() names the calling lane's row) and leaves in acc[n] the full
-// sum for (lane's row, column n), identical in every lane of the row's
-// group.  lds holds at least N * its * U * SBPU * kActBytesPerBlock bytes.
-// Every thread of the workgroup must call it (it has barriers); it starts
-// with no barrier, so a caller that reuses lds must place one before.
-template <class F, int N, int U, bool DUMP>
+template <int U, int P>
+constexpr int kRowsPerWave = P * (kWave / U);
+
+// Computes N dot products for P rows per lane of one workgroup (rows
+// lane_row<U, P>(row0, p)) and leaves in acc[p][n] the full sum of (row p,
+// column n), identical in every lane of the row's group.  Rows at or past
+// a.rows compute on clamped data and must not be stored.  NTHR is the
+// workgroup size; lds holds at least
+// N * its_for(F::IT, N, U, F::SBPU, NTHR) * U * F::SBPU * kActBytesPerBlock
+// bytes.  Every thread of the workgroup must call it (it has barriers); it
+// starts with no barrier, so a caller that reuses lds must place one before.
+template <class F, int N, int U, int P, int NTHR, bool DUMP>
 __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
-                                          float acc[N]) {
+                                          float (&acc)[P][N]) {
     constexpr int IT = F::IT;
     constexpr int SBPU = F::SBPU;
+    constexpr int ITS = its_for(IT, N, U, SBPU, NTHR);   // register steps per LDS sub-tile
+    constexpr int TNB = ITS * U * SBPU;                  // tile column stride (blocks)
     constexpr int SI = 3;   // activation blocks per thread loaded ahead of the weights
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int tid = threadIdx.x;
     const int u = (tid & (kWave - 1)) % U;
-    const int64_t row = lane_row<U>(row0);
-    const bool row_ok = row < a.rows;
+    int64_t row[P];
+    bool rok[P];
+#pragma unroll
+    for (int p = 0; p < P; p++) {
+        row[p] = lane_row<U, P>(row0, p);
+        rok[p] = row[p] < a.rows;
+    }
     const int64_t nsb = a.K / 32;
     const int units = (int)(nsb / SBPU);
 
 #pragma unroll
-    for (int n = 0; n < N; n++) acc[n] = 0.0f;
+    for (int p = 0; p < P; p++)
+#pragma unroll
+        for (int n = 0; n < N; n++) acc[p][n] = 0.0f;
 
     for (int c0 = 0; c0 < units; c0 += U * IT) {            // register chunk
-        typename F::Raw r[IT];
+        typename F::Raw r[IT][P];
         bool ok[IT];
         int sub_sb0 = c0 * SBPU;
-        int sub_nsb = min(a.its * U * SBPU, (int)nsb - sub_sb0);
+        int sub_nsb = min(ITS * U * SBPU, (int)nsb - sub_sb0);
         int items = N * sub_nsb;
         if (c0 > 0) lds_barrier();
-        // activation loads are issued before the weight loads: loads retire
-        // in order, so waiting for them does not wait for the weights
+        // activation loads go first: loads retire in order, so waiting for
+        // them does not wait for the weight loads behind them.  The loads are
+        // unconditional (clamped index) so the order survives scheduling.
         ActRaw ar[SI];
 #pragma unroll
         for (int s = 0; s < SI; s++) {
-            // unconditional (clamped) so the loads stay ahead of the weights
-            int i = min(tid + s * nthr, items - 1);
-            int n = i / sub_nsb, b = i - n * sub_nsb;
+            const int i = min(tid + s * NTHR, items - 1);
+            const int n = i / sub_nsb, b = i - n * sub_nsb;
             act_load(ar[s], a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
         }
-        // keep every activation load ahead of the weight loads
         __builtin_amdgcn_sched_barrier(0);
-        // unconditional loads (out-of-range lanes read a clamped, valid
-        // address and ignore it): branches here would make the wait counts
-        // conservative and serialize the weight stream behind the tile
+        // weight loads, unconditional too (lanes past the end read a clamped,
+        // valid address and ignore it): branches here would make the wait
+        // counts conservative and serialize the stream behind the tile
+        int64_t lrow[P];
 #pragma unroll
-        for (int it = 0; it < IT; it++) {
-            int unit = c0 + u + U * it;
-            ok[it] = row_ok && unit < units;
-            fmt.load(r[it], row_ok ? row : a.rows - 1, min(unit, units - 1));
+        for (int p = 0; p < P; p++) lrow[p] = rok[p] ? row[p] : a.rows - 1;
+        if (c0 + U * IT <= units) {
+            // whole chunk in range: addresses are linear in it (constant offsets)
+#pragma unroll
+            for (int it = 0; it < IT; it++) {
+                ok[it] = true;
+#pragma unroll
+                for (int p = 0; p < P; p++) fmt.load(r[it][p], lrow[p], c0 + u + U * it);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < IT; it++) {
+                const int unit = c0 + u + U * it;
+                ok[it] = unit < units;
+#pragma unroll
+                for (int p = 0; p < P; p++) fmt.load(r[it][p], lrow[p], min(unit, units - 1));
+            }
         }
-        ActTile t = act_tile(lds, N, sub_nsb);
+        const ActTile<TNB> t = act_tile<TNB>(lds, N);
 #pragma unroll
         for (int s = 0; s < SI; s++) {
-            int i = tid + s * nthr;
-            if (i < items) act_store(t, i, ar[s], F::DSCALE);
+            const int i = tid + s * NTHR;
+            if (i < items) {
+                const int n = i / sub_nsb, b = i - n * sub_nsb;
+                act_store<F::NEED_SUM>(t, n * TNB + b, ar[s], F::DSCALE);
+            }
         }
-        for (int i = tid + SI * nthr; i < items; i += nthr) {
-            int n = i / sub_nsb, b = i - n * sub_nsb;
+        for (int i = tid + SI * NTHR; i < items; i += NTHR) {
+            const int n = i / sub_nsb, b = i - n * sub_nsb;
             ActRaw x;
             act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
-            act_store(t, i, x, F::DSCALE);
+            act_store<F::NEED_SUM>(t, n * TNB + b, x, F::DSCALE);
         }
         lds_barrier();
 
-        int it_lo = 0;
-        while (true) {
-            int it_hi = min(it_lo + a.its, IT);
 #pragma unroll
-            for (int it = 0; it < IT; it++) {
-                if (it < it_lo || it >= it_hi) continue;
+        for (int st = 0; st < IT; st += ITS) {
+            if (st > 0) {                                   // next LDS sub-tile
+                if (c0 + st * U >= units) break;
+                lds_barrier();
+                sub_sb0 = (c0 + st * U) * SBPU;
+                sub_nsb = min(ITS * U * SBPU, (int)nsb - sub_sb0);
+                items = N * sub_nsb;
+                for (int i = tid; i < items; i += NTHR) {
+                    const int n = i / sub_nsb, b = i - n * sub_nsb;
+                    ActRaw x;
+                    act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
+                    act_store<F::NEED_SUM>(t, n * TNB + b, x, F::DSCALE);
+                }
+                lds_barrier();
+            }
+#pragma unroll
+            for (int it = st; it < st + ITS && it < IT; it++) {
                 if (ok[it]) {
-                    int unit = c0 + u + U * it;
-                    int tb = (u + U * (it - it_lo)) * SBPU;
-                    int32_t *dp = nullptr;
-                    if constexpr (DUMP) dp = a.dump + row * nsb + (int64_t)unit * SBPU;
-                    Dot<F>::template run<N, DUMP>(r[it], unit, t, tb, acc, dp, a.rows * nsb);
+                    const int unit = c0 + u + U * it;
+                    const int tb = (u + U * (it - st)) * SBPU;
+                    int32_t *dp[P];
+#pragma unroll
+                    for (int p = 0; p < P; p++)
+                        dp[p] = DUMP ? a.dump + row[p] * nsb + (int64_t)unit * SBPU : nullptr;
+                    Dot<F>::template run<N, P, DUMP, TNB>(r[it], unit, t, tb, acc, dp, rok, a.rows * nsb);
                 }
             }
-            it_lo = it_hi;
-            if (it_lo >= IT || c0 + it_lo * U >= units) break;
-            // next LDS sub-tile of the same register chunk
-            lds_barrier();
-            sub_sb0 = (c0 + it_lo * U) * SBPU;
-            sub_nsb = min(a.its * U * SBPU, (int)nsb - sub_sb0);
-            items = N * sub_nsb;
-            t = act_tile(lds, N, sub_nsb);
-            for (int i = tid; i < items; i += nthr) {
-                int n = i / sub_nsb, b = i - n * sub_nsb;
-                ActRaw x;
-                act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
-                act_store(t, i, x, F::DSCALE);
-            }
-            lds_barrier();
         }
     }
 #pragma unroll
-    for (int n = 0; n < N; n++) acc[n] = group_sum<U>(acc[n]);
+    for (int p = 0; p < P; p++)
+#pragma unroll
+        for (int n = 0; n < N; n++) acc[p][n] = group_sum<U>(acc[p][n]);
 }
 
 }  // namespace qmv

@@ -4,30 +4,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device.hpp"
+
 namespace qmv {
 
 enum Fmt { FMT_Q6_PLANAR = 0, FMT_Q6_GGUF = 1, FMT_Q4 = 2, FMT_Q5 = 3 };
 
-// Lanes sharing a row: the largest of 64, 32, 16 (not above cap) that
-// divides the row's units with at least three units per lane, else 8.  A
-// function of the row length only, so every launch of a given K sums a row
-// in the same order.
-__host__ __device__ constexpr int choose_u(int units, int cap = 64) {
-    for (int U = 64; U >= 16; U /= 2)
-        if (U <= cap && units % U == 0 && units / U >= 3) return U;
-    return 8;
-}
-
-// Register steps staged per LDS sub-tile: the first sub-tile's activation
-// blocks must fit three per thread.
-__host__ __device__ constexpr int its_for(int IT, int N, int U, int SBPU, int nthr) {
-    int its = IT;
-    while (its > 1 && N * its * U * SBPU > 3 * nthr) its--;
-    return its;
-}
-
 hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t nblocks, hipStream_t s);
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t nblocks, hipStream_t s);
 
 hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int32_t *dump,

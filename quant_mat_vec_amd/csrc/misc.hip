@@ -111,6 +111,38 @@ __global__ __launch_bounds__(256) void k_unpack_q6k(const uint8_t *__restrict__ 
     blk[209] = src[208 * NB + 2 * t + 1];
 }
 
+// Streaming-read calibration: every thread issues four independent 16-byte
+// loads per step (grid-stride), folds them with XOR and leaves one word per
+// workgroup, so the compiler cannot drop the loads.
+__global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src, int64_t n16,
+                                                     uint32_t *__restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    __shared__ uint32_t red[256];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int k = 0; k < (int)blockDim.x; k++) r ^= red[k];
+        sink[blockIdx.x] = r;
+    }
+}
+
+hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s) {
+    hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint4 *>(src),
+                       bytes / 16, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t NB, hipStream_t s) {
     const int64_t grid = (NB * 8 + 255) / 256;
     hipLaunchKernelGGL(k_repack_q6k, dim3((unsigned)grid), dim3(256), 0, s, src, dst, NB);

@@ -8,32 +8,50 @@
 
 namespace qmv {
 
-constexpr int kDenseWaves = 4;
+#ifndef QMV_DENSE_WAVES
+#define QMV_DENSE_WAVES 4
+#endif
+#ifndef QMV_DENSE_P2_FROM
+#define QMV_DENSE_P2_FROM 9
+#endif
+constexpr int kDenseWaves = QMV_DENSE_WAVES;
 
-template <class F, int N, int U, bool DUMP>
-__global__ __launch_bounds__(kDenseWaves * kWave) void k_mmvq_dense(const void *__restrict__ w, MmvqArgs a,
-                                                                  float *__restrict__ out) {
+// Rows per lane: two from QMV_DENSE_P2_FROM columns on, where the activation
+// reads from LDS become the limit (it changes no row's summation order).
+template <int N>
+constexpr int kDenseP = N >= QMV_DENSE_P2_FROM ? 2 : 1;
+
+// W waves per workgroup; the kernel is compiled for up to kMaxDenseWaves.
+constexpr int kMaxDenseWaves = 10;
+
+template <class F, int N, int U, int W, bool DUMP>
+__global__ __launch_bounds__(kMaxDenseWaves * kWave) void k_mmvq_dense(const void *__restrict__ w, MmvqArgs a,
+                                                                     float *__restrict__ out) {
+    constexpr int P = kDenseP<N>;
     extern __shared__ __align__(16) uint8_t lds[];
     F fmt;
     fmt.init(w, a.rows, a.K);
-    const int64_t row0 = (int64_t)blockIdx.x * kDenseWaves * (kWave / U);
-    float acc[N];
-    mmvq_rows<F, N, U, DUMP>(fmt, a, row0, lds, acc);
+    const int64_t row0 = (int64_t)blockIdx.x * W * kRowsPerWave<U, P>;
+    float acc[P][N];
+    mmvq_rows<F, N, U, P, W * kWave, DUMP>(fmt, a, row0, lds, acc);
     if constexpr (!DUMP) {
-        const int64_t row = lane_row<U>(row0);
         const int u = (threadIdx.x & (kWave - 1)) % U;
-        if (row < a.rows) {
 #pragma unroll
-            for (int n = 0; n < N; n++)
-                if (u == n % U) out[(int64_t)n * a.rows + row] = acc[n];
+        for (int p = 0; p < P; p++) {
+            const int64_t row = lane_row<U, P>(row0, p);
+            if (row < a.rows) {
+#pragma unroll
+                for (int n = 0; n < N; n++)
+                    if (u == n % U) out[(int64_t)n * a.rows + row] = acc[p][n];
+            }
         }
     }
 }
 
-template <class F, int N, int U, bool DUMP>
-hipError_t launch_dense_nu(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                           hipStream_t s) {
-    constexpr int threads = kDenseWaves * kWave;
+template <class F, int N, int U, int W, bool DUMP>
+hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                            hipStream_t s) {
+    constexpr int threads = W * kWave;
     constexpr int its = its_for(F::IT, N, U, F::SBPU, threads);
     MmvqArgs a;
     a.xq = reinterpret_cast<const uint8_t *>(xq);
@@ -44,10 +62,27 @@ hipError_t launch_dense_nu(const void *w, const void *xq, float *out, int32_t *d
     a.xstride = K / 32;
     a.its = its;
     const size_t lds = (size_t)N * its * U * F::SBPU * kActBytesPerBlock;
-    const int64_t rpb = kDenseWaves * (kWave / U);
+    const int64_t rpb = W * kRowsPerWave<U, kDenseP<N>>;
     const int64_t grid = (rows + rpb - 1) / rpb;
-    hipLaunchKernelGGL((k_mmvq_dense<F, N, U, DUMP>), dim3((unsigned)grid), dim3(threads), lds, s, w, a, out);
+    hipLaunchKernelGGL((k_mmvq_dense<F, N, U, W, DUMP>), dim3((unsigned)grid), dim3(threads), lds, s, w, a, out);
     return hipGetLastError();
+}
+
+// Ten-wave workgroups for long rows (a wave holds at most two rows) when that
+// still gives about one workgroup per CU or more: the activation tile is then
+// staged once per CU rather than once per four waves.  Four-wave workgroups
+// otherwise.
+#ifndef QMV_DENSE_BIG_GRID
+#define QMV_DENSE_BIG_GRID 224
+#endif
+template <class F, int N, int U, bool DUMP>
+hipError_t launch_dense_nu(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                           hipStream_t s) {
+    constexpr int64_t rpb10 = kMaxDenseWaves * kRowsPerWave<U, kDenseP<N>>;
+    // measured: ten waves pay off where a wave holds one or two rows (long K)
+    if (!DUMP && kRowsPerWave<U, kDenseP<N>> <= 2 && (rows + rpb10 - 1) / rpb10 >= QMV_DENSE_BIG_GRID)
+        return launch_dense_nuw<F, N, U, kMaxDenseWaves, DUMP>(w, xq, out, dump, rows, K, s);
+    return launch_dense_nuw<F, N, U, kDenseWaves, DUMP>(w, xq, out, dump, rows, K, s);
 }
 
 template <class F, int U, bool DUMP>

@@ -124,17 +124,17 @@ __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t 
     a.xstride = m.d_model / 32;
     a.its = its;
     const int64_t row0 = (int64_t)tile * 2 * kGuRows;
-    float acc[N];
-    mmvq_rows<Q4GateUp, N, U, false>(f, a, row0, act, acc);
+    float acc[1][N];
+    mmvq_rows<Q4GateUp, N, U, 1, nthr, false>(f, a, row0, act, acc);
 
     const int lane = threadIdx.x & (kWave - 1), u = lane % U;
-    const int64_t vrow = lane_row<U>(row0);
+    const int64_t vrow = lane_row<U, 1>(row0, 0);
     float *hg = reinterpret_cast<float *>(m.ws + m.off_h);
 #pragma unroll
     for (int n = 0; n < N; n++) {
-        const float up = __shfl_down(acc[n], U);
+        const float up = __shfl_down(acc[0][n], U);
         if ((vrow & 1) == 0 && vrow < a.rows && u == n % U) {
-            const float g = acc[n];
+            const float g = acc[0][n];
             const float h = g / (1.0f + expf(-g)) * up;
             const int r = (int)((vrow - row0) >> 1);
             H[n * kGuRows + r] = h;
@@ -204,15 +204,15 @@ __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t *s
     a.xstride = m.d_ff / 32;
     a.its = its;
     const int64_t row0 = (int64_t)e * m.d_model + (int64_t)tile * kDnWaves * (kWave / U);
-    float acc[N];
-    mmvq_rows<F, N, U, false>(f, a, row0, lds, acc);
-    const int64_t row = lane_row<U>(row0);
+    float acc[1][N];
+    mmvq_rows<F, N, U, 1, nthr, false>(f, a, row0, lds, acc);
+    const int64_t row = lane_row<U, 1>(row0, 0);
     const int u = (threadIdx.x & (kWave - 1)) % U;
     float *y = reinterpret_cast<float *>(m.ws + m.off_y);
     if (row < a.rows) {
 #pragma unroll
         for (int n = 0; n < N; n++)
-            if (u == n % U) y[(int64_t)sl[n] * m.d_model + (row - (int64_t)e * m.d_model)] = acc[n];
+            if (u == n % U) y[(int64_t)sl[n] * m.d_model + (row - (int64_t)e * m.d_model)] = acc[0][n];
     }
 }
 

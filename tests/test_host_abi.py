@@ -26,7 +26,7 @@ def test_exports_every_declared_symbol(L):
     expected = {"quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
                 "unpack_q6k_planar", "mmvq_q6k_isums", "mmvq_q4k_isums", "mmvq_q5k_isums",
                 "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "qmv_strerror",
-                "qmv_last_hip_error"}
+                "qmv_last_hip_error", "qmv_stream_read"}
     assert expected <= set(names), set(names) ^ expected
     for n in names:
         assert hasattr(L, n), n
@@ -128,6 +128,15 @@ def test_moe_rejects_and_workspace(L):
     assert call(wg=P + 8) == E_ALN
     assert call(wd=P + 2, lay=0) == E_ALN
     assert call(wd=P + 8, lay=1) == E_ALN
+
+
+def test_stream_read_rejects(L):
+    f = L.qmv_stream_read
+    assert f(None, 4096, P, 8, None) == E_INV
+    assert f(P, 0, P, 8, None) == E_INV
+    assert f(P, 4096, P, 0, None) == E_INV
+    assert f(P, 4100, P, 8, None) == E_UNS
+    assert f(P + 4, 4096, P, 8, None) == E_ALN
 
 
 def test_binding_raises_on_missing_library(monkeypatch, tmp_path):
