@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark of the Q6_K MMVQ decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+
+Workload (one "step"): for each activation column count N in (1, 4, 8),
+quantize N fp32 columns to Q8_1 and run the planar Q6_K MMVQ of a
+10240 x 2560 (rows x cols) matrix -- the decode matrix the pages measure as
+"2560 x 10240" (n_in x n_out).  Weights are resident in HBM before timing and
+each launch reads a different copy out of 25 (538 MB, more than the 256 MB
+Infinity Cache), so every weight byte comes from HBM.
+
+Printed: one JSON line.  `value` is effective weight throughput over the
+whole step (weight bytes of the three products / step wall time, GB/s).
+`roofline` is for the dominant kernel (the MMVQ instantiation with the
+largest share of GPU time): algorithmic bytes per launch over its average
+launch time, from HIP events on its launch stream around graph replays of
+back-to-back launches.  The step itself is timed from HIP graph replays
+(events on the stream, and host wall time; the larger is used).  `cpu_baseline` times the CPU oracle on
+the same step.  `extras` holds per-N figures, the other shapes, the grouped
+MoE, a cache-warm figure (not HBM) and a plain device copy for calibration.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROWS, K = 10240, 2560
+# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
+# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on a
+# plain copy of known size (see the profiles directory); None when the kernel
+# changed after the counters were taken.
+TRAFFIC = {}
+NCOLS = (1, 4, 8)
+Q6K_BYTES = 210
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 * 2**20
+# pages' figures for this matrix (Arc A770, large-GRF launch, 1/4/8 columns):
+# 86.1, 92.9, 370.5 us per call
+PAGES_US = {1: 86.1, 4: 92.9, 8: 370.5}
+
+
+def weight_bytes(rows, k, per_block=Q6K_BYTES):
+    return rows * (k // 256) * per_block
+
+
+def alg_bytes(rows, k, n, per_block=Q6K_BYTES):
+    """Algorithmic bytes of one MMVQ launch: weights once, Q8_1 activations,
+    fp32 outputs."""
+    return weight_bytes(rows, k, per_block) + n * (k // 32) * 36 + 4 * n * rows
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=300)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--no-extras", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def timed_launches(torch, fn, n_iter, copies):
+    """Per-launch GPU time (us) from events around each launch; fn(buf)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_iter)]
+    for i in range(n_iter):
+        evs[i][0].record()
+        fn(copies[i % len(copies)])
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    return {"mean_us": sum(t) / len(t), "median_us": t[len(t) // 2], "p10_us": t[len(t) // 10],
+            "p90_us": t[(9 * len(t)) // 10]}
+
+
+def graph_avg_us(torch, calls, reps=6):
+    """Average device time per call (us): events on the current stream around
+    replays of a HIP graph holding the calls back to back."""
+    stream = torch.cuda.current_stream()
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph, stream=stream):
+        for c in calls:
+            c()
+    gph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        gph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (reps * len(calls))
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on one GPU only (the MMVQ would shard by output rows "
+              "across GPUs; no multi-GPU path is built). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quant_mat_vec_amd import qmv, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda:0"
+    # all work on one non-default stream (graph capture needs one; default
+    # priority, like every stream here)
+    torch.cuda.set_stream(torch.cuda.Stream())
+    PL = qmv.LAYOUT_PLANAR
+    g = synth.rng(synth.seed_for(1, 1, 8))
+    w_np = synth.q6k_blocks(g, ROWS, K)
+    x_np = synth.activations(g, 8, K)
+    wb = weight_bytes(ROWS, K)
+    ncopies = max(2, math.ceil(2 * MALL_BYTES / wb) + 1)
+    w_gguf = torch.from_numpy(w_np).to(dev)
+    base = torch.empty_like(w_gguf)
+    qmv.repack_q6k_planar(w_gguf, base, ROWS, K)
+    copies = [base.clone() for _ in range(ncopies)]
+    xd = torch.from_numpy(x_np).to(dev)
+    xq = torch.empty(8 * (K // 32) * 36, dtype=torch.uint8, device=dev)
+    out = torch.empty(8 * ROWS, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        for j, n in enumerate(NCOLS):
+            c = copies[(len(NCOLS) * i + j) % ncopies]
+            qmv.quantize_q8_1(xd, xq, K, n)
+            qmv.mmvq_q6k(c, PL, xq, out, ROWS, K, n)
+
+    # One HIP graph per rotation offset: step i replays graph i % ncopies, so
+    # exactly `steps` steps run with the weight copies rotating as in eager mode.
+    graphs = []
+    for i in range(ncopies):
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph, stream=stream):
+            step(i)
+        graphs.append(gph)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        graphs[i % ncopies].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        graphs[i % ncopies].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    wall_ms_per_step = (t1 - t0) * 1e3 / args.steps
+    step_bytes = wb * len(NCOLS)
+    value = step_bytes / (max(ms_per_step, wall_ms_per_step) * 1e-3) / 1e9
+
+    # Per-kernel average launch time: events on the launch stream around
+    # graph replays of back-to-back launches of one MMVQ instantiation
+    # (rotating copies), so host launch cost is excluded and only the device's
+    # per-launch time (kernel plus the dispatch gap between kernels) remains.
+    per_n = {}
+    reps, per_graph = 8, ncopies * 2
+    for n in NCOLS:
+        qmv.quantize_q8_1(xd, xq, K, n)
+        gph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gph, stream=stream):
+            for i in range(per_graph):
+                qmv.mmvq_q6k(copies[i % ncopies], PL, xq, out, ROWS, K, n)
+        gph.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            gph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        mean = a.elapsed_time(b) * 1e3 / (reps * per_graph)
+        per_n[n] = {"kernel": f"qmv::k_mmvq_dense<qmv::Q6Planar, {n}, 16, 4, false>",
+                    "avg_launch_us": round(mean, 3),
+                    "weight_GBps": round(wb / (mean * 1e-6) / 1e9, 1),
+                    "weight_frac_of_8TBps": round(wb / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "alg_bytes": alg_bytes(ROWS, K, n), "launches_timed": reps * per_graph}
+        del gph
+    dom = max(NCOLS, key=lambda n: per_n[n]["avg_launch_us"])
+    ach = alg_bytes(ROWS, K, dom) / (per_n[dom]["avg_launch_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": TRAFFIC.get(dom),
+                "kernel": per_n[dom]["kernel"], "ncols": dom,
+                "alg_bytes_per_launch": alg_bytes(ROWS, K, dom),
+                "avg_launch_us": per_n[dom]["avg_launch_us"]}
+
+    # eager launches with per-launch events (host launch path included)
+    eager = {}
+    for n in NCOLS:
+        qmv.quantize_q8_1(xd, xq, K, n)
+        r = timed_launches(torch, lambda c, n=n: qmv.mmvq_q6k(c, PL, xq, out, ROWS, K, n), 100, copies)
+        eager[str(n)] = round(r["mean_us"], 3)
+
+    # checksum of the last step's N=8 output bits (FNV-1a 32)
+    torch.cuda.synchronize()
+    ob = out.cpu().numpy().view(np.uint32)
+    h = np.uint32(2166136261)
+    for byte in ob.view(np.uint8)[:4096 * 4]:
+        h = np.uint32((int(h) ^ int(byte)) * 16777619 & 0xFFFFFFFF)
+
+    extras = {"per_ncols": {str(n): per_n[n] for n in NCOLS},
+              "eager_event_us_per_launch": eager,
+              "wall_ms_per_step": round(wall_ms_per_step, 4),
+              "weight_copies": ncopies, "weight_bytes_per_copy": wb,
+              "fnv1a32_out_prefix": int(h),
+              "pages_A770_us": PAGES_US}
+    if not args.no_extras:
+        extras.update(run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out))
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(np, synth, w_np, x_np, args.cpu_seconds)
+
+    pages_gbs = step_bytes / (sum(PAGES_US.values()) * 1e-6) / 1e9
+    line = {
+        "metric": "Q6_K MMVQ us/call and effective weight GB/s (% HBM peak) at 1/4/8 columns",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": round(value / pages_gbs, 2), "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "Q6_K MMVQ 10240x2560 (rows x cols), planar weights, 1/4/8 columns, "
+                               "Q8_1 quantize + MMVQ per column count, weights rotated over "
+                               f"{ncopies} HBM copies",
+                   "rows": ROWS, "cols": K, "ncols": list(NCOLS),
+                   "vs_baseline_basis": f"pages' A770 large-GRF figures for this matrix "
+                                        f"(86.1/92.9/370.5 us) = {pages_gbs:.1f} GB/s; other hardware, context"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line))
+
+
+def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
+    PL, GG = qmv.LAYOUT_PLANAR, qmv.LAYOUT_GGUF
+    ex = {}
+    it = 200
+    # cache-warm: the same buffer every launch (Infinity Cache / L2 resident)
+    warm = {}
+    for n in NCOLS:
+        qmv.quantize_q8_1(xd, xq, K, n)
+        us = graph_avg_us(torch, [lambda n=n: qmv.mmvq_q6k(base, PL, xq, out, ROWS, K, n)] * 52)
+        warm[str(n)] = {"avg_launch_us": round(us, 3),
+                        "weight_GBps_not_hbm": round(weight_bytes(ROWS, K) / (us * 1e-6) / 1e9, 1)}
+    ex["cache_warm_not_hbm"] = warm
+    # plain streaming reads and a device copy of the same bytes, rotated:
+    # the achievable ceiling at this size
+    wb = weight_bytes(ROWS, K)
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    us = graph_avg_us(torch, [lambda c=c: qmv.qmv_stream_read(c, wb // 16 * 16, sink, 2048) for c in copies * 2])
+    ex["stream_read_calibration"] = {"bytes": wb, "avg_launch_us": round(us, 3),
+                                     "read_GBps": round(wb / (us * 1e-6) / 1e9, 1)}
+    dst = torch.empty_like(base)
+    us = graph_avg_us(torch, [lambda c=c: dst.copy_(c) for c in copies * 2])
+    ex["copy_calibration"] = {"bytes_read": wb, "avg_launch_us": round(us, 3),
+                              "read_plus_write_GBps": round(2 * wb / (us * 1e-6) / 1e9, 1)}
+
+    def shape_case(kind, rows, k, ncols_list, layout=PL, seed=0):
+        g = synth.rng(seed)
+        per = {"q6k": 210, "q4k": 144, "q5k": 176}[kind]
+        w = torch.from_numpy(synth.blocks(kind, g, rows, k)).to(dev)
+        wbytes = weight_bytes(rows, k, per)
+        if kind == "q6k" and layout == PL:
+            p = torch.empty_like(w)
+            qmv.repack_q6k_planar(w, p, rows, k)
+            w = p
+        nc = max(2, math.ceil(2 * MALL_BYTES / wbytes) + 1)
+        cs = [w] + [w.clone() for _ in range(nc - 1)]
+        x = torch.from_numpy(synth.activations(g, max(ncols_list), k)).to(dev)
+        q = torch.empty(max(ncols_list) * (k // 32) * 36, dtype=torch.uint8, device=dev)
+        o = torch.empty(max(ncols_list) * rows, dtype=torch.float32, device=dev)
+        res = {}
+        for n in ncols_list:
+            qmv.quantize_q8_1(x, q, k, n)
+            if kind == "q6k":
+                fn = lambda c, n=n: qmv.mmvq_q6k(c, layout, q, o, rows, k, n)  # noqa: E731
+            elif kind == "q4k":
+                fn = lambda c, n=n: qmv.mmvq_q4k(c, q, o, rows, k, n)  # noqa: E731
+            else:
+                fn = lambda c, n=n: qmv.mmvq_q5k(c, q, o, rows, k, n)  # noqa: E731
+            calls = [lambda c=c, fn=fn: fn(c) for c in cs] * max(1, 40 // len(cs))
+            us = graph_avg_us(torch, calls, reps=4)
+            res[str(n)] = {"avg_launch_us": round(us, 3),
+                           "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1)}
+        del cs
+        torch.cuda.empty_cache()
+        return res
+
+    ex["q6k_2560x10240"] = shape_case("q6k", 2560, 10240, (1, 2, 4, 6, 8), seed=11)
+    ex["q6k_10240x2560_2_6cols"] = shape_case("q6k", 10240, 2560, (2, 6), seed=12)
+    ex["q6k_2560x2560"] = shape_case("q6k", 2560, 2560, (1,), seed=13)
+    ex["q6k_lm_head_151936x2560"] = shape_case("q6k", 151936, 2560, (1, 4), seed=14)
+    ex["q6k_lm_head_151936x2560_gguf"] = shape_case("q6k", 151936, 2560, (1, 4), layout=GG, seed=14)
+    for kind in ("q4k", "q5k"):
+        for (r_, k_) in ((12288, 2560), (6144, 2560), (2560, 6144), (512, 2560)):
+            ex[f"{kind}_{r_}x{k_}"] = shape_case(kind, r_, k_, (1, 4), seed=15 + r_)
+    ex["moe_e128_2560_768"] = moe_case(torch, np, qmv, synth, dev)
+    return ex
+
+
+def moe_case(torch, np, qmv, synth, dev):
+    E, DM, DFF, TOPK = 128, 2560, 768, 8
+    g = synth.rng(synth.seed_for(4, 0, 0))
+    gate, up, down = synth.moe_weights(g, E, DM, DFF)
+    gd, ud = torch.from_numpy(gate).to(dev), torch.from_numpy(up).to(dev)
+    dd = torch.from_numpy(down).to(dev)
+    dp = torch.empty_like(dd)
+    qmv.repack_q6k_planar(dd, dp, E * DM, DFF)
+    del dd
+    res = {}
+    per_expert = 2 * DFF * (DM // 256) * 144 + DM * (DFF // 256) * 210
+    for T in (1, 2, 4, 8):
+        sets = []
+        for s in range(8):                      # different routings (and so different experts)
+            ids, rw = synth.routing(synth.rng(1000 + 10 * T + s), T, E, TOPK)
+            x = synth.activations(synth.rng(2000 + 10 * T + s), T, DM)
+            xq = torch.empty(T * (DM // 32) * 36, dtype=torch.uint8, device=dev)
+            qmv.quantize_q8_1(torch.from_numpy(x).to(dev), xq, DM, T)
+            sets.append((torch.from_numpy(ids).to(dev), torch.from_numpy(rw).to(dev), xq,
+                         len(set(ids.reshape(-1).tolist()))))
+        wsb = qmv.grouped_expert_mmvq_workspace(E, T, TOPK, DM, DFF)
+        ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        o = torch.empty(T * DM, dtype=torch.float32, device=dev)
+
+        def fn(sidx):
+            ids, rw, xq, _ = sets[sidx]
+            qmv.grouped_expert_mmvq(gd, ud, dp, qmv.LAYOUT_PLANAR, xq, ids, rw, o, E, T, TOPK, DM, DFF, ws, wsb)
+
+        us = graph_avg_us(torch, [lambda i=i: fn(i) for i in range(len(sets))] * 4, reps=4)
+        hit = sum(s[3] for s in sets) / len(sets)
+        res[f"T{T}"] = {"avg_call_us_4_launches": round(us, 3), "experts_hit_avg": hit,
+                        "touched_weight_GBps": round(hit * per_expert / (us * 1e-6) / 1e9, 1)}
+    return res
+
+
+def cpu_baseline(np, synth, w_np, x_np, seconds):
+    """The CPU oracle (single-threaded scalar C, untuned) on the same step:
+    quantize N columns and the Q6_K product, N = 1, 4, 8, repeated for about
+    `seconds` of CPU time."""
+    import oracle as orc
+    reps, t_total = 0, 0.0
+    while t_total < seconds or reps == 0:
+        t0 = time.perf_counter()
+        for n in NCOLS:
+            xq = orc.quantize_q8_1(x_np[:n])
+            orc.mmvq("q6k", w_np, xq, ROWS, K)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    per_step = t_total / reps
+    return {"value": round(weight_bytes(ROWS, K) * len(NCOLS) / per_step / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"the full step (10240x2560 Q6_K, N=1,4,8, quantize + product), {reps} reps, "
+                      f"{per_step * 1e3:.1f} ms/step on one host core",
+            "ms_per_step": round(per_step * 1e3, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -36,12 +36,29 @@ __host__ __device__ constexpr int choose_u(int units, int cap = 64) {
     return 8;
 }
 
-// Register steps staged per LDS sub-tile: the first sub-tile's activation
-// blocks must fit three per thread.
+// Activation tile limits: bytes of LDS per workgroup (the device allows
+// 160 KB) and Q8_1 blocks each thread loads ahead of the weights.
+constexpr int kMaxTileBytes = 120 * 1024;
+constexpr int kMaxStageItems = 5;
+constexpr int kActBytesPerBlock = 40;
+
+// Register steps staged per LDS sub-tile: as many as fit both limits
+// (ideally all IT steps, so a register chunk needs one staging pass).  Large
+// workgroups keep to three staged blocks per thread: they run three waves per
+// SIMD, and the staging registers would not fit beside the weights.
 __host__ __device__ constexpr int its_for(int IT, int N, int U, int SBPU, int nthr) {
+    const int max_items = nthr > 256 ? 3 : kMaxStageItems;
     int its = IT;
-    while (its > 1 && N * its * U * SBPU > 3 * nthr) its--;
+    while (its > 1 && (N * its * U * SBPU > max_items * nthr ||
+                       N * its * U * SBPU * kActBytesPerBlock > kMaxTileBytes))
+        its--;
     return its;
+}
+
+// Register depth: three steps when a lane has at most three units of a row
+// (no clamped duplicate loads), else the format's own depth.
+__host__ __device__ constexpr int depth_for(int units, int U, int IT) {
+    return (units + U - 1) / U <= 3 ? 3 : IT;
 }
 
 // ---------------------------------------------------------------- basics
@@ -126,8 +143,6 @@ __device__ __forceinline__ ActTile<NB> act_tile(void *lds, int ncols) {
     t.f = reinterpret_cast<float2 *>(t.x1 + ncols * NB);
     return t;
 }
-
-constexpr int kActBytesPerBlock = 40;
 
 struct ActRaw {
     uint32_t w[9];
@@ -215,7 +230,7 @@ struct Q6Planar {
 // Q6_K, GGUF layout: 210-byte blocks, only 2-byte aligned; read as aligned
 // dwords and realigned with alignbit, then turned into the same 4x codes.
 struct Q6Gguf {
-    static constexpr int SBPU = 1, IT = 2;
+    static constexpr int SBPU = 1, IT = 3;
     static constexpr float DSCALE = 0.25f;
     static constexpr bool NEED_SUM = false;
     struct Raw {
@@ -312,7 +327,7 @@ __device__ __forceinline__ void q6_dot(const typename F::Raw (&r)[P], const ActT
 // low nibbles are sub-block 2p' and high nibbles sub-block 2p'+1.
 template <bool FIVE>
 struct Q45 {
-    static constexpr int SBPU = 2, IT = FIVE ? 3 : 4;
+    static constexpr int SBPU = 2, IT = 5;
     static constexpr float DSCALE = 1.0f;
     static constexpr bool NEED_SUM = true;
     static constexpr int BYTES = FIVE ? kQ5Bytes : kQ4Bytes;
@@ -504,10 +519,24 @@ struct Dot<Q4GateUp> {
 // fp16 d and s bits are returned in every lane.  d = amax/127 and x/d are
 // IEEE fp32 divisions, rounding is half away from zero, the fp16 stores
 // round to nearest even.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true)));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_iadd(int v) {
+    return v + __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ int q8_1_quantize32(float x, uint32_t &dbits, uint32_t &sbits) {
+    // max and sum over the 32 lanes: DPP inside each 16-lane row, then one
+    // exchange between the two rows (both orders give the same result)
     float a = fabsf(x);
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 32));
+    a = dpp_max<0xB1>(a);
+    a = dpp_max<0x4E>(a);
+    a = dpp_max<0x141>(a);
+    a = dpp_max<0x140>(a);
+    a = fmaxf(a, __shfl_xor(a, 16, 32));
     float d = a / 127.0f;
     int q = 0;
     if (d != 0.0f) {
@@ -516,8 +545,11 @@ __device__ __forceinline__ int q8_1_quantize32(float x, uint32_t &dbits, uint32_
         q = (int)r;
     }
     int s = q;
-#pragma unroll
-    for (int m = 16; m >= 1; m >>= 1) s += __shfl_xor(s, m, 32);
+    s = dpp_iadd<0xB1>(s);
+    s = dpp_iadd<0x4E>(s);
+    s = dpp_iadd<0x141>(s);
+    s = dpp_iadd<0x140>(s);
+    s += __shfl_xor(s, 16, 32);
     dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
     sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
     return q;
@@ -573,18 +605,18 @@ constexpr int kRowsPerWave = P * (kWave / U);
 // lane_row<U, P>(row0, p)) and leaves in acc[p][n] the full sum of (row p,
 // column n), identical in every lane of the row's group.  Rows at or past
 // a.rows compute on clamped data and must not be stored.  NTHR is the
-// workgroup size; lds holds at least
-// N * its_for(F::IT, N, U, F::SBPU, NTHR) * U * F::SBPU * kActBytesPerBlock
-// bytes.  Every thread of the workgroup must call it (it has barriers); it
+// workgroup size, IT the register depth (units per lane held at once); lds
+// holds at least N * its_for(IT, N, U, F::SBPU, NTHR) * U * F::SBPU *
+// kActBytesPerBlock bytes.  Every thread of the workgroup must call it (it has barriers); it
 // starts with no barrier, so a caller that reuses lds must place one before.
-template <class F, int N, int U, int P, int NTHR, bool DUMP>
+template <class F, int N, int U, int P, int NTHR, bool DUMP, int IT = F::IT>
 __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
                                           float (&acc)[P][N]) {
-    constexpr int IT = F::IT;
     constexpr int SBPU = F::SBPU;
     constexpr int ITS = its_for(IT, N, U, SBPU, NTHR);   // register steps per LDS sub-tile
     constexpr int TNB = ITS * U * SBPU;                  // tile column stride (blocks)
-    constexpr int SI = 3;   // activation blocks per thread loaded ahead of the weights
+    // activation blocks per thread loaded ahead of the weights
+    constexpr int SI = (N * TNB + NTHR - 1) / NTHR;
     const int tid = threadIdx.x;
     const int u = (tid & (kWave - 1)) % U;
     int64_t row[P];

@@ -10,6 +10,13 @@ namespace qmv {
 
 enum Fmt { FMT_Q6_PLANAR = 0, FMT_Q6_GGUF = 1, FMT_Q4 = 2, FMT_Q5 = 3 };
 
+// Lets a kernel use more than 64 KB of dynamic LDS (gfx950 allows 160 KB per
+// workgroup); a no-op below that.
+inline hipError_t allow_lds(const void *kernel, size_t bytes) {
+    if (bytes <= 65536) return hipSuccess;
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t nblocks, hipStream_t s);
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s);

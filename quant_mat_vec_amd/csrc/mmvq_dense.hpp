@@ -24,16 +24,16 @@ constexpr int kDenseP = N >= QMV_DENSE_P2_FROM ? 2 : 1;
 // W waves per workgroup; the kernel is compiled for up to kMaxDenseWaves.
 constexpr int kMaxDenseWaves = 10;
 
-template <class F, int N, int U, int W, bool DUMP>
-__global__ __launch_bounds__(kMaxDenseWaves * kWave) void k_mmvq_dense(const void *__restrict__ w, MmvqArgs a,
-                                                                     float *__restrict__ out) {
+template <class F, int N, int U, int W, int IT, bool DUMP>
+__global__ __launch_bounds__(W * kWave) void k_mmvq_dense(const void *__restrict__ w, MmvqArgs a,
+                                                        float *__restrict__ out) {
     constexpr int P = kDenseP<N>;
     extern __shared__ __align__(16) uint8_t lds[];
     F fmt;
     fmt.init(w, a.rows, a.K);
     const int64_t row0 = (int64_t)blockIdx.x * W * kRowsPerWave<U, P>;
     float acc[P][N];
-    mmvq_rows<F, N, U, P, W * kWave, DUMP>(fmt, a, row0, lds, acc);
+    mmvq_rows<F, N, U, P, W * kWave, DUMP, IT>(fmt, a, row0, lds, acc);
     if constexpr (!DUMP) {
         const int u = (threadIdx.x & (kWave - 1)) % U;
 #pragma unroll
@@ -48,11 +48,11 @@ __global__ __launch_bounds__(kMaxDenseWaves * kWave) void k_mmvq_dense(const voi
     }
 }
 
-template <class F, int N, int U, int W, bool DUMP>
+template <class F, int N, int U, int W, int IT, bool DUMP>
 hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                             hipStream_t s) {
     constexpr int threads = W * kWave;
-    constexpr int its = its_for(F::IT, N, U, F::SBPU, threads);
+    constexpr int its = its_for(IT, N, U, F::SBPU, threads);
     MmvqArgs a;
     a.xq = reinterpret_cast<const uint8_t *>(xq);
     a.dump = dump;
@@ -64,7 +64,10 @@ hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *
     const size_t lds = (size_t)N * its * U * F::SBPU * kActBytesPerBlock;
     const int64_t rpb = W * kRowsPerWave<U, kDenseP<N>>;
     const int64_t grid = (rows + rpb - 1) / rpb;
-    hipLaunchKernelGGL((k_mmvq_dense<F, N, U, W, DUMP>), dim3((unsigned)grid), dim3(threads), lds, s, w, a, out);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_dense<F, N, U, W, IT, DUMP>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mmvq_dense<F, N, U, W, IT, DUMP>), dim3((unsigned)grid), dim3(threads), lds, s, w, a,
+                       out);
     return hipGetLastError();
 }
 
@@ -75,14 +78,27 @@ hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *
 #ifndef QMV_DENSE_BIG_GRID
 #define QMV_DENSE_BIG_GRID 224
 #endif
+template <class F, int N, int U, int IT, bool DUMP>
+hipError_t launch_dense_nui(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                            hipStream_t s) {
+    // (not for Q5_K: its registers do not fit three waves per SIMD)
+    if constexpr (!DUMP && kRowsPerWave<U, kDenseP<N>> <= 2 && sizeof(typename F::Raw) <= 64) {
+        constexpr int64_t rpb10 = kMaxDenseWaves * kRowsPerWave<U, kDenseP<N>>;
+        if ((rows + rpb10 - 1) / rpb10 >= QMV_DENSE_BIG_GRID)
+            return launch_dense_nuw<F, N, U, kMaxDenseWaves, IT, DUMP>(w, xq, out, dump, rows, K, s);
+    }
+    return launch_dense_nuw<F, N, U, kDenseWaves, IT, DUMP>(w, xq, out, dump, rows, K, s);
+}
+
 template <class F, int N, int U, bool DUMP>
 hipError_t launch_dense_nu(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                            hipStream_t s) {
-    constexpr int64_t rpb10 = kMaxDenseWaves * kRowsPerWave<U, kDenseP<N>>;
-    // measured: ten waves pay off where a wave holds one or two rows (long K)
-    if (!DUMP && kRowsPerWave<U, kDenseP<N>> <= 2 && (rows + rpb10 - 1) / rpb10 >= QMV_DENSE_BIG_GRID)
-        return launch_dense_nuw<F, N, U, kMaxDenseWaves, DUMP>(w, xq, out, dump, rows, K, s);
-    return launch_dense_nuw<F, N, U, kDenseWaves, DUMP>(w, xq, out, dump, rows, K, s);
+    const int units = (int)(K / 32 / F::SBPU);
+    if constexpr (F::IT > 3) {
+        if (depth_for(units, U, F::IT) == 3)
+            return launch_dense_nui<F, N, U, 3, DUMP>(w, xq, out, dump, rows, K, s);
+    }
+    return launch_dense_nui<F, N, U, F::IT, DUMP>(w, xq, out, dump, rows, K, s);
 }
 
 template <class F, int U, bool DUMP>

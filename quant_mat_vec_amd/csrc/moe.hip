@@ -1,17 +1,17 @@
 // moe.hip -- grouped MoE-expert product over a window of routed tokens.
 //
-// Four launches on one stream, none needing a host synchronization:
-//   route   : one workgroup groups the T*topk slots by expert (ascending id,
-//             ascending slot inside a group) into the workspace tables;
-//   gate/up : workgroup (i, tile) takes the i-th hit expert and 32 rows of
-//             d_ff; gate and up are read once for all of the expert's tokens
-//             (the token count is the MMVQ column count, 1..8), then
-//             h = silu(g)*u and its Q8_1 block are written per slot;
-//   down    : workgroup (i, tile) takes the i-th hit expert and a row tile of
-//             d_model, Q6_K MMVQ over the expert's requantized slots;
+// Three launches on one stream, none needing a host synchronization:
+//   gate/up : workgroup (i, tile) looks at slot i (slot = t*topk + k); if
+//             slot i is the first slot routed to its expert e, it takes e and
+//             32 rows of d_ff: gate and up are read once for all of e's slots
+//             (their count is the MMVQ column count), then h = silu(g)*u and
+//             its Q8_1 block are written per slot.  Other workgroups exit.
+//   down    : the same selection, with a row tile of d_model: Q6_K MMVQ over
+//             the expert's requantized slots, y written per slot;
 //   combine : out[t] = sum over k, ascending, of route_w[t][k] * y[t][k].
-// Workgroups of experts that were not hit exit at once, so unrouted expert
-// weights are never read.
+// The selection is one wave ballot over the slot ids (S <= 64 = one wave),
+// and an expert's slots are taken in ascending slot order.  No workgroup
+// reads the weights of an expert no slot is routed to.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -31,52 +31,54 @@ MoeLayout moe_layout(int T, int topk, int64_t d_model, int64_t d_ff) {
     return L;
 }
 
-struct MoeTables {
-    const int32_t *expert, *count, *first, *slot_list;
-};
-
-__device__ __forceinline__ MoeTables moe_tables(const MoeArgs &m) {
-    const int32_t *wsi = reinterpret_cast<const int32_t *>(m.ws);
-    MoeTables t;
-    t.expert = wsi + 64;
-    t.count = t.expert + m.S;
-    t.first = t.count + m.S;
-    t.slot_list = t.first + m.S;
-    return t;
+// Slot selection shared by the gate/up and down kernels.  Every wave loads
+// the S slot ids (lane s holds ids[s], or -1 when out of range or s >= S).
+// Returns false when slot i is not the first slot of a valid expert; else
+// sets e and the mask of e's slots.
+__device__ __forceinline__ bool moe_select(const MoeArgs &m, int i, int &e, uint64_t &mask) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int id = -1;
+    if (lane < m.S) {
+        id = m.ids[lane];
+        if (id < 0 || id >= m.E) id = -1;
+    }
+    e = __builtin_amdgcn_readlane(id, i);
+    if (e < 0) return false;
+    mask = __ballot(id == e);
+    return (mask & ((1ull << i) - 1)) == 0;
 }
 
-// S <= 64 slots, one thread per slot.
-__global__ __launch_bounds__(64) void k_moe_route(MoeArgs m) {
-    __shared__ int es[64];
-    __shared__ int fo[64];
-    const int s = threadIdx.x;
+// Routing tables of the workspace (documented in qmv.h, for inspection):
+// written by one wave, each lane for its own slot.
+__device__ void moe_write_tables(const MoeArgs &m) {
+    const int s = threadIdx.x & (kWave - 1);
     int e = -1;
     if (s < m.S) {
         e = m.ids[s];
         if (e < 0 || e >= m.E) e = -1;
     }
-    es[s] = e;
-    __syncthreads();
+    const uint64_t valid = __ballot(e >= 0);
     bool first_occ = e >= 0;
-    for (int t = 0; t < s; t++)
-        if (es[t] == e) first_occ = false;
-    fo[s] = first_occ ? 1 : 0;
-    __syncthreads();
+    for (int t = 0; t < kWave; t++) {
+        const int et = __shfl(e, t);
+        if (et >= 0 && et == e && t < s) first_occ = false;
+    }
+    const uint64_t fo = __ballot(first_occ);
+    int before = 0, pos = 0, cnt = 0, rank = 0;
+    for (int t = 0; t < kWave; t++) {
+        const int et = __shfl(e, t);
+        if (et < 0 || e < 0) continue;
+        if (et < e) {
+            before++;
+            rank += (int)((fo >> t) & 1);
+        } else if (et == e) {
+            cnt++;
+            if (t < s) pos++;
+        }
+    }
     int32_t *wsi = reinterpret_cast<int32_t *>(m.ws);
     int32_t *expert = wsi + 64, *count = expert + m.S, *first = count + m.S, *slot_list = first + m.S;
     if (e >= 0) {
-        int before = 0, pos = 0, cnt = 0, rank = 0;
-        for (int t = 0; t < m.S; t++) {
-            const int et = es[t];
-            if (et < 0) continue;
-            if (et < e) {
-                before++;
-                rank += fo[t];
-            } else if (et == e) {
-                cnt++;
-                if (t < s) pos++;
-            }
-        }
         slot_list[before + pos] = s;
         if (first_occ) {
             expert[rank] = e;
@@ -85,13 +87,8 @@ __global__ __launch_bounds__(64) void k_moe_route(MoeArgs m) {
         }
     }
     if (s == 0) {
-        int nd = 0, bad = 0;
-        for (int t = 0; t < m.S; t++) {
-            nd += fo[t];
-            bad += es[t] < 0 ? 1 : 0;
-        }
-        wsi[0] = nd;
-        wsi[1] = bad;
+        wsi[0] = __popcll(fo);
+        wsi[1] = m.S - __popcll(valid);
     }
 }
 
@@ -99,7 +96,7 @@ __global__ __launch_bounds__(64) void k_moe_route(MoeArgs m) {
 constexpr int kGuRows = 32;   // real rows per workgroup: one Q8_1 block of h
 
 template <int N, int U>
-__device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t *slots, int tile,
+__device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t (&slots)[8], int tile,
                                          uint8_t *lds) {
     constexpr int nthr = U * kWave;
     constexpr int its = its_for(Q4GateUp::IT, N, U, Q4GateUp::SBPU, nthr);
@@ -159,15 +156,24 @@ __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t 
 template <int U>
 __global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int32_t *wsi = reinterpret_cast<const int32_t *>(m.ws);
-    const int i = blockIdx.x;
-    if (i >= wsi[0]) return;
-    const MoeTables tb = moe_tables(m);
-    const int e = tb.expert[i], c = tb.count[i], f = tb.first[i];
-    for (int c0 = 0; c0 < c; c0 += 8) {
-        if (c0 > 0) lds_barrier();
-        const int nc = min(8, c - c0);
-        const int32_t *sl = tb.slot_list + f + c0;
+    int e;
+    uint64_t mask;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kWave) moe_write_tables(m);
+    if (!moe_select(m, blockIdx.x, e, mask)) return;
+    int done = 0;
+    while (mask) {
+        if (done > 0) lds_barrier();
+        int32_t sl[8];
+        int nc = 0;
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            sl[n] = 0;
+            if (mask) {
+                sl[n] = __ffsll((long long)mask) - 1;
+                mask &= mask - 1;
+                nc++;
+            }
+        }
         switch (nc) {
         case 1: gateup_n<1, U>(m, e, sl, blockIdx.y, lds); break;
         case 2: gateup_n<2, U>(m, e, sl, blockIdx.y, lds); break;
@@ -178,16 +184,18 @@ __global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
         case 7: gateup_n<7, U>(m, e, sl, blockIdx.y, lds); break;
         default: gateup_n<8, U>(m, e, sl, blockIdx.y, lds); break;
         }
+        done += nc;
     }
 }
 
 // ------------------------------------------------------------------ down
 constexpr int kDnWaves = 4;
 
-template <class F, int N, int U>
-__device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t *slots, int tile, uint8_t *lds) {
+template <class F, int N, int U, int IT>
+__device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t (&slots)[8], int tile,
+                                       uint8_t *lds) {
     constexpr int nthr = kDnWaves * kWave;
-    constexpr int its = its_for(F::IT, N, U, F::SBPU, nthr);
+    constexpr int its = its_for(IT, N, U, F::SBPU, nthr);
     int sl[N];
 #pragma unroll
     for (int n = 0; n < N; n++) sl[n] = slots[n];
@@ -205,7 +213,7 @@ __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t *s
     a.its = its;
     const int64_t row0 = (int64_t)e * m.d_model + (int64_t)tile * kDnWaves * (kWave / U);
     float acc[1][N];
-    mmvq_rows<F, N, U, 1, nthr, false>(f, a, row0, lds, acc);
+    mmvq_rows<F, N, U, 1, nthr, false, IT>(f, a, row0, lds, acc);
     const int64_t row = lane_row<U, 1>(row0, 0);
     const int u = (threadIdx.x & (kWave - 1)) % U;
     float *y = reinterpret_cast<float *>(m.ws + m.off_y);
@@ -216,28 +224,37 @@ __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t *s
     }
 }
 
-template <class F, int U>
+template <class F, int U, int IT>
 __global__ __launch_bounds__(kDnWaves *kWave) void k_moe_down(MoeArgs m) {
     extern __shared__ __align__(16) uint8_t lds[];
-    const int32_t *wsi = reinterpret_cast<const int32_t *>(m.ws);
-    const int i = blockIdx.x;
-    if (i >= wsi[0]) return;
-    const MoeTables tb = moe_tables(m);
-    const int e = tb.expert[i], c = tb.count[i], f = tb.first[i];
-    for (int c0 = 0; c0 < c; c0 += 8) {
-        if (c0 > 0) lds_barrier();
-        const int nc = min(8, c - c0);
-        const int32_t *sl = tb.slot_list + f + c0;
-        switch (nc) {
-        case 1: down_n<F, 1, U>(m, e, sl, blockIdx.y, lds); break;
-        case 2: down_n<F, 2, U>(m, e, sl, blockIdx.y, lds); break;
-        case 3: down_n<F, 3, U>(m, e, sl, blockIdx.y, lds); break;
-        case 4: down_n<F, 4, U>(m, e, sl, blockIdx.y, lds); break;
-        case 5: down_n<F, 5, U>(m, e, sl, blockIdx.y, lds); break;
-        case 6: down_n<F, 6, U>(m, e, sl, blockIdx.y, lds); break;
-        case 7: down_n<F, 7, U>(m, e, sl, blockIdx.y, lds); break;
-        default: down_n<F, 8, U>(m, e, sl, blockIdx.y, lds); break;
+    int e;
+    uint64_t mask;
+    if (!moe_select(m, blockIdx.x, e, mask)) return;
+    int done = 0;
+    while (mask) {
+        if (done > 0) lds_barrier();
+        int32_t sl[8];
+        int nc = 0;
+#pragma unroll
+        for (int n = 0; n < 8; n++) {
+            sl[n] = 0;
+            if (mask) {
+                sl[n] = __ffsll((long long)mask) - 1;
+                mask &= mask - 1;
+                nc++;
+            }
         }
+        switch (nc) {
+        case 1: down_n<F, 1, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        case 2: down_n<F, 2, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        case 3: down_n<F, 3, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        case 4: down_n<F, 4, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        case 5: down_n<F, 5, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        case 6: down_n<F, 6, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        case 7: down_n<F, 7, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        default: down_n<F, 8, U, IT>(m, e, sl, blockIdx.y, lds); break;
+        }
+        done += nc;
     }
 }
 
@@ -273,20 +290,30 @@ static hipError_t launch_gateup(const MoeArgs &m, int smax, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <class F, int U>
-static hipError_t launch_down_u(const MoeArgs &m, int smax, hipStream_t s) {
+template <class F, int U, int IT>
+static hipError_t launch_down_ui(const MoeArgs &m, int smax, hipStream_t s) {
     constexpr int nthr = kDnWaves * kWave;
     size_t lds = 0;
     // largest tile over the column counts a workgroup may meet
     for (int n = 1; n <= 8; n++) {
-        int its = its_for(F::IT, n, U, F::SBPU, nthr);
+        int its = its_for(IT, n, U, F::SBPU, nthr);
         size_t b = (size_t)n * its * U * F::SBPU * kActBytesPerBlock;
         if (b > lds) lds = b;
     }
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_moe_down<F, U, IT>), lds);
+    if (e != hipSuccess) return e;
     const int64_t rpb = kDnWaves * (kWave / U);
-    hipLaunchKernelGGL((k_moe_down<F, U>), dim3(smax, (unsigned)((m.d_model + rpb - 1) / rpb)), dim3(nthr), lds,
-                       s, m);
+    hipLaunchKernelGGL((k_moe_down<F, U, IT>), dim3(smax, (unsigned)((m.d_model + rpb - 1) / rpb)), dim3(nthr),
+                       lds, s, m);
     return hipGetLastError();
+}
+
+template <class F, int U>
+static hipError_t launch_down_u(const MoeArgs &m, int smax, hipStream_t s) {
+    if constexpr (F::IT > 3) {
+        if (depth_for((int)(m.d_ff / 32), U, F::IT) == 3) return launch_down_ui<F, U, 3>(m, smax, s);
+    }
+    return launch_down_ui<F, U, F::IT>(m, smax, s);
 }
 
 template <class F>
@@ -300,11 +327,10 @@ static hipError_t launch_down(const MoeArgs &m, int smax, hipStream_t s) {
 }
 
 hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s) {
-    hipLaunchKernelGGL(k_moe_route, dim3(1), dim3(64), 0, s, m);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int smax = m.S < m.E ? m.S : m.E;
-    err = choose_u((int)(m.d_model / 64), 16) == 8 ? launch_gateup<8>(m, smax, s) : launch_gateup<16>(m, smax, s);
+    const int smax = m.S;   // one workgroup column per slot; non-first slots exit
+    // gate/up: eight lanes per row whatever d_model (512-thread workgroups
+    // keep the register budget of two waves per SIMD)
+    hipError_t err = launch_gateup<8>(m, smax, s);
     if (err != hipSuccess) return err;
     err = down_layout == 1 ? launch_down<Q6Planar>(m, smax, s) : launch_down<Q6Gguf>(m, smax, s);
     if (err != hipSuccess) return err;
