@@ -7,8 +7,8 @@ Workload (one "step"): for each activation column count N in (1, 4, 8),
 quantize N fp32 columns to Q8_1 and run the planar Q6_K MMVQ of a
 10240 x 2560 (rows x cols) matrix -- the decode matrix the pages measure as
 "2560 x 10240" (n_in x n_out).  Weights are resident in HBM before timing and
-each launch reads a different copy out of 25 (538 MB, more than the 256 MB
-Infinity Cache), so every weight byte comes from HBM.
+each launch reads a different one of 26 copies (559 MB, more than twice the
+256 MB Infinity Cache), so every weight byte comes from HBM.
 
 Printed: one JSON line.  `value` is effective weight throughput over the
 whole step (weight bytes of the three products / step wall time, GB/s).
@@ -32,9 +32,9 @@ import time
 ROWS, K = 10240, 2560
 # HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on a
-# plain copy of known size (see the profiles directory); None when the kernel
-# changed after the counters were taken.
-TRAFFIC = {}
+# plain copy of known size (FETCH_SIZE x 1.9977, WRITE_SIZE x 1.0); to be
+# emptied whenever the kernel changes after the counters were taken.
+TRAFFIC = {1: 21667516, 4: 21884410, 8: 22180194}
 NCOLS = (1, 4, 8)
 Q6K_BYTES = 210
 HBM_PEAK_GBS = 8000.0
@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--pmc-workload", action="store_true",
+                   help="only run 30 launches each of the N=1/4/8 products and of a 21.5 MB device "
+                        "copy (for rocprofv3 --pmc passes), print nothing")
     return p.parse_args()
 
 
@@ -132,6 +135,20 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+
+    if args.pmc_workload:
+        # fixed workload for hardware-counter passes: the three products on
+        # rotated copies, then a plain copy of the same size (its FETCH_SIZE /
+        # WRITE_SIZE calibrate the counters against known bytes)
+        for n in NCOLS:
+            qmv.quantize_q8_1(xd, xq, K, n)
+            for i in range(30):
+                qmv.mmvq_q6k(copies[i % ncopies], PL, xq, out, ROWS, K, n)
+        dst = torch.empty_like(base)
+        for i in range(30):
+            dst.copy_(copies[i % ncopies])
+        torch.cuda.synchronize()
+        return
 
     def step(i):
         for j, n in enumerate(NCOLS):
