@@ -183,10 +183,12 @@ size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, in
 
 /* Diagnostics. */
 /* Streaming-read calibration: reads `bytes` (a multiple of 16) from src
- * (16-byte aligned) with 16-byte loads over `blocks` (1..65535) workgroups of
- * 256 threads and writes one XOR word per workgroup to sink (uint32
- * [blocks]).  Its duration at a given size is the achievable read time the
- * MMVQ kernels are measured against. */
+ * (16-byte aligned) with 16-byte non-temporal loads, four per thread per
+ * step, over `blocks` (1..65535) workgroups of 256 threads, or, when blocks
+ * is 0, over one workgroup per 16 KiB so that each thread takes one step.
+ * sink (uint32, as many words as workgroups) is written only if a thread's
+ * XOR of its data equals a fixed constant.  Its duration at a given size is
+ * the achievable read time the MMVQ kernels are measured against. */
 int qmv_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, void *stream);
 
 const char *qmv_strerror(int code);

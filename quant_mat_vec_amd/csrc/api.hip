@@ -181,7 +181,7 @@ int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down
 }
 
 int qmv_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, void *stream) {
-    if (!src || !sink || bytes <= 0 || blocks <= 0) return QMV_ERR_INVALID_ARG;
+    if (!src || !sink || bytes <= 0 || blocks < 0) return QMV_ERR_INVALID_ARG;
     if (bytes % 16 != 0 || bytes >= kMaxBytes || blocks > 65535) return QMV_ERR_UNSUPPORTED;
     if (!aligned(src, 16) || !aligned(sink, 4)) return QMV_ERR_ALIGNMENT;
     return from_hip(qmv::launch_stream_read(src, bytes, sink, blocks, as_stream(stream)));

@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace qmv {
 
 constexpr int kWave = 64;
@@ -214,6 +216,30 @@ struct Q6Planar {
         r.sc = SC[i];
         r.d = D[i >> 3];
     }
+    // units unit0 + U*it (it < IT) of one row, all in range
+    template <int U, int IT, int P>
+    __device__ __forceinline__ void load_chunk(Raw (&r)[IT][P], int p, int64_t row, int unit0) const {
+        static_assert(U % 8 == 0, "d index shift");
+        const int64_t i0 = row * nsb + unit0;
+        const uint4 *pa = A + i0;
+        const uint2 *pb = B + i0;
+        const uint16_t *ps = SC + i0;
+        const uint16_t *pd = D + (i0 >> 3);
+        // the small scale and d loads first, then the code planes unit by
+        // unit, so unit it waits only for the loads of units 0..it
+#pragma unroll
+        for (int it = 0; it < IT; it++) {
+            r[it][p].sc = ps[U * it];
+            r[it][p].d = pd[(U / 8) * it];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int it = 0; it < IT; it++) {
+            r[it][p].a = pa[U * it];
+            r[it][p].b = pb[U * it];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
     __device__ __forceinline__ static void codes(const Raw &r, int v[8]) {
         const uint32_t m3 = 0x03030303u, mfc = 0xFCFCFCFCu;
         v[0] = (int)(r.a.x & mfc);
@@ -273,9 +299,10 @@ struct Q6Gguf {
     }
 };
 
-// Q6_K dot products of one unit for P rows and N columns; each LDS read of
-// the activation serves all P rows, and column n+1 is read while column n is
-// computed.  Shared by the two Q6_K layouts.
+// Q6_K dot products of one unit for P rows and N columns; the activation of
+// all N columns is read from LDS in one burst (one LDS latency per unit, not
+// per column), and each read serves all P rows.  Shared by the two Q6_K
+// layouts.
 template <class F, int N, int P, bool DUMP, int NB>
 __device__ __forceinline__ void q6_dot(const typename F::Raw (&r)[P], const ActTile<NB> &t, int tb,
                                        float (&acc)[P][N], int32_t *const (&dump)[P], const bool (&rok)[P],
@@ -289,18 +316,19 @@ __device__ __forceinline__ void q6_dot(const typename F::Raw (&r)[P], const ActT
         sc1[p] = sext8(r[p].sc, 1);
         dw[p] = half_to_float(r[p].d);
     }
-    uint4 nx0 = t.x0[tb], nx1 = t.x1[tb];
-    float nda = 0.0f;
-    if constexpr (!DUMP) nda = t.f[tb].x;
+    // all columns' activation for this unit in one burst of LDS reads
+    uint4 ax0[N], ax1[N];
+    float ada[N];
 #pragma unroll
     for (int n = 0; n < N; n++) {
-        const uint4 x0 = nx0, x1 = nx1;
-        const float da = nda;                                     // d_a / 4
-        if (n + 1 < N) {
-            nx0 = t.x0[(n + 1) * NB + tb];
-            nx1 = t.x1[(n + 1) * NB + tb];
-            if constexpr (!DUMP) nda = t.f[(n + 1) * NB + tb].x;
-        }
+        ax0[n] = t.x0[n * NB + tb];
+        ax1[n] = t.x1[n * NB + tb];
+        ada[n] = DUMP ? 0.0f : t.f[n * NB + tb].x;
+    }
+#pragma unroll
+    for (int n = 0; n < N; n++) {
+        const uint4 x0 = ax0[n], x1 = ax1[n];
+        const float da = ada[n];
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int d0 = sdot4_head(v[p][0], (int)x0.x);
@@ -570,6 +598,20 @@ __device__ __forceinline__ void q8_1_store32(uint8_t *blk, int i, int q, uint32_
     }
 }
 
+// Loads of one register chunk of one row: the policy's own chunk loader
+// where it has one (constant offsets from per-plane bases), unit by unit
+// otherwise.
+template <class F, int U, int IT, int P>
+__device__ __forceinline__ void load_chunk(const F &fmt, typename F::Raw (&r)[IT][P], int p, int64_t row,
+                                           int unit0) {
+    if constexpr (std::is_same<F, Q6Planar>::value) {
+        fmt.template load_chunk<U, IT, P>(r, p, row, unit0);
+    } else {
+#pragma unroll
+        for (int it = 0; it < IT; it++) fmt.load(r[it][p], row, unit0 + U * it);
+    }
+}
+
 // ------------------------------------------------------------- the core
 // Parameters of one MMVQ call as the kernel sees them.  Column n of the
 // activation starts at Q8_1 block ((colpack >> 8n) & 255) * xstride of xq
@@ -601,24 +643,127 @@ __device__ __forceinline__ int64_t lane_row(int64_t row0, int p) {
 template <int U, int P>
 constexpr int kRowsPerWave = P * (kWave / U);
 
+
+// One register chunk of a call: units c0 + u + U*it (it < IT) of each of the
+// lane's rows.  FULL: the chunk lies wholly inside the row, so every address
+// is a constant offset from a per-lane base and no bound is checked.
+template <bool FULL, class F, int N, int U, int P, int NTHR, bool DUMP, int IT>
+__device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void *lds, int c0, int units,
+                                           const int64_t (&row)[P], const bool (&rok)[P], float (&acc)[P][N]) {
+    constexpr int SBPU = F::SBPU;
+    constexpr int ITS = its_for(IT, N, U, SBPU, NTHR);   // register steps per LDS sub-tile
+    constexpr int TNB = ITS * U * SBPU;                  // tile column stride (blocks)
+    // activation blocks per thread loaded ahead of the weights; item i is
+    // block i % TNB of column i / TNB (a constant divisor)
+    constexpr int SI = (N * TNB + NTHR - 1) / NTHR;
+    const int tid = threadIdx.x;
+    const int u = (tid & (kWave - 1)) % U;
+    const int64_t nsb = a.K / 32;
+    typename F::Raw r[IT][P];
+    bool ok[IT];
+    int sub_sb0 = c0 * SBPU;
+    int sub_nsb = FULL ? TNB : min(TNB, (int)nsb - sub_sb0);
+    // activation loads go first: loads retire in order, so waiting for them
+    // does not wait for the weight loads behind them.  Unconditional (clamped
+    // index), so the order survives scheduling.
+    ActRaw ar[SI];
+#pragma unroll
+    for (int s = 0; s < SI; s++) {
+        const int i = min(tid + s * NTHR, N * TNB - 1), n = i / TNB;
+        const int b = FULL ? i - n * TNB : min(i - n * TNB, sub_nsb - 1);
+        act_load(ar[s], a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const ActTile<TNB> t = act_tile<TNB>(lds, N);
+    // One-workgroup-per-CU launches (long rows) stage the tile before any
+    // weight load is issued: the tile then arrives in about the unloaded
+    // latency instead of queueing behind the whole weight stream, and the
+    // dot products can start as the first weights land.  With several
+    // workgroups per CU the tile is staged behind the weight loads instead,
+    // so the stream starts at once.
+    constexpr bool ACT_FIRST = NTHR > 256;
+    if constexpr (ACT_FIRST) {
+#pragma unroll
+        for (int s = 0; s < SI; s++) {
+            const int i = tid + s * NTHR, n = i / TNB, b = i - n * TNB;
+            if (i < N * TNB && (FULL || b < sub_nsb)) act_store<F::NEED_SUM>(t, i, ar[s], F::DSCALE);
+        }
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // weight loads, unconditional too (lanes past the end read a clamped,
+    // valid address and ignore it): branches here would make the wait counts
+    // conservative and serialize the stream behind the tile
+    int64_t lrow[P];
+#pragma unroll
+    for (int p = 0; p < P; p++) lrow[p] = rok[p] ? row[p] : a.rows - 1;
+    if constexpr (FULL) {
+#pragma unroll
+        for (int it = 0; it < IT; it++) ok[it] = true;
+#pragma unroll
+        for (int p = 0; p < P; p++) load_chunk<F, U, IT, P>(fmt, r, p, lrow[p], c0 + u);
+    } else {
+#pragma unroll
+        for (int it = 0; it < IT; it++) {
+            const int unit = c0 + u + U * it;
+            ok[it] = unit < units;
+#pragma unroll
+            for (int p = 0; p < P; p++) fmt.load(r[it][p], lrow[p], min(unit, units - 1));
+        }
+    }
+    if constexpr (!ACT_FIRST) {
+#pragma unroll
+        for (int s = 0; s < SI; s++) {
+            const int i = tid + s * NTHR, n = i / TNB, b = i - n * TNB;
+            if (i < N * TNB && (FULL || b < sub_nsb)) act_store<F::NEED_SUM>(t, i, ar[s], F::DSCALE);
+        }
+        lds_barrier();
+    }
+
+#pragma unroll
+    for (int st = 0; st < IT; st += ITS) {
+        if (st > 0) {                                       // next LDS sub-tile
+            if (!FULL && c0 + st * U >= units) break;
+            lds_barrier();
+            sub_sb0 = (c0 + st * U) * SBPU;
+            sub_nsb = FULL ? TNB : min(TNB, (int)nsb - sub_sb0);
+            for (int i = tid; i < N * TNB; i += NTHR) {
+                const int n = i / TNB, b = i - n * TNB;
+                if (FULL || b < sub_nsb) {
+                    ActRaw x;
+                    act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
+                    act_store<F::NEED_SUM>(t, i, x, F::DSCALE);
+                }
+            }
+            lds_barrier();
+        }
+#pragma unroll
+        for (int it = st; it < st + ITS && it < IT; it++) {
+            if (FULL || ok[it]) {
+                const int unit = c0 + u + U * it;
+                const int tb = (u + U * (it - st)) * SBPU;
+                int32_t *dp[P];
+#pragma unroll
+                for (int p = 0; p < P; p++)
+                    dp[p] = DUMP ? a.dump + row[p] * nsb + (int64_t)unit * SBPU : nullptr;
+                Dot<F>::template run<N, P, DUMP, TNB>(r[it], unit, t, tb, acc, dp, rok, a.rows * nsb);
+            }
+        }
+    }
+}
+
 // Computes N dot products for P rows per lane of one workgroup (rows
 // lane_row<U, P>(row0, p)) and leaves in acc[p][n] the full sum of (row p,
 // column n), identical in every lane of the row's group.  Rows at or past
 // a.rows compute on clamped data and must not be stored.  NTHR is the
 // workgroup size, IT the register depth (units per lane held at once); lds
 // holds at least N * its_for(IT, N, U, F::SBPU, NTHR) * U * F::SBPU *
-// kActBytesPerBlock bytes.  Every thread of the workgroup must call it (it has barriers); it
-// starts with no barrier, so a caller that reuses lds must place one before.
+// kActBytesPerBlock bytes.  Every thread of the workgroup must call it (it
+// has barriers); it starts with no barrier, so a caller that reuses lds must
+// place one before.
 template <class F, int N, int U, int P, int NTHR, bool DUMP, int IT = F::IT>
 __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
                                           float (&acc)[P][N]) {
-    constexpr int SBPU = F::SBPU;
-    constexpr int ITS = its_for(IT, N, U, SBPU, NTHR);   // register steps per LDS sub-tile
-    constexpr int TNB = ITS * U * SBPU;                  // tile column stride (blocks)
-    // activation blocks per thread loaded ahead of the weights
-    constexpr int SI = (N * TNB + NTHR - 1) / NTHR;
-    const int tid = threadIdx.x;
-    const int u = (tid & (kWave - 1)) % U;
     int64_t row[P];
     bool rok[P];
 #pragma unroll
@@ -626,101 +771,21 @@ __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64
         row[p] = lane_row<U, P>(row0, p);
         rok[p] = row[p] < a.rows;
     }
-    const int64_t nsb = a.K / 32;
-    const int units = (int)(nsb / SBPU);
-
+    const int units = (int)(a.K / 32 / F::SBPU);
 #pragma unroll
     for (int p = 0; p < P; p++)
 #pragma unroll
         for (int n = 0; n < N; n++) acc[p][n] = 0.0f;
 
-    for (int c0 = 0; c0 < units; c0 += U * IT) {            // register chunk
-        typename F::Raw r[IT][P];
-        bool ok[IT];
-        int sub_sb0 = c0 * SBPU;
-        int sub_nsb = min(ITS * U * SBPU, (int)nsb - sub_sb0);
-        int items = N * sub_nsb;
-        if (c0 > 0) lds_barrier();
-        // activation loads go first: loads retire in order, so waiting for
-        // them does not wait for the weight loads behind them.  The loads are
-        // unconditional (clamped index) so the order survives scheduling.
-        ActRaw ar[SI];
-#pragma unroll
-        for (int s = 0; s < SI; s++) {
-            const int i = min(tid + s * NTHR, items - 1);
-            const int n = i / sub_nsb, b = i - n * sub_nsb;
-            act_load(ar[s], a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        // weight loads, unconditional too (lanes past the end read a clamped,
-        // valid address and ignore it): branches here would make the wait
-        // counts conservative and serialize the stream behind the tile
-        int64_t lrow[P];
-#pragma unroll
-        for (int p = 0; p < P; p++) lrow[p] = rok[p] ? row[p] : a.rows - 1;
-        if (c0 + U * IT <= units) {
-            // whole chunk in range: addresses are linear in it (constant offsets)
-#pragma unroll
-            for (int it = 0; it < IT; it++) {
-                ok[it] = true;
-#pragma unroll
-                for (int p = 0; p < P; p++) fmt.load(r[it][p], lrow[p], c0 + u + U * it);
-            }
-        } else {
-#pragma unroll
-            for (int it = 0; it < IT; it++) {
-                const int unit = c0 + u + U * it;
-                ok[it] = unit < units;
-#pragma unroll
-                for (int p = 0; p < P; p++) fmt.load(r[it][p], lrow[p], min(unit, units - 1));
-            }
-        }
-        const ActTile<TNB> t = act_tile<TNB>(lds, N);
-#pragma unroll
-        for (int s = 0; s < SI; s++) {
-            const int i = tid + s * NTHR;
-            if (i < items) {
-                const int n = i / sub_nsb, b = i - n * sub_nsb;
-                act_store<F::NEED_SUM>(t, n * TNB + b, ar[s], F::DSCALE);
-            }
-        }
-        for (int i = tid + SI * NTHR; i < items; i += NTHR) {
-            const int n = i / sub_nsb, b = i - n * sub_nsb;
-            ActRaw x;
-            act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
-            act_store<F::NEED_SUM>(t, n * TNB + b, x, F::DSCALE);
-        }
-        lds_barrier();
-
-#pragma unroll
-        for (int st = 0; st < IT; st += ITS) {
-            if (st > 0) {                                   // next LDS sub-tile
-                if (c0 + st * U >= units) break;
-                lds_barrier();
-                sub_sb0 = (c0 + st * U) * SBPU;
-                sub_nsb = min(ITS * U * SBPU, (int)nsb - sub_sb0);
-                items = N * sub_nsb;
-                for (int i = tid; i < items; i += NTHR) {
-                    const int n = i / sub_nsb, b = i - n * sub_nsb;
-                    ActRaw x;
-                    act_load(x, a.xq, xcol_of<N>(a, n) + sub_sb0 + b);
-                    act_store<F::NEED_SUM>(t, n * TNB + b, x, F::DSCALE);
-                }
-                lds_barrier();
-            }
-#pragma unroll
-            for (int it = st; it < st + ITS && it < IT; it++) {
-                if (ok[it]) {
-                    const int unit = c0 + u + U * it;
-                    const int tb = (u + U * (it - st)) * SBPU;
-                    int32_t *dp[P];
-#pragma unroll
-                    for (int p = 0; p < P; p++)
-                        dp[p] = DUMP ? a.dump + row[p] * nsb + (int64_t)unit * SBPU : nullptr;
-                    Dot<F>::template run<N, P, DUMP, TNB>(r[it], unit, t, tb, acc, dp, rok, a.rows * nsb);
-                }
-            }
-        }
+    constexpr int CH = U * IT;                              // units per register chunk
+    const int nfull = units / CH;
+    for (int c = 0; c < nfull; c++) {
+        if (c > 0) lds_barrier();
+        mmvq_chunk<true, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, c * CH, units, row, rok, acc);
+    }
+    if (nfull * CH < units) {                               // ragged last chunk
+        if (nfull > 0) lds_barrier();
+        mmvq_chunk<false, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, nfull * CH, units, row, rok, acc);
     }
 #pragma unroll
     for (int p = 0; p < P; p++)

@@ -111,35 +111,35 @@ __global__ __launch_bounds__(256) void k_unpack_q6k(const uint8_t *__restrict__ 
     blk[209] = src[208 * NB + 2 * t + 1];
 }
 
-// Streaming-read calibration: every thread issues four independent 16-byte
-// loads per step (grid-stride), folds them with XOR and leaves one word per
-// workgroup, so the compiler cannot drop the loads.
+// Streaming-read calibration: the fastest plain read of a buffer found on
+// this GPU.  Every thread issues four independent 16-byte non-temporal loads
+// per step (a grid-stride loop; with the default grid each thread takes one
+// step), folds them with XOR and stores only if the fold hits a fixed
+// value, so the loads stay live without write traffic.
 __global__ __launch_bounds__(256) void k_stream_read(const uint4 *__restrict__ src, int64_t n16,
                                                      uint32_t *__restrict__ sink) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(src);
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x * 4;
     uint32_t acc = 0;
-    for (; i + 3 * stride < n16; i += 4 * stride) {
-        const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x * 4 + threadIdx.x; i < n16; i += stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const int64_t j = min(i + (int64_t)k * blockDim.x, n16 - 1);
+            v[k] = __builtin_nontemporal_load(p + j);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;
     }
-    for (; i < n16; i += stride) {
-        const uint4 a = src[i];
-        acc ^= a.x ^ a.y ^ a.z ^ a.w;
-    }
-    __shared__ uint32_t red[256];
-    red[threadIdx.x] = acc;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = 0;
-        for (int k = 0; k < (int)blockDim.x; k++) r ^= red[k];
-        sink[blockIdx.x] = r;
-    }
+    if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s) {
-    hipLaunchKernelGGL(k_stream_read, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint4 *>(src),
-                       bytes / 16, sink);
+    const int64_t n16 = bytes / 16;
+    const int64_t grid = blocks > 0 ? blocks : (n16 + 1023) / 1024;
+    hipLaunchKernelGGL(k_stream_read, dim3((unsigned)grid), dim3(256), 0, s, reinterpret_cast<const uint4 *>(src),
+                       n16, sink);
     return hipGetLastError();
 }
 

@@ -35,15 +35,17 @@ __global__ __launch_bounds__(W * kWave) void k_mmvq_dense(const void *__restrict
     float acc[P][N];
     mmvq_rows<F, N, U, P, W * kWave, DUMP, IT>(fmt, a, row0, lds, acc);
     if constexpr (!DUMP) {
+        // every lane of a row holds all N sums; lane u < N of the row stores
+        // column u (U >= 8 >= N)
+        static_assert(U >= N, "one lane per column");
         const int u = (threadIdx.x & (kWave - 1)) % U;
 #pragma unroll
         for (int p = 0; p < P; p++) {
             const int64_t row = lane_row<U, P>(row0, p);
-            if (row < a.rows) {
+            float v = acc[p][0];
 #pragma unroll
-                for (int n = 0; n < N; n++)
-                    if (u == n % U) out[(int64_t)n * a.rows + row] = acc[p][n];
-            }
+            for (int n = 1; n < N; n++) v = u == n ? acc[p][n] : v;
+            if (row < a.rows && u < N) out[(int64_t)u * a.rows + row] = v;
         }
     }
 }
@@ -85,7 +87,8 @@ hipError_t launch_dense_nui(const void *w, const void *xq, float *out, int32_t *
     if constexpr (!DUMP && kRowsPerWave<U, kDenseP<N>> <= 2 && sizeof(typename F::Raw) <= 64) {
         constexpr int64_t rpb10 = kMaxDenseWaves * kRowsPerWave<U, kDenseP<N>>;
         if ((rows + rpb10 - 1) / rpb10 >= QMV_DENSE_BIG_GRID)
-            return launch_dense_nuw<F, N, U, kMaxDenseWaves, IT, DUMP>(w, xq, out, dump, rows, K, s);
+            // (seven columns at depth five do not fit 168 registers)
+            return launch_dense_nuw<F, N, U, kMaxDenseWaves, (N == 7 ? 3 : IT), DUMP>(w, xq, out, dump, rows, K, s);
     }
     return launch_dense_nuw<F, N, U, kDenseWaves, IT, DUMP>(w, xq, out, dump, rows, K, s);
 }

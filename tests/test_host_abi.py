@@ -134,7 +134,7 @@ def test_stream_read_rejects(L):
     f = L.qmv_stream_read
     assert f(None, 4096, P, 8, None) == E_INV
     assert f(P, 0, P, 8, None) == E_INV
-    assert f(P, 4096, P, 0, None) == E_INV
+    assert f(P, 4096, P, -1, None) == E_INV
     assert f(P, 4100, P, 8, None) == E_UNS
     assert f(P + 4, 4096, P, 8, None) == E_ALN
 
