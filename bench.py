@@ -367,7 +367,7 @@ def moe_case(torch, np, qmv, synth, dev):
 
         us = graph_avg_us(torch, [lambda i=i: fn(i) for i in range(len(sets))] * 4, reps=4)
         hit = sum(s[3] for s in sets) / len(sets)
-        res[f"T{T}"] = {"avg_call_us_4_launches": round(us, 3), "experts_hit_avg": hit,
+        res[f"T{T}"] = {"avg_call_us_3_launches": round(us, 3), "experts_hit_avg": hit,
                         "touched_weight_GBps": round(hit * per_expert / (us * 1e-6) / 1e9, 1)}
     return res
 

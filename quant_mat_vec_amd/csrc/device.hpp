@@ -527,7 +527,12 @@ struct Q4GateUp {
     int64_t base_row;   // first row of the expert in both tensors
 
     __device__ __forceinline__ void load(Raw &r, int64_t vrow, int unit) const {
-        const Q45<false> &m = (vrow & 1) ? u : g;
+        // select the base pointer, not the policy object (a runtime choice
+        // between two objects would put them in scratch memory)
+        const uintptr_t wg = reinterpret_cast<uintptr_t>(g.W), wu = reinterpret_cast<uintptr_t>(u.W);
+        Q45<false> m;
+        m.W = reinterpret_cast<const uint8_t *>(wg ^ ((wg ^ wu) & (uintptr_t)0 - (uintptr_t)(vrow & 1)));
+        m.nbk = g.nbk;
         m.load(r, base_row + (vrow >> 1), unit);
     }
 };
@@ -760,8 +765,10 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
 // holds at least N * its_for(IT, N, U, F::SBPU, NTHR) * U * F::SBPU *
 // kActBytesPerBlock bytes.  Every thread of the workgroup must call it (it
 // has barriers); it starts with no barrier, so a caller that reuses lds must
-// place one before.
-template <class F, int N, int U, int P, int NTHR, bool DUMP, int IT = F::IT>
+// place one before.  RAGGED = false: the caller guarantees that the row
+// length is a whole number of register chunks (K/32/SBPU % (U*IT) == 0), and
+// the ragged-chunk code is not compiled.
+template <class F, int N, int U, int P, int NTHR, bool DUMP, int IT = F::IT, bool RAGGED = true>
 __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
                                           float (&acc)[P][N]) {
     int64_t row[P];
@@ -783,9 +790,11 @@ __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64
         if (c > 0) lds_barrier();
         mmvq_chunk<true, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, c * CH, units, row, rok, acc);
     }
-    if (nfull * CH < units) {                               // ragged last chunk
-        if (nfull > 0) lds_barrier();
-        mmvq_chunk<false, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, nfull * CH, units, row, rok, acc);
+    if constexpr (RAGGED) {                                 // ragged last chunk
+        if (nfull * CH < units) {
+            if (nfull > 0) lds_barrier();
+            mmvq_chunk<false, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, nfull * CH, units, row, rok, acc);
+        }
     }
 #pragma unroll
     for (int p = 0; p < P; p++)

@@ -92,10 +92,21 @@ __device__ void moe_write_tables(const MoeArgs &m) {
     }
 }
 
+// Slot columns per pass of an expert's workgroup.  An expert with more
+// routed slots takes further passes, whose weight reads hit L2; few
+// column-count variants keep the kernels' register budget small (every
+// variant is inlined into the one kernel and the register count is that of
+// the union).
+#ifndef QMV_MOE_COLS
+#define QMV_MOE_COLS 2
+#endif
+constexpr int kMoeCols = QMV_MOE_COLS;
+static_assert(kMoeCols >= 1 && kMoeCols <= 4, "pass width");
+
 // ------------------------------------------------------------- gate / up
 constexpr int kGuRows = 32;   // real rows per workgroup: one Q8_1 block of h
 
-template <int N, int U>
+template <int N, int U, bool RAGGED>
 __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t (&slots)[8], int tile,
                                          uint8_t *lds) {
     constexpr int nthr = U * kWave;
@@ -122,7 +133,7 @@ __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t 
     a.its = its;
     const int64_t row0 = (int64_t)tile * 2 * kGuRows;
     float acc[1][N];
-    mmvq_rows<Q4GateUp, N, U, 1, nthr, false>(f, a, row0, act, acc);
+    mmvq_rows<Q4GateUp, N, U, 1, nthr, false, Q4GateUp::IT, RAGGED>(f, a, row0, act, acc);
 
     const int lane = threadIdx.x & (kWave - 1), u = lane % U;
     const int64_t vrow = lane_row<U, 1>(row0, 0);
@@ -153,7 +164,7 @@ __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t 
     }
 }
 
-template <int U>
+template <int U, bool RAGGED>
 __global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
     extern __shared__ __align__(16) uint8_t lds[];
     int e;
@@ -168,22 +179,16 @@ __global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
 #pragma unroll
         for (int n = 0; n < 8; n++) {
             sl[n] = 0;
-            if (mask) {
+            if (mask && n < kMoeCols) {
                 sl[n] = __ffsll((long long)mask) - 1;
                 mask &= mask - 1;
                 nc++;
             }
         }
-        switch (nc) {
-        case 1: gateup_n<1, U>(m, e, sl, blockIdx.y, lds); break;
-        case 2: gateup_n<2, U>(m, e, sl, blockIdx.y, lds); break;
-        case 3: gateup_n<3, U>(m, e, sl, blockIdx.y, lds); break;
-        case 4: gateup_n<4, U>(m, e, sl, blockIdx.y, lds); break;
-        case 5: gateup_n<5, U>(m, e, sl, blockIdx.y, lds); break;
-        case 6: gateup_n<6, U>(m, e, sl, blockIdx.y, lds); break;
-        case 7: gateup_n<7, U>(m, e, sl, blockIdx.y, lds); break;
-        default: gateup_n<8, U>(m, e, sl, blockIdx.y, lds); break;
-        }
+        if (nc == 1) gateup_n<1, U, RAGGED>(m, e, sl, blockIdx.y, lds);
+        if constexpr (kMoeCols >= 2) if (nc == 2) gateup_n<2, U, RAGGED>(m, e, sl, blockIdx.y, lds);
+        if constexpr (kMoeCols >= 3) if (nc == 3) gateup_n<3, U, RAGGED>(m, e, sl, blockIdx.y, lds);
+        if constexpr (kMoeCols >= 4) if (nc == 4) gateup_n<4, U, RAGGED>(m, e, sl, blockIdx.y, lds);
         done += nc;
     }
 }
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
 // ------------------------------------------------------------------ down
 constexpr int kDnWaves = 4;
 
-template <class F, int N, int U, int IT>
+template <class F, int N, int U, int IT, bool RAGGED>
 __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t (&slots)[8], int tile,
                                        uint8_t *lds) {
     constexpr int nthr = kDnWaves * kWave;
@@ -213,7 +218,7 @@ __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t (&
     a.its = its;
     const int64_t row0 = (int64_t)e * m.d_model + (int64_t)tile * kDnWaves * (kWave / U);
     float acc[1][N];
-    mmvq_rows<F, N, U, 1, nthr, false, IT>(f, a, row0, lds, acc);
+    mmvq_rows<F, N, U, 1, nthr, false, IT, RAGGED>(f, a, row0, lds, acc);
     const int64_t row = lane_row<U, 1>(row0, 0);
     const int u = (threadIdx.x & (kWave - 1)) % U;
     float *y = reinterpret_cast<float *>(m.ws + m.off_y);
@@ -224,7 +229,7 @@ __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t (&
     }
 }
 
-template <class F, int U, int IT>
+template <class F, int U, int IT, bool RAGGED>
 __global__ __launch_bounds__(kDnWaves *kWave) void k_moe_down(MoeArgs m) {
     extern __shared__ __align__(16) uint8_t lds[];
     int e;
@@ -238,74 +243,94 @@ __global__ __launch_bounds__(kDnWaves *kWave) void k_moe_down(MoeArgs m) {
 #pragma unroll
         for (int n = 0; n < 8; n++) {
             sl[n] = 0;
-            if (mask) {
+            if (mask && n < kMoeCols) {
                 sl[n] = __ffsll((long long)mask) - 1;
                 mask &= mask - 1;
                 nc++;
             }
         }
-        switch (nc) {
-        case 1: down_n<F, 1, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        case 2: down_n<F, 2, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        case 3: down_n<F, 3, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        case 4: down_n<F, 4, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        case 5: down_n<F, 5, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        case 6: down_n<F, 6, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        case 7: down_n<F, 7, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        default: down_n<F, 8, U, IT>(m, e, sl, blockIdx.y, lds); break;
-        }
+        if (nc == 1) down_n<F, 1, U, IT, RAGGED>(m, e, sl, blockIdx.y, lds);
+        if constexpr (kMoeCols >= 2) if (nc == 2) down_n<F, 2, U, IT, RAGGED>(m, e, sl, blockIdx.y, lds);
+        if constexpr (kMoeCols >= 3) if (nc == 3) down_n<F, 3, U, IT, RAGGED>(m, e, sl, blockIdx.y, lds);
+        if constexpr (kMoeCols >= 4) if (nc == 4) down_n<F, 4, U, IT, RAGGED>(m, e, sl, blockIdx.y, lds);
         done += nc;
     }
 }
 
 // --------------------------------------------------------------- combine
+// out[t][i] = sum over k ascending of route_w[t][k] * y[t*topk+k][i]; slots
+// with an out-of-range id add nothing.  All ids, weights and y values are
+// loaded before the sum (one round of memory latency, not topk).
 __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs m) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int t = blockIdx.y;
     if (i >= m.d_model) return;
     const float *y = reinterpret_cast<const float *>(m.ws + m.off_y);
-    float acc = 0.0f;
-    for (int k = 0; k < m.topk; k++) {
-        const int s = t * m.topk + k;
-        const int e = m.ids[s];
-        if (e < 0 || e >= m.E) continue;
-        acc = __builtin_fmaf(m.route_w[s], y[(int64_t)s * m.d_model + i], acc);
+    int e[8];
+    float w[8], v[8];
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+        const int s = t * m.topk + min(k, m.topk - 1);
+        e[k] = m.ids[s];
+        w[k] = m.route_w[s];
+        v[k] = y[(int64_t)s * m.d_model + i];
     }
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; k++)
+        if (k < m.topk && e[k] >= 0 && e[k] < m.E) acc = __builtin_fmaf(w[k], v[k], acc);
     m.out[(int64_t)t * m.d_model + i] = acc;
 }
 
 // ------------------------------------------------------------------ host
-template <int U>
-static hipError_t launch_gateup(const MoeArgs &m, int smax, hipStream_t s) {
+template <int U, bool RAGGED>
+static hipError_t launch_gateup_r(const MoeArgs &m, int smax, hipStream_t s) {
     constexpr int nthr = U * kWave;
     size_t act = 0;
     // largest tile over the column counts a workgroup may meet
-    for (int n = 1; n <= 8; n++) {
+    for (int n = 1; n <= kMoeCols; n++) {
         size_t b = (size_t)n * its_for(Q4GateUp::IT, n, U, Q4GateUp::SBPU, nthr) * U * Q4GateUp::SBPU *
                    kActBytesPerBlock;
         if (b > act) act = b;
     }
     const size_t lds = 8 * kGuRows * sizeof(float) + act;
-    hipLaunchKernelGGL((k_moe_gateup<U>), dim3(smax, (unsigned)(m.d_ff / kGuRows)), dim3(nthr), lds, s, m);
+    hipLaunchKernelGGL((k_moe_gateup<U, RAGGED>), dim3(smax, (unsigned)(m.d_ff / kGuRows)), dim3(nthr), lds, s,
+                       m);
+    return hipGetLastError();
+}
+
+// Rows that are a whole number of register chunks use the kernels without
+// the ragged-chunk code (fewer registers).
+template <int U>
+static hipError_t launch_gateup(const MoeArgs &m, int smax, hipStream_t s) {
+    const int units = (int)(m.d_model / 32 / Q4GateUp::SBPU);
+    return units % (U * Q4GateUp::IT) == 0 ? launch_gateup_r<U, false>(m, smax, s)
+                                           : launch_gateup_r<U, true>(m, smax, s);
+}
+
+template <class F, int U, int IT, bool RAGGED>
+static hipError_t launch_down_r(const MoeArgs &m, int smax, hipStream_t s) {
+    constexpr int nthr = kDnWaves * kWave;
+    size_t lds = 0;
+    // largest tile over the column counts a workgroup may meet
+    for (int n = 1; n <= kMoeCols; n++) {
+        int its = its_for(IT, n, U, F::SBPU, nthr);
+        size_t b = (size_t)n * its * U * F::SBPU * kActBytesPerBlock;
+        if (b > lds) lds = b;
+    }
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_moe_down<F, U, IT, RAGGED>), lds);
+    if (e != hipSuccess) return e;
+    const int64_t rpb = kDnWaves * (kWave / U);
+    hipLaunchKernelGGL((k_moe_down<F, U, IT, RAGGED>), dim3(smax, (unsigned)((m.d_model + rpb - 1) / rpb)),
+                       dim3(nthr), lds, s, m);
     return hipGetLastError();
 }
 
 template <class F, int U, int IT>
 static hipError_t launch_down_ui(const MoeArgs &m, int smax, hipStream_t s) {
-    constexpr int nthr = kDnWaves * kWave;
-    size_t lds = 0;
-    // largest tile over the column counts a workgroup may meet
-    for (int n = 1; n <= 8; n++) {
-        int its = its_for(IT, n, U, F::SBPU, nthr);
-        size_t b = (size_t)n * its * U * F::SBPU * kActBytesPerBlock;
-        if (b > lds) lds = b;
-    }
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_moe_down<F, U, IT>), lds);
-    if (e != hipSuccess) return e;
-    const int64_t rpb = kDnWaves * (kWave / U);
-    hipLaunchKernelGGL((k_moe_down<F, U, IT>), dim3(smax, (unsigned)((m.d_model + rpb - 1) / rpb)), dim3(nthr),
-                       lds, s, m);
-    return hipGetLastError();
+    const int units = (int)(m.d_ff / 32 / F::SBPU);
+    return units % (U * IT) == 0 ? launch_down_r<F, U, IT, false>(m, smax, s)
+                                 : launch_down_r<F, U, IT, true>(m, smax, s);
 }
 
 template <class F, int U>
