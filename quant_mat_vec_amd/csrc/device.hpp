@@ -217,7 +217,9 @@ struct Q6Planar {
         r.d = D[i >> 3];
     }
     // units unit0 + U*it (it < IT) of one row, all in range
-    template <int U, int IT, int P>
+    // units unit0 + U*it, it in [B0, B1), of one row, all in range; SCD: also
+    // the scale and d loads of all IT units (issued first)
+    template <int U, int IT, int P, int B0, int B1, bool SCD>
     __device__ __forceinline__ void load_chunk(Raw (&r)[IT][P], int p, int64_t row, int unit0) const {
         static_assert(U % 8 == 0, "d index shift");
         const int64_t i0 = row * nsb + unit0;
@@ -227,14 +229,16 @@ struct Q6Planar {
         const uint16_t *pd = D + (i0 >> 3);
         // the small scale and d loads first, then the code planes unit by
         // unit, so unit it waits only for the loads of units 0..it
+        if constexpr (SCD) {
 #pragma unroll
-        for (int it = 0; it < IT; it++) {
-            r[it][p].sc = ps[U * it];
-            r[it][p].d = pd[(U / 8) * it];
+            for (int it = 0; it < IT; it++) {
+                r[it][p].sc = ps[U * it];
+                r[it][p].d = pd[(U / 8) * it];
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int it = 0; it < IT; it++) {
+        for (int it = B0; it < B1; it++) {
             r[it][p].a = pa[U * it];
             r[it][p].b = pb[U * it];
             __builtin_amdgcn_sched_barrier(0);
@@ -606,14 +610,14 @@ __device__ __forceinline__ void q8_1_store32(uint8_t *blk, int i, int q, uint32_
 // Loads of one register chunk of one row: the policy's own chunk loader
 // where it has one (constant offsets from per-plane bases), unit by unit
 // otherwise.
-template <class F, int U, int IT, int P>
+template <class F, int U, int IT, int P, int B0 = 0, int B1 = IT, bool SCD = true>
 __device__ __forceinline__ void load_chunk(const F &fmt, typename F::Raw (&r)[IT][P], int p, int64_t row,
                                            int unit0) {
     if constexpr (std::is_same<F, Q6Planar>::value) {
-        fmt.template load_chunk<U, IT, P>(r, p, row, unit0);
+        fmt.template load_chunk<U, IT, P, B0, B1, SCD>(r, p, row, unit0);
     } else {
 #pragma unroll
-        for (int it = 0; it < IT; it++) fmt.load(r[it][p], row, unit0 + U * it);
+        for (int it = B0; it < B1; it++) fmt.load(r[it][p], row, unit0 + U * it);
     }
 }
 
@@ -649,6 +653,11 @@ template <int U, int P>
 constexpr int kRowsPerWave = P * (kWave / U);
 
 
+// Register units whose weight loads are issued before the activation tile
+// is stored (see mmvq_chunk); two measured best on the 10240 x 2560 and
+// 8192 x 2560 Q6_K products (zero, one, three, four and all were slower).
+constexpr int kPreUnits = 2;
+
 // One register chunk of a call: units c0 + u + U*it (it < IT) of each of the
 // lane's rows.  FULL: the chunk lies wholly inside the row, so every address
 // is a constant offset from a per-lane base and no bound is checked.
@@ -680,14 +689,14 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
     }
     __builtin_amdgcn_sched_barrier(0);
     const ActTile<TNB> t = act_tile<TNB>(lds, N);
-    // One-workgroup-per-CU launches (long rows) stage the tile before any
-    // weight load is issued: the tile then arrives in about the unloaded
-    // latency instead of queueing behind the whole weight stream, and the
-    // dot products can start as the first weights land.  With several
-    // workgroups per CU the tile is staged behind the weight loads instead,
-    // so the stream starts at once.
-    constexpr bool ACT_FIRST = NTHR > 256;
-    if constexpr (ACT_FIRST) {
+    // Weight loads of the first PRE units go out with the activation loads;
+    // then the tile is stored (waiting for the activation only) and the
+    // remaining units' loads follow.  The tile thus arrives behind only a
+    // fraction of the weight stream and the dot products start while most
+    // weights are still in flight.  One-workgroup-per-CU launches (long
+    // rows) stage the whole tile first (PRE = 0).
+    constexpr int PRE = NTHR > 256 ? 0 : (kPreUnits < IT ? kPreUnits : IT);
+    auto stage = [&]() {
 #pragma unroll
         for (int s = 0; s < SI; s++) {
             const int i = tid + s * NTHR, n = i / TNB, b = i - n * TNB;
@@ -695,9 +704,9 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
         }
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-    }
-    // weight loads, unconditional too (lanes past the end read a clamped,
-    // valid address and ignore it): branches here would make the wait counts
+    };
+    // weight loads, unconditional (lanes past the end read a clamped, valid
+    // address and ignore it): branches here would make the wait counts
     // conservative and serialize the stream behind the tile
     int64_t lrow[P];
 #pragma unroll
@@ -705,9 +714,17 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
     if constexpr (FULL) {
 #pragma unroll
         for (int it = 0; it < IT; it++) ok[it] = true;
+        if constexpr (PRE > 0) {
 #pragma unroll
-        for (int p = 0; p < P; p++) load_chunk<F, U, IT, P>(fmt, r, p, lrow[p], c0 + u);
+            for (int p = 0; p < P; p++) load_chunk<F, U, IT, P, 0, PRE, true>(fmt, r, p, lrow[p], c0 + u);
+        }
+        stage();
+        if constexpr (PRE < IT) {
+#pragma unroll
+            for (int p = 0; p < P; p++) load_chunk<F, U, IT, P, PRE, IT, PRE == 0>(fmt, r, p, lrow[p], c0 + u);
+        }
     } else {
+        if constexpr (PRE == 0) stage();
 #pragma unroll
         for (int it = 0; it < IT; it++) {
             const int unit = c0 + u + U * it;
@@ -715,14 +732,7 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
 #pragma unroll
             for (int p = 0; p < P; p++) fmt.load(r[it][p], lrow[p], min(unit, units - 1));
         }
-    }
-    if constexpr (!ACT_FIRST) {
-#pragma unroll
-        for (int s = 0; s < SI; s++) {
-            const int i = tid + s * NTHR, n = i / TNB, b = i - n * TNB;
-            if (i < N * TNB && (FULL || b < sub_nsb)) act_store<F::NEED_SUM>(t, i, ar[s], F::DSCALE);
-        }
-        lds_barrier();
+        if constexpr (PRE > 0) stage();
     }
 
 #pragma unroll
