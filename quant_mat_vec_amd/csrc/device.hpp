@@ -661,7 +661,7 @@ constexpr int kPreUnits = 2;
 // One register chunk of a call: units c0 + u + U*it (it < IT) of each of the
 // lane's rows.  FULL: the chunk lies wholly inside the row, so every address
 // is a constant offset from a per-lane base and no bound is checked.
-template <bool FULL, class F, int N, int U, int P, int NTHR, bool DUMP, int IT>
+template <bool FULL, class F, int N, int U, int P, int NTHR, bool DUMP, int IT, int PRE>
 __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void *lds, int c0, int units,
                                            const int64_t (&row)[P], const bool (&rok)[P], float (&acc)[P][N]) {
     constexpr int SBPU = F::SBPU;
@@ -693,9 +693,8 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
     // then the tile is stored (waiting for the activation only) and the
     // remaining units' loads follow.  The tile thus arrives behind only a
     // fraction of the weight stream and the dot products start while most
-    // weights are still in flight.  One-workgroup-per-CU launches (long
-    // rows) stage the whole tile first (PRE = 0).
-    constexpr int PRE = NTHR > 256 ? 0 : (kPreUnits < IT ? kPreUnits : IT);
+    // weights are still in flight.  PRE = 0 stages the whole tile first.
+    static_assert(PRE >= 0 && PRE <= IT, "pre-issued units");
     auto stage = [&]() {
 #pragma unroll
         for (int s = 0; s < SI; s++) {
@@ -778,7 +777,15 @@ __device__ __forceinline__ void mmvq_chunk(const F &fmt, const MmvqArgs &a, void
 // place one before.  RAGGED = false: the caller guarantees that the row
 // length is a whole number of register chunks (K/32/SBPU % (U*IT) == 0), and
 // the ragged-chunk code is not compiled.
-template <class F, int N, int U, int P, int NTHR, bool DUMP, int IT = F::IT, bool RAGGED = true>
+// Default pre-issued units: the dense one-workgroup-per-CU launches (long
+// rows, more than 256 threads) stage the whole tile first, which measured
+// better there; other launches issue kPreUnits units first.
+__host__ __device__ constexpr int default_pre(int nthr, int it) {
+    return nthr > 256 ? 0 : (kPreUnits < it ? kPreUnits : it);
+}
+
+template <class F, int N, int U, int P, int NTHR, bool DUMP, int IT = F::IT, bool RAGGED = true,
+          int PRE = default_pre(NTHR, IT)>
 __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
                                           float (&acc)[P][N]) {
     int64_t row[P];
@@ -798,12 +805,12 @@ __device__ __forceinline__ void mmvq_rows(const F &fmt, const MmvqArgs &a, int64
     const int nfull = units / CH;
     for (int c = 0; c < nfull; c++) {
         if (c > 0) lds_barrier();
-        mmvq_chunk<true, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, c * CH, units, row, rok, acc);
+        mmvq_chunk<true, F, N, U, P, NTHR, DUMP, IT, PRE>(fmt, a, lds, c * CH, units, row, rok, acc);
     }
     if constexpr (RAGGED) {                                 // ragged last chunk
         if (nfull * CH < units) {
             if (nfull > 0) lds_barrier();
-            mmvq_chunk<false, F, N, U, P, NTHR, DUMP, IT>(fmt, a, lds, nfull * CH, units, row, rok, acc);
+            mmvq_chunk<false, F, N, U, P, NTHR, DUMP, IT, PRE>(fmt, a, lds, nfull * CH, units, row, rok, acc);
         }
     }
 #pragma unroll

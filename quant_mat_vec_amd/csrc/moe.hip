@@ -133,7 +133,9 @@ __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t 
     a.its = its;
     const int64_t row0 = (int64_t)tile * 2 * kGuRows;
     float acc[1][N];
-    mmvq_rows<Q4GateUp, N, U, 1, nthr, false, Q4GateUp::IT, RAGGED>(f, a, row0, act, acc);
+    // the gate/up weight loads of the first kPreUnits units go out with the
+    // activation loads (the tile of this 512-thread kernel is small)
+    mmvq_rows<Q4GateUp, N, U, 1, nthr, false, Q4GateUp::IT, RAGGED, kPreUnits>(f, a, row0, act, acc);
 
     const int lane = threadIdx.x & (kWave - 1), u = lane % U;
     const int64_t vrow = lane_row<U, 1>(row0, 0);
