@@ -50,7 +50,7 @@ def test_quantize_q8_1_ties_golden():
 SMALL = [(1, 256, 1), (37, 768, 3), (19, 2560, 8), (9, 10240, 2), (70, 512, 5), (5, 1280, 8)]
 
 
-@pytest.mark.parametrize("rows,K,ncols", SMALL)
+@pytest.mark.parametrize("rows,K,ncols", SMALL + [(40, 3584, 5)])
 @pytest.mark.parametrize("layout", [PL, GG])
 def test_q6k_isums_bitexact(rows, K, ncols, layout):
     note(f"mmvq_q6k_isums rows={rows} K={K} ncols={ncols} layout={layout}")
@@ -63,7 +63,7 @@ def test_q6k_isums_bitexact(rows, K, ncols, layout):
     assert np.array_equal(isums("q6k", wd, xq, rows, K, ncols, layout), orc.q6k_isums(w, xq_np, rows, K))
 
 
-@pytest.mark.parametrize("rows,K,ncols", SMALL + [(33, 6144, 4)])
+@pytest.mark.parametrize("rows,K,ncols", SMALL + [(33, 6144, 4), (24, 7168, 8), (33, 6144, 8)])
 @pytest.mark.parametrize("kind", ["q4k", "q5k"])
 def test_q45_isums_bitexact(rows, K, ncols, kind):
     note(f"mmvq_{kind}_isums rows={rows} K={K} ncols={ncols}")
@@ -74,7 +74,10 @@ def test_q45_isums_bitexact(rows, K, ncols, kind):
 
 
 # --------------------------------------------------------------- outputs
-@pytest.mark.parametrize("rows,K,ncols", SMALL + [(130, 2560, 4)])
+# (40, 3584): a full register chunk then a ragged one in every row (Q6_K: 16
+# lanes x 7 units, depth 5); (24, 7168, 8): the same for Q4_K/Q5_K; (33,
+# 6144, 8): Q4_K/Q5_K with the activation tile in two LDS sub-tiles.
+@pytest.mark.parametrize("rows,K,ncols", SMALL + [(130, 2560, 4), (40, 3584, 5), (24, 7168, 8), (33, 6144, 8)])
 @pytest.mark.parametrize("kind", ["q6k", "q4k", "q5k"])
 def test_mmvq_outputs_vs_oracle(rows, K, ncols, kind):
     note(f"mmvq_{kind} rows={rows} K={K} ncols={ncols}")
@@ -124,6 +127,41 @@ def test_column_count_invariance(K, kind, layout):
     for c in (0, 3, 7):
         one = mmvq(kind, wd, xq[c * nb:(c + 1) * nb], rows, K, 1, layout)
         assert np.array_equal(one[0].view(np.uint32), full[c].view(np.uint32))
+
+
+@pytest.mark.parametrize("ncols", range(1, 9))
+@pytest.mark.parametrize("kind", ["q6k", "q4k", "q5k"])
+def test_every_column_count(kind, ncols):
+    """Each of the eight column-count instantiations against the oracle."""
+    note(f"mmvq_{kind} every column count: N={ncols}")
+    rows, K = 96, 2560
+    g = synth.rng(700 + ncols)
+    w = synth.blocks(kind, g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    ref, ab = orc.mmvq(kind, w, xq_np, rows, K)
+    wd = dev(w)
+    if kind == "q6k":
+        got = mmvq(kind, planar(wd, rows, K), xq, rows, K, ncols, PL)
+        got_g = mmvq(kind, wd, xq, rows, K, ncols, GG)
+        assert np.array_equal(got_g.view(np.uint32), got.view(np.uint32)), "planar != GGUF bits"
+    else:
+        got = mmvq(kind, wd, xq, rows, K, ncols)
+    assert_close(got, ref, ab, f"{kind} {rows}x{K} N={ncols}")
+
+
+def test_ten_wave_launch_two_chunks():
+    """Long rows in one-workgroup-per-CU launches: 64 lanes per row, two full
+    register chunks and several LDS sub-tiles per row (K = 20480)."""
+    note("Q6_K 2240x20480 N=8 (ten-wave workgroups, two chunks, LDS sub-tiles), sampled")
+    rows, K = 2240, 20480
+    g = synth.rng(720)
+    w = synth.q6k_blocks(g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, 8, K))
+    wd = dev(w)
+    got = mmvq("q6k", planar(wd, rows, K), xq, rows, K, 8, PL)
+    check_sampled("q6k", w, xq_np, got, rows, K, g)
+    got_g = mmvq("q6k", wd, xq, rows, K, 8, GG)
+    assert np.array_equal(got_g.view(np.uint32), got.view(np.uint32)), "planar != GGUF bits"
 
 
 # ------------------------------------------------------ planar conversion
@@ -342,3 +380,34 @@ def test_moe_out_of_range_id_is_skipped(moe):
     res = orc.grouped_expert(moe["gate"], moe["up"], moe["down"], xq_np, ids, rw0, E, T, TOPK, DM, DFF)
     # the oracle chain requantizes its own h, so compare at the end-to-end level
     assert np.abs(out - res["out"]).max() <= 1e-2 * np.abs(res["out"]).max()
+
+
+def test_moe_small_ragged_topk4():
+    """Rows that are not whole register chunks (the ragged kernels) and a
+    routing width of 4: E = 6, d_model = 512, d_ff = 256, T = 3."""
+    note("grouped_expert_mmvq small: E=6 d_model=512 d_ff=256 T=3 topk=4")
+    e_, dm, dff, tk, T = 6, 512, 256, 4, 3
+    g = synth.rng(730)
+    gate, up, down = synth.moe_weights(g, e_, dm, dff)
+    ids, rw = synth.routing(g, T, e_, tk)
+    xq, xq_np = quantize(synth.activations(g, T, dm))
+    wsb = qmv.grouped_expert_mmvq_workspace(e_, T, tk, dm, dff)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    L = qmv.moe_workspace_layout(T, tk, dm, dff)
+    for layout in (PL, GG):
+        dd = dev(down)
+        wdn = planar(dd, e_ * dm, dff) if layout == PL else dd
+        out, buf = guarded(T * dm)
+        qmv.grouped_expert_mmvq(dev(gate), dev(up), wdn, layout, xq, dev(ids), dev(rw), out, e_, T, tk, dm, dff,
+                                ws, wsb)
+        assert canaries_intact(buf, T * dm)
+        got, wsh = host(out).reshape(T, dm), host(ws)
+        S = T * tk
+        h = wsh[L["h"]:L["h"] + 4 * S * dff].view(np.float32).reshape(S, dff)
+        hq = wsh[L["hq"]:L["hq"] + 36 * S * dff // 32].reshape(S, -1)
+        y = wsh[L["y"]:L["y"] + 4 * S * dm].view(np.float32).reshape(S, dm)
+        res = orc.grouped_expert(gate, up, down, xq_np, ids, rw, e_, T, tk, dm, dff, hq_in=hq)
+        for s in range(S):
+            assert np.array_equal(hq[s], orc.quantize_q8_1(h[s][None])[0]), f"hq slot {s}"
+            assert_close(y[s][None], res["y"][s][None], res["y_absum"][s][None], f"y slot {s}")
+        assert_close(got, res["out"], res["out_absum"], f"out layout {layout}")
