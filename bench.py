@@ -15,8 +15,10 @@ whole step (weight bytes of the three products / step wall time, GB/s).
 `roofline` is for the dominant kernel (the MMVQ instantiation with the
 largest share of GPU time): algorithmic bytes per launch over its average
 launch time, from HIP events on its launch stream around graph replays of
-back-to-back launches.  The step itself is timed from HIP graph replays
-(events on the stream, and host wall time; the larger is used).  `cpu_baseline` times the CPU oracle on
+back-to-back launches.  The step itself is timed from HIP graph replays,
+each graph holding 26 consecutive steps (events on the stream, and host wall
+time; the larger is used); `extras` also gives the rate with one graph launch
+per step.  `cpu_baseline` times the CPU oracle on
 the same step.  `extras` holds per-N figures, the other shapes, the grouped
 MoE, a cache-warm figure (not HBM) and a plain device copy for calibration.
 """
@@ -164,30 +166,51 @@ def main():
             c = copies[(len(NCOLS) * i + j) % ncopies]
             qmv.mmvq_q6k(c, PL, xq_of(n), out, ROWS, K, n)
 
-    # One HIP graph per rotation offset: step i replays graph i % ncopies, so
-    # exactly `steps` steps run with the weight copies rotating as in eager mode.
+    # Step i uses weight copies at rotation offset i % ncopies.  HIP graphs:
+    # one holding `ncopies` consecutive steps (offsets 0 .. ncopies-1, so the
+    # rotation continues across replays) and one single-step graph per
+    # offset for a remainder; exactly `steps` steps run in the timed region.
+    # A decode loop captures many launches per graph; the single-step figure
+    # (one graph launch per step) is reported beside it.
     graphs = []
     for i in range(ncopies):
         gph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gph, stream=stream):
             step(i)
         graphs.append(gph)
+    multi = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(multi, stream=stream):
+        for i in range(ncopies):
+            step(i)
     torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % ncopies].replay()
+
+    def run_steps(n, batched):
+        done = 0
+        if batched:
+            while n - done >= ncopies:
+                multi.replay()
+                done += ncopies
+        while done < n:
+            graphs[done % ncopies].replay()
+            done += 1
+
+    def timed_steps(n, batched):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record(stream)
+        run_steps(n, batched)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return e0.elapsed_time(e1) / n, (t1 - t0) * 1e3 / n
+
+    run_steps(args.warmup, True)
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        graphs[i % ncopies].replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    wall_ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_step, wall_ms_per_step = timed_steps(args.steps, True)
     step_bytes = wb * len(NCOLS)
     value = step_bytes / (max(ms_per_step, wall_ms_per_step) * 1e-3) / 1e9
+    single_ms, single_wall_ms = timed_steps(args.steps, False)
 
     # Per-kernel average launch time: events on the launch stream around
     # graph replays of back-to-back launches of one MMVQ instantiation
@@ -240,6 +263,10 @@ def main():
     extras = {"per_ncols": {str(n): per_n[n] for n in NCOLS},
               "eager_event_us_per_launch": eager,
               "wall_ms_per_step": round(wall_ms_per_step, 4),
+              "one_graph_launch_per_step": {"ms_per_step": round(single_ms, 4),
+                                            "wall_ms_per_step": round(single_wall_ms, 4),
+                                            "weight_GBps": round(step_bytes / (max(single_ms, single_wall_ms) * 1e-3) / 1e9, 1)},
+              "steps_per_graph": ncopies,
               "weight_copies": ncopies, "weight_bytes_per_copy": wb,
               "fnv1a32_out_prefix": int(h),
               "pages_A770_us": PAGES_US}

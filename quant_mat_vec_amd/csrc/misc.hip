@@ -5,26 +5,53 @@
 
 namespace qmv {
 
-// One 32-lane group per Q8_1 block; x is [ncols][K], xq [ncols][K/32].
+// Eight lanes per Q8_1 block, four consecutive values per lane: the max and
+// the quant sum reduce inside each lane and then over the eight lanes with
+// DPP (no cross-row exchange), and every lane writes its own dword of four
+// quants.  x is [ncols][K], xq [ncols][K/32].  The arithmetic (max, d =
+// max / 127, round(x / d), sum) is that of q8_1_quantize32.
 __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__ x, uint8_t *__restrict__ xq,
                                                        int64_t K, int64_t nblocks) {
-    const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 5;
-    const int i = threadIdx.x & 31;
+    const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
+    const int i = threadIdx.x & 7;
     const bool ok = g < nblocks;
     const int64_t nb = K / 32;
-    float v = 0.0f;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (ok) {
         const int64_t col = g / nb, b = g - col * nb;
-        v = x[col * K + b * 32 + i];
+        const float *p = x + col * K + b * 32 + 4 * i;
+#pragma unroll
+        for (int k = 0; k < 4; k++) v[k] = p[k];
     }
-    uint32_t db, sb;
-    int q = q8_1_quantize32(v, db, sb);
-    q8_1_store32(xq + g * kQ81Bytes, i, q, db, sb, ok);
+    float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    a = dpp_max<0xB1>(a);     // lane ^ 1
+    a = dpp_max<0x4E>(a);     // lane ^ 2
+    a = dpp_max<0x141>(a);    // mirror within eight lanes
+    const float d = a / 127.0f;
+    int q[4] = {0, 0, 0, 0};
+    if (d != 0.0f) {
+#pragma unroll
+        for (int k = 0; k < 4; k++) q[k] = (int)fminf(fmaxf(roundf(v[k] / d), -127.0f), 127.0f);
+    }
+    int s = q[0] + q[1] + q[2] + q[3];
+    s = dpp_iadd<0xB1>(s);
+    s = dpp_iadd<0x4E>(s);
+    s = dpp_iadd<0x141>(s);
+    if (ok) {
+        uint32_t *blk = reinterpret_cast<uint32_t *>(xq + g * kQ81Bytes);
+        blk[1 + i] = ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) | (((uint32_t)q[2] & 0xFFu) << 16) |
+                     ((uint32_t)q[3] << 24);
+        if (i == 0) {
+            const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
+            const uint32_t sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+            blk[0] = dbits | (sbits << 16);
+        }
+    }
 }
 
 hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s) {
     const int64_t nblocks = (int64_t)ncols * (K / 32);
-    const int64_t threads = nblocks * 32;
+    const int64_t threads = nblocks * 8;
     const int64_t grid = (threads + 255) / 256;
     hipLaunchKernelGGL(k_quantize_q8_1, dim3((unsigned)grid), dim3(256), 0, s, x, xq, K, nblocks);
     return hipGetLastError();
