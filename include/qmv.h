@@ -56,6 +56,27 @@
  * six-bit offset costs no instruction.  Planar and GGUF inputs give
  * bit-identical outputs.
  *
+ * Tiled Q6_K layout (QMV_LAYOUT_TILED), produced by repack_q6k_tiled: the
+ * planes of the planar layout (same sizes and offsets, same 16-byte A and
+ * 8-byte B pieces, same scale and d bytes), with the entries of each group
+ * of 16 consecutive rows interleaved so that the entries of one position in
+ * the 16 rows are adjacent.  Rows form tiles 16*T .. 16*T+R_T-1, R_T =
+ * min(16, R - 16*T); row r of tile T, with nsb = K/32 and nb = K/256:
+ *   plane A: the 16-byte piece of sub-block s (0..nsb-1) at entry
+ *     16*T*nsb + s*R_T + r (entries of 16 bytes from byte 0);
+ *   plane B: the 8-byte piece of sub-block s at entry 16*T*nsb + s*R_T + r
+ *     (entries of 8 bytes from byte 128*NB);
+ *   plane SC: for z = 0..nsb/4-1, the eight scale bytes 8*(z%2) .. 8*(z%2)+7
+ *     of block z/2 (the scales of sub-blocks 4z .. 4z+3) at entry
+ *     16*T*(nsb/4) + z*R_T + r (entries of 8 bytes from byte 192*NB);
+ *   plane D: fp16 d of block b at entry 16*T*nb + b*R_T + r (entries of
+ *     2 bytes from byte 208*NB).
+ * With it a 64-lane load of 16 rows x 4 sub-blocks reads one contiguous
+ * kilobyte, the operand shape of the int8 matrix-core kernel that serves
+ * this layout.  Its outputs agree with the other layouts' to fp32 rounding
+ * (a different summation order), and its per-sub-block integer sums are
+ * identical.
+ *
  * Conventions for every entry point.
  *   Memory: all data pointers are device pointers owned by the caller; the
  *   library never allocates, frees or synchronizes.  `stream` is a
@@ -88,7 +109,7 @@ enum {
     QMV_ERR_HIP = -5            /* a HIP launch failed */
 };
 
-enum { QMV_LAYOUT_GGUF = 0, QMV_LAYOUT_PLANAR = 1 };
+enum { QMV_LAYOUT_GGUF = 0, QMV_LAYOUT_PLANAR = 1, QMV_LAYOUT_TILED = 2 };
 
 /* Largest supported sizes: rows <= 2^31-1, K <= 2^20, and every weight,
  * activation and output buffer below 2^40 bytes. */
@@ -105,9 +126,11 @@ int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream);
 /* Q6_K weights x Q8_1 activations (the Q6_K dense decode product of PR
  * #2340 "What it changes" and PR #2207 "How it was checked").
  * w: rows x K Q6_K matrix in `layout` (QMV_LAYOUT_GGUF: 210-byte blocks,
- * 4-byte aligned; QMV_LAYOUT_PLANAR: the planar layout above, 16-byte
- * aligned).  xq: Q8_1 [ncols][K/32], 4-byte aligned.  out: fp32
- * [ncols][rows], 4-byte aligned.  K % 256 == 0, 1 <= ncols <= 8. */
+ * 4-byte aligned; QMV_LAYOUT_PLANAR, QMV_LAYOUT_TILED: the layouts above,
+ * 16-byte aligned).  xq: Q8_1 [ncols][K/32], 4-byte aligned.  out: fp32
+ * [ncols][rows], 4-byte aligned.  K % 256 == 0, 1 <= ncols <= 8.
+ * GGUF and planar inputs run on the vector ALU (dot4); tiled inputs on the
+ * int8 matrix cores. */
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out,
              int64_t rows, int64_t K, int ncols, void *stream);
 
@@ -128,6 +151,10 @@ int mmvq_q5k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
 int repack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
 /* Inverse conversion, planar -> GGUF (for tests and for exporting). */
 int unpack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
+/* The same two conversions for the tiled layout above (same sizes,
+ * alignments and checks). */
+int repack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
+int unpack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
 
 /* Per-sub-block integer sums of the same kernels (for verification):
  * isums int32 [ncols][rows][K/32].  Q6_K: sum over the sub-block's two

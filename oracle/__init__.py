@@ -53,7 +53,7 @@ def lib():
         for name in ("orc_q4k_decode", "orc_q5k_decode"):
             getattr(L, name).argtypes = [P, P, P, P, P, P]
         for name in ("orc_dequant_q6k", "orc_dequant_q4k", "orc_dequant_q5k",
-                     "orc_q6k_to_planar"):
+                     "orc_q6k_to_planar", "orc_q6k_to_tiled"):
             getattr(L, name).argtypes = [P, P, I64, I64]
         L.orc_quantize_q8_1.argtypes = [P, P, I64, I]
         L.orc_dequant_q8_1.argtypes = [P, P, I64, I]
@@ -182,6 +182,13 @@ def q6k_to_planar(w, rows: int, K: int):
     w = _u8(w)
     dst = np.zeros(w.size, np.uint8)
     lib().orc_q6k_to_planar(_p(w), _p(dst), rows, K)
+    return dst
+
+
+def q6k_to_tiled(w, rows: int, K: int):
+    w = _u8(w)
+    dst = np.zeros(w.size, np.uint8)
+    lib().orc_q6k_to_tiled(_p(w), _p(dst), rows, K)
     return dst
 
 

@@ -472,6 +472,44 @@ void orc_q6k_to_planar(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K
     }
 }
 
+/* -------------------------------------------------------- tiled Q6_K
+ * The planar planes above with each group of 16 consecutive rows
+ * interleaved, so that the entries of one position of the 16 rows are
+ * adjacent (the same load-time conversion of P2340 "What it changes", laid
+ * out for a 16-row operand).  Restated from the GPU library's published
+ * layout text (its C header): rows form tiles 16T .. 16T+R_T-1 with
+ * R_T = min(16, rows - 16T); for row r of tile T, nsb = K/32, nb = K/256:
+ *   A entry (16 B) of sub-block s:  16*T*nsb + s*R_T + r
+ *   B entry (8 B) of sub-block s:   16*T*nsb + s*R_T + r
+ *   SC entry (8 B) of step z (scale bytes 8*(z%2).. of block z/2):
+ *                                   16*T*(nsb/4) + z*R_T + r
+ *   D entry (2 B) of block b:       16*T*nb + b*R_T + r
+ * with the planes at the planar layout's byte offsets. */
+void orc_q6k_to_tiled(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K) {
+    const int64_t nb = K / QK, nsb = K / 32, NB = rows * nb;
+    uint8_t *pl = (uint8_t *)malloc((size_t)(210 * NB));
+    if (!pl) abort();
+    orc_q6k_to_planar(src, pl, rows, K);
+    for (int64_t row = 0; row < rows; row++) {
+        const int64_t T = row / 16, r = row % 16;
+        const int64_t R = rows - 16 * T < 16 ? rows - 16 * T : 16;
+        for (int64_t s = 0; s < nsb; s++) {
+            const int64_t e = 16 * T * nsb + s * R + r, p = row * nsb + s;
+            memcpy(dst + 16 * e, pl + 16 * p, 16);
+            memcpy(dst + 128 * NB + 8 * e, pl + 128 * NB + 8 * p, 8);
+        }
+        for (int64_t z = 0; z < nsb / 4; z++) {
+            const int64_t e = 16 * T * (nsb / 4) + z * R + r;
+            memcpy(dst + 192 * NB + 8 * e, pl + 192 * NB + 16 * (row * nb + z / 2) + 8 * (z % 2), 8);
+        }
+        for (int64_t b = 0; b < nb; b++) {
+            const int64_t e = 16 * T * nb + b * R + r;
+            memcpy(dst + 208 * NB + 2 * e, pl + 208 * NB + 2 * (row * nb + b), 2);
+        }
+    }
+    free(pl);
+}
+
 /* ------------------------------------------------------ grouped MoE
  * Routed-expert chain over a window of T tokens [I2801; P2746 "B70
  * validation"], for each token t and slot k (slot index t*topk + k):

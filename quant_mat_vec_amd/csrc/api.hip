@@ -38,16 +38,20 @@ int check_mmvq(const void *w, const void *xq, const void *out, int64_t rows, int
 
 int q6_dispatch(const void *w, int layout, const void *xq, float *out, int32_t *dump, int64_t rows,
                 int64_t K, int ncols, void *stream) {
-    if (layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR) {
+    if (layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR && layout != QMV_LAYOUT_TILED) {
         if (!w || !xq || !(out || dump)) return QMV_ERR_INVALID_ARG;
         return QMV_ERR_UNSUPPORTED;
     }
     const void *o = out ? static_cast<const void *>(out) : static_cast<const void *>(dump);
-    int rc = check_mmvq(w, xq, o, rows, K, ncols, 210, layout == QMV_LAYOUT_PLANAR ? 16 : 4);
+    int rc = check_mmvq(w, xq, o, rows, K, ncols, 210, layout == QMV_LAYOUT_GGUF ? 4 : 16);
     if (rc) return rc;
-    hipError_t e = layout == QMV_LAYOUT_PLANAR
-                       ? qmv::launch_mmvq_q6_planar(w, xq, out, dump, rows, K, ncols, as_stream(stream))
-                       : qmv::launch_mmvq_q6_gguf(w, xq, out, dump, rows, K, ncols, as_stream(stream));
+    hipError_t e;
+    if (layout == QMV_LAYOUT_TILED)
+        e = qmv::launch_mmvq_q6_tiled(w, xq, out, dump, rows, K, ncols, as_stream(stream));
+    else if (layout == QMV_LAYOUT_PLANAR)
+        e = qmv::launch_mmvq_q6_planar(w, xq, out, dump, rows, K, ncols, as_stream(stream));
+    else
+        e = qmv::launch_mmvq_q6_gguf(w, xq, out, dump, rows, K, ncols, as_stream(stream));
     return from_hip(e);
 }
 
@@ -124,14 +128,28 @@ int repack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void 
     int rc = check_repack(src, dst, rows, K, 2, 16);
     if (rc) return rc;
     return from_hip(qmv::launch_repack(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst),
-                                       rows * (K / 256), as_stream(stream)));
+                                       rows, K, false, as_stream(stream)));
 }
 
 int unpack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void *stream) {
     int rc = check_repack(src, dst, rows, K, 16, 2);
     if (rc) return rc;
     return from_hip(qmv::launch_unpack(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst),
-                                       rows * (K / 256), as_stream(stream)));
+                                       rows, K, false, as_stream(stream)));
+}
+
+int repack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *stream) {
+    int rc = check_repack(src, dst, rows, K, 2, 16);
+    if (rc) return rc;
+    return from_hip(qmv::launch_repack(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst),
+                                       rows, K, true, as_stream(stream)));
+}
+
+int unpack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *stream) {
+    int rc = check_repack(src, dst, rows, K, 16, 2);
+    if (rc) return rc;
+    return from_hip(qmv::launch_unpack(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst),
+                                       rows, K, true, as_stream(stream)));
 }
 
 size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff) {

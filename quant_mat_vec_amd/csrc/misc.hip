@@ -57,11 +57,37 @@ hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hi
     return hipGetLastError();
 }
 
-// GGUF Q6_K -> planar.  One thread per (block, sub-block j): it decodes the
-// 32 six-bit values of sub-block j, writes its 16-byte plane-A and 8-byte
-// plane-B pieces, and sub-block 0's thread copies the scales and d.
+// Where the parts of GGUF block t (row t / nb, block t % nb of the row) go
+// in the planar layouts, in units of the part's size: 16-byte A and 8-byte B
+// pieces of sub-block j, the two 8-byte halves of the scales, the 2-byte d.
+//   planar: row-major, pieces t*8 + j, halves 2t + h, d t;
+//   tiled:  16-row tiles (the last one R = rows - 16*tile rows high), row r
+//           of the tile, sub-block s = 8*(t % nb) + j of the row:
+//           pieces 16*tile*nsb + s*R + r, halves 16*tile*(nsb/4) + (2*(t%nb)
+//           + h)*R + r, d 16*tile*nb + (t%nb)*R + r.
+template <bool TILED>
+struct PlaneIndex {
+    int64_t rows, nb;
+    __device__ __forceinline__ void at(int64_t t, int64_t &p0, int64_t &pstride, int64_t &h0, int64_t &hstride,
+                                       int64_t &d) const {
+        if constexpr (!TILED) {
+            p0 = t * 8, pstride = 1, h0 = 2 * t, hstride = 1, d = t;
+        } else {
+            const int64_t row = t / nb, b = t - row * nb, tile = row >> 4, r = row & 15;
+            const int64_t R = min((int64_t)16, rows - 16 * tile), nsb = 8 * nb;
+            p0 = 16 * tile * nsb + 8 * b * R + r, pstride = R;
+            h0 = 16 * tile * (nsb / 4) + 2 * b * R + r, hstride = R;
+            d = 16 * tile * nb + b * R + r;
+        }
+    }
+};
+
+// GGUF Q6_K -> planar or tiled.  One thread per (block, sub-block j): it
+// decodes the 32 six-bit values of sub-block j, writes its 16-byte plane-A
+// and 8-byte plane-B pieces, and sub-block 0's thread copies the scales and d.
+template <bool TILED>
 __global__ __launch_bounds__(256) void k_repack_q6k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
-                                                    int64_t NB) {
+                                                    int64_t NB, PlaneIndex<TILED> ix) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gid >= NB * 8) return;
     const int64_t t = gid >> 3;
@@ -93,27 +119,35 @@ __global__ __launch_bounds__(256) void k_repack_q6k(const uint8_t *__restrict__ 
         B[0] |= ((w28 >> 2) & 3u) << (8 * k);
         B[1] |= ((w28 >> 4) & 3u) << (8 * k);
     }
-    reinterpret_cast<uint4 *>(dst)[t * 8 + j] = make_uint4(A[0], A[1], A[2], A[3]);
-    reinterpret_cast<uint2 *>(dst + 128 * NB)[t * 8 + j] = make_uint2(B[0], B[1]);
+    int64_t p0, ps, h0, hs, di;
+    ix.at(t, p0, ps, h0, hs, di);
+    reinterpret_cast<uint4 *>(dst)[p0 + j * ps] = make_uint4(A[0], A[1], A[2], A[3]);
+    reinterpret_cast<uint2 *>(dst + 128 * NB)[p0 + j * ps] = make_uint2(B[0], B[1]);
     if (j == 0) {
-        uint8_t *sc = dst + 192 * NB + 16 * t;
 #pragma unroll
-        for (int k = 0; k < 16; k++) sc[k] = blk[192 + k];
-        dst[208 * NB + 2 * t] = blk[208];
-        dst[208 * NB + 2 * t + 1] = blk[209];
+        for (int hh = 0; hh < 2; hh++) {
+            uint8_t *sc = dst + 192 * NB + 8 * (h0 + hh * hs);
+#pragma unroll
+            for (int k = 0; k < 8; k++) sc[k] = blk[192 + 8 * hh + k];
+        }
+        dst[208 * NB + 2 * di] = blk[208];
+        dst[208 * NB + 2 * di + 1] = blk[209];
     }
 }
 
-// planar -> GGUF Q6_K, one thread per block.
+// planar or tiled -> GGUF Q6_K, one thread per block.
+template <bool TILED>
 __global__ __launch_bounds__(256) void k_unpack_q6k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
-                                                    int64_t NB) {
+                                                    int64_t NB, PlaneIndex<TILED> ix) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= NB) return;
+    int64_t p0, ps, h0, hs, di;
+    ix.at(t, p0, ps, h0, hs, di);
     uint8_t *blk = dst + t * kQ6Bytes;
     uint8_t ql[128] = {}, qh[64] = {};
     for (int j = 0; j < 8; j++) {
-        const uint4 a = reinterpret_cast<const uint4 *>(src)[t * 8 + j];
-        const uint2 b = reinterpret_cast<const uint2 *>(src + 128 * NB)[t * 8 + j];
+        const uint4 a = reinterpret_cast<const uint4 *>(src)[p0 + j * ps];
+        const uint2 b = reinterpret_cast<const uint2 *>(src + 128 * NB)[p0 + j * ps];
         const uint32_t A[4] = {a.x, a.y, a.z, a.w}, B[2] = {b.x, b.y};
         uint32_t v[32];
         for (int k = 0; k < 16; k++) v[k] = (A[k >> 2] >> (8 * (k & 3) + 2)) & 63u;
@@ -132,10 +166,12 @@ __global__ __launch_bounds__(256) void k_unpack_q6k(const uint8_t *__restrict__ 
     }
     for (int k = 0; k < 128; k++) blk[k] = ql[k];
     for (int k = 0; k < 64; k++) blk[128 + k] = qh[k];
-    const uint8_t *sc = src + 192 * NB + 16 * t;
-    for (int k = 0; k < 16; k++) blk[192 + k] = sc[k];
-    blk[208] = src[208 * NB + 2 * t];
-    blk[209] = src[208 * NB + 2 * t + 1];
+    for (int hh = 0; hh < 2; hh++) {
+        const uint8_t *sc = src + 192 * NB + 8 * (h0 + hh * hs);
+        for (int k = 0; k < 8; k++) blk[192 + 8 * hh + k] = sc[k];
+    }
+    blk[208] = src[208 * NB + 2 * di];
+    blk[209] = src[208 * NB + 2 * di + 1];
 }
 
 // Streaming-read calibration: the fastest plain read of a buffer found on
@@ -170,15 +206,23 @@ hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, in
     return hipGetLastError();
 }
 
-hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t NB, hipStream_t s) {
-    const int64_t grid = (NB * 8 + 255) / 256;
-    hipLaunchKernelGGL(k_repack_q6k, dim3((unsigned)grid), dim3(256), 0, s, src, dst, NB);
+hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s) {
+    const int64_t nb = K / 256, NB = rows * nb;
+    const dim3 grid((unsigned)((NB * 8 + 255) / 256));
+    if (tiled)
+        hipLaunchKernelGGL(k_repack_q6k<true>, grid, dim3(256), 0, s, src, dst, NB, PlaneIndex<true>{rows, nb});
+    else
+        hipLaunchKernelGGL(k_repack_q6k<false>, grid, dim3(256), 0, s, src, dst, NB, PlaneIndex<false>{rows, nb});
     return hipGetLastError();
 }
 
-hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t NB, hipStream_t s) {
-    const int64_t grid = (NB + 255) / 256;
-    hipLaunchKernelGGL(k_unpack_q6k, dim3((unsigned)grid), dim3(256), 0, s, src, dst, NB);
+hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s) {
+    const int64_t nb = K / 256, NB = rows * nb;
+    const dim3 grid((unsigned)((NB + 255) / 256));
+    if (tiled)
+        hipLaunchKernelGGL(k_unpack_q6k<true>, grid, dim3(256), 0, s, src, dst, NB, PlaneIndex<true>{rows, nb});
+    else
+        hipLaunchKernelGGL(k_unpack_q6k<false>, grid, dim3(256), 0, s, src, dst, NB, PlaneIndex<false>{rows, nb});
     return hipGetLastError();
 }
 

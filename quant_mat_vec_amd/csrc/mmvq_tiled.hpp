@@ -1,0 +1,306 @@
+// mmvq_tiled.hpp -- Q6_K MMVQ on the int8 matrix cores, tiled weight layout.
+//
+// The integer part of the Q6_K x Q8_1 dot product (per 16-weight scale
+// group, the sum of code x quant) comes from v_mfma_i32_16x16x64_i8; the
+// scales are then applied on the vector ALU per sub-block, as in the dot4
+// kernels, so every integer partial sum is the same number.
+//
+// Mapping (one wave, one 16-row tile, one step z of four sub-blocks 4z..4z+3):
+//   B operand (weights): lane l holds row l%16 of the tile, sub-block
+//     4z + l/16, half h (16 codes); with the tiled layout the 64 lanes of a
+//     load instruction read one contiguous kilobyte.
+//   A operand (activations): row r' = l%16 of A is the pair (column
+//     n = 4cg + r'/4, sub-block 4z + r'%4); lane l holds the 16 quants of its
+//     k-group (sub-block 4z + l/16, half h) when that sub-block is r'%4 and
+//     reads a zero entry otherwise, so output (r', row) sums only its own
+//     scale group.  (The 16x16x64 operands share one k order for A and B:
+//     lane l carries k-group l/16 in both.)
+//   Result: lane l gets, for tile row l%16 and column 4cg + l/16, the four
+//     half-sub-block sums of sub-blocks 4z..4z+3 in its four registers.
+// The two halves (codes 0-15, 16-31) take one MFMA each per group of four
+// columns.  A workgroup holds RTW row tiles x KS waves along K; the KS
+// partial sums of a row are added through LDS in wave order at the end.
+#pragma once
+
+#include <type_traits>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace qmv {
+
+typedef int v4i32 __attribute__((ext_vector_type(4)));
+
+// Weight planes of the tiled layout (see repack_q6k_tiled): per 16-row tile
+// (the last one R rows high) entries are ordered [position][row of tile].
+struct Q6Tiled {
+    const uint4 *A;        // 16 B per (row, sub-block)
+    const uint2 *B;        // 8 B per (row, sub-block)
+    const uint2 *SC;       // 8 B per (row, four sub-blocks): their scale pairs
+    const uint16_t *D;     // 2 B per (row, block)
+    int64_t nsb, nb;       // sub-blocks and blocks per row
+
+    __device__ __forceinline__ void init(const void *w, int64_t rows, int64_t K) {
+        const uint8_t *base = reinterpret_cast<const uint8_t *>(w);
+        nb = K / 256;
+        nsb = K / 32;
+        const int64_t NB = rows * nb;
+        A = reinterpret_cast<const uint4 *>(base);
+        B = reinterpret_cast<const uint2 *>(base + 128 * NB);
+        SC = reinterpret_cast<const uint2 *>(base + 192 * NB);
+        D = reinterpret_cast<const uint16_t *>(base + 208 * NB);
+    }
+};
+
+// Weight steps whose code-plane loads are issued before the activation tile
+// is stored (the rest follow it): measured best at two.
+constexpr int kTiledPre = 2;
+
+template <int N, int KS, int RTW, int IT>
+struct TiledCfg {
+    static constexpr int W = KS * RTW;                 // waves per workgroup
+    static constexpr int NTHR = W * kWave;
+    static constexpr int NCG = (N + 3) / 4;            // column groups of four
+    static constexpr int CZ = KS * IT;                 // steps per chunk
+    static constexpr int TNB = 4 * CZ;                 // tile blocks per column
+    static constexpr int SI = (N * TNB + NTHR - 1) / NTHR;
+    // x0 | zero | x1 | zero (uint4) and d/4 per block (float)
+    static constexpr size_t TILE = (size_t)(N * TNB + 1) * 32 + (size_t)N * TNB * 4;
+    static constexpr size_t RED = KS > 1 ? (size_t)W * NCG * kWave * 4 : 0;
+    static constexpr size_t LDS = TILE > RED ? TILE : RED;
+    static constexpr int PRE = kTiledPre < IT ? kTiledPre : IT;
+};
+
+// Per-lane position in the tiled planes.
+struct TiledLane {
+    int64_t piece0;    // A/B entry of (row, sub-block 0)
+    int64_t sc0;       // SC entry of (row, step 0)
+    int64_t d0;        // D entry of (row, block 0)
+    int R;             // rows of the lane's tile: entry stride between positions
+};
+
+// One chunk of CZ steps starting at step zc0: wave ks of the row tile takes
+// steps zc0 + ks*IT + it.  FULL: all steps exist (no clamping).
+template <bool FULL, int N, int KS, int RTW, int IT, bool DUMP>
+__device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane &tl, const MmvqArgs &a, uint8_t *lds,
+                                            int zc0, int ZS, int64_t row, bool rok,
+                                            float (&acc)[TiledCfg<N, KS, RTW, IT>::NCG]) {
+    using C = TiledCfg<N, KS, RTW, IT>;
+    constexpr int TNB = C::TNB, NTHR = C::NTHR;
+    const int tid = threadIdx.x, l = tid & (kWave - 1), ks = (tid / kWave) % KS, kg = l >> 4;
+    const int64_t nsb = f.nsb;
+    const int nblk = FULL ? TNB : min(TNB, (int)(nsb - 4 * (int64_t)zc0));
+
+    // activation loads first (loads retire in order: the tile can be stored
+    // while the weight loads behind it are still in flight)
+    ActRaw ar[C::SI];
+#pragma unroll
+    for (int s = 0; s < C::SI; s++) {
+        const int i = min(tid + s * NTHR, N * TNB - 1), n = i / TNB;
+        const int b = FULL ? i - n * TNB : min(i - n * TNB, nblk - 1);
+        act_load(ar[s], a.xq, xcol_of<N>(a, n) + 4 * (int64_t)zc0 + b);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // weight loads: scales and d of every step, then the code planes of the
+    // first PRE steps; the rest after the tile is stored
+    uint4 wa[IT];
+    uint2 wb[IT], wsc[IT];
+    uint32_t wd[IT];
+    int zs[IT];
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int z = zc0 + ks * IT + it;
+        zs[it] = FULL ? z : min(z, ZS - 1);
+        wsc[it] = f.SC[tl.sc0 + (int64_t)zs[it] * tl.R];
+        wd[it] = f.D[tl.d0 + (int64_t)(zs[it] >> 1) * tl.R];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    auto load_ab = [&](auto lo_c, auto hi_c) {
+        constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+#pragma unroll
+        for (int it = LO; it < HI; it++) {
+            const int64_t e = tl.piece0 + (int64_t)(4 * zs[it] + kg) * tl.R;
+            wa[it] = f.A[e];
+            wb[it] = f.B[e];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    load_ab(std::integral_constant<int, 0>{}, std::integral_constant<int, C::PRE>{});
+
+    // stage the tile: x0 (N*TNB entries + a zero entry), x1 (the same), fd
+    uint4 *x0 = reinterpret_cast<uint4 *>(lds);
+    uint4 *x1 = x0 + N * TNB + 1;
+    float *fd = reinterpret_cast<float *>(x1 + N * TNB + 1);
+    if (tid == 0) {
+        x0[N * TNB] = make_uint4(0, 0, 0, 0);
+        x1[N * TNB] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < C::SI; s++) {
+        const int i = tid + s * NTHR, n = i / TNB, b = i - n * TNB;
+        if (i < N * TNB && (FULL || b < nblk)) {
+            x0[i] = make_uint4(ar[s].w[1], ar[s].w[2], ar[s].w[3], ar[s].w[4]);
+            x1[i] = make_uint4(ar[s].w[5], ar[s].w[6], ar[s].w[7], ar[s].w[8]);
+            fd[i] = half_to_float(ar[s].w[0]) * 0.25f;    // the codes are 4 * (q6 - 32)
+        }
+    }
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_ab(std::integral_constant<int, C::PRE>{}, std::integral_constant<int, IT>{});
+
+    const bool am = (l & 3) == kg;        // this lane's k-group is its A row's sub-block
+#pragma unroll
+    for (int it = 0; it < IT; it++) {
+        const int z = zc0 + ks * IT + it;
+        if (!FULL && z >= ZS) break;
+        const int zt = 4 * (z - zc0);
+        Q6Planar::Raw r;
+        r.a = wa[it];
+        r.b = wb[it];
+        int v[8];
+        Q6Planar::codes(r, v);
+        const v4i32 W0 = {v[0], v[1], v[2], v[3]}, W1 = {v[4], v[5], v[6], v[7]};
+        int sl[4], sh[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t word = i < 2 ? wsc[it].x : wsc[it].y;
+            sl[i] = sext8(word, 2 * (i & 1));
+            sh[i] = sext8(word, 2 * (i & 1) + 1);
+        }
+        const float dw = half_to_float(wd[it]);
+        v4i32 D0[C::NCG], D1[C::NCG];
+#pragma unroll
+        for (int cg = 0; cg < C::NCG; cg++) {
+            const int na = min(4 * cg + ((l & 15) >> 2), N - 1);
+            const int idx = am ? na * TNB + zt + kg : N * TNB;    // masked lanes read the zero entry
+            const uint4 X0 = x0[idx], X1 = x1[idx];
+            const v4i32 A0 = {(int)X0.x, (int)X0.y, (int)X0.z, (int)X0.w};
+            const v4i32 A1 = {(int)X1.x, (int)X1.y, (int)X1.z, (int)X1.w};
+            const v4i32 Z = {0, 0, 0, 0};
+            D0[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, W0, Z, 0, 0, 0);
+            D1[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, W1, Z, 0, 0, 0);
+        }
+#pragma unroll
+        for (int cg = 0; cg < C::NCG; cg++) {
+            const int no = 4 * cg + kg;            // this lane's output column
+            const float4 dx = *reinterpret_cast<const float4 *>(fd + min(no, N - 1) * TNB + zt);
+            const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
+            int I[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) I[i] = __mul24(sl[i], D0[cg][i]) + __mul24(sh[i], D1[cg][i]);   // 4 * isum
+            if constexpr (DUMP) {
+                if (rok && no < N) {
+                    int32_t *dp = a.dump + ((int64_t)no * a.rows + row) * nsb + 4 * (int64_t)z;
+#pragma unroll
+                    for (int i = 0; i < 4; i++) dp[i] = I[i] >> 2;
+                }
+            } else {
+                float t = dxa[0] * (float)I[0];
+#pragma unroll
+                for (int i = 1; i < 4; i++) t = __builtin_fmaf(dxa[i], (float)I[i], t);
+                acc[cg] = __builtin_fmaf(dw, t, acc[cg]);
+            }
+        }
+    }
+}
+
+template <int N, int KS, int RTW, int IT, bool DUMP>
+__global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
+                                                                    float *__restrict__ out) {
+    using C = TiledCfg<N, KS, RTW, IT>;
+    extern __shared__ __align__(16) uint8_t lds[];
+    Q6Tiled f;
+    f.init(w, a.rows, a.K);
+    const int tid = threadIdx.x, l = tid & (kWave - 1), wave = tid / kWave;
+    const int ks = wave % KS, rt = wave / KS;
+    // the lane's tile and row; lanes past the last row load from a row that
+    // exists and store nothing
+    const int64_t ntiles = (a.rows + 15) / 16;
+    const int64_t tile = (int64_t)blockIdx.x * RTW + rt, tc = min(tile, ntiles - 1);
+    const int R = (int)min((int64_t)16, a.rows - 16 * tc);
+    const int r = l & 15, rr = min(r, R - 1);
+    const int64_t row = 16 * tile + r;
+    const bool rok = tile < ntiles && r < R;
+    TiledLane tl;
+    tl.R = R;
+    tl.piece0 = 16 * tc * f.nsb + rr;
+    tl.sc0 = 16 * tc * (f.nsb / 4) + rr;
+    tl.d0 = 16 * tc * f.nb + rr;
+    const int ZS = (int)(a.K / 128);
+    float acc[C::NCG];
+#pragma unroll
+    for (int cg = 0; cg < C::NCG; cg++) acc[cg] = 0.0f;
+    const int nfull = ZS / C::CZ;
+    for (int c = 0; c < nfull; c++) {
+        if (c > 0) lds_barrier();
+        tiled_chunk<true, N, KS, RTW, IT, DUMP>(f, tl, a, lds, c * C::CZ, ZS, row, rok, acc);
+    }
+    if (nfull * C::CZ < ZS) {
+        if (nfull > 0) lds_barrier();
+        tiled_chunk<false, N, KS, RTW, IT, DUMP>(f, tl, a, lds, nfull * C::CZ, ZS, row, rok, acc);
+    }
+    if constexpr (!DUMP) {
+        if constexpr (KS > 1) {
+            // partial sums of the KS waves of each row tile, added in wave order
+            float *red = reinterpret_cast<float *>(lds);
+            lds_barrier();
+#pragma unroll
+            for (int cg = 0; cg < C::NCG; cg++) red[(wave * C::NCG + cg) * kWave + l] = acc[cg];
+            lds_barrier();
+            if (ks == 0) {
+#pragma unroll
+                for (int cg = 0; cg < C::NCG; cg++) {
+                    float s = red[((rt * KS) * C::NCG + cg) * kWave + l];
+#pragma unroll
+                    for (int k = 1; k < KS; k++) s += red[((rt * KS + k) * C::NCG + cg) * kWave + l];
+                    acc[cg] = s;
+                }
+            }
+        }
+        if (ks == 0) {
+#pragma unroll
+            for (int cg = 0; cg < C::NCG; cg++) {
+                const int no = 4 * cg + (l >> 4);
+                if (rok && no < N) out[(int64_t)no * a.rows + row] = acc[cg];
+            }
+        }
+    }
+}
+
+template <int N, int KS, int RTW, int IT, bool DUMP>
+hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                            hipStream_t s) {
+    using C = TiledCfg<N, KS, RTW, IT>;
+    MmvqArgs a;
+    a.xq = reinterpret_cast<const uint8_t *>(xq);
+    a.dump = dump;
+    a.rows = rows;
+    a.K = K;
+    a.colpack = 0x0706050403020100ull;
+    a.xstride = K / 32;
+    a.its = IT;
+    const int64_t tiles = (rows + 15) / 16;
+    const int64_t grid = (tiles + RTW - 1) / RTW;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP>), C::LDS);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP>), dim3((unsigned)grid), dim3(C::NTHR), C::LDS, s, w,
+                       a, out);
+    return hipGetLastError();
+}
+
+// Waves along K per row tile: about ten waves per CU in all, at most sixteen
+// per workgroup; workgroups of at least four waves.  A function of the row
+// count only, so every column count sums a row in the same order.
+template <int N, bool DUMP>
+hipError_t launch_tiled_n(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                          hipStream_t s) {
+    const int64_t tiles = (rows + 15) / 16;
+    if (tiles >= 2048) return launch_tiled_cfg<N, 1, 4, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (tiles >= 1024) return launch_tiled_cfg<N, 2, 2, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (tiles >= 512) return launch_tiled_cfg<N, 4, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (tiles >= 256) return launch_tiled_cfg<N, 8, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    return launch_tiled_cfg<N, 16, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
+}
+
+}  // namespace qmv

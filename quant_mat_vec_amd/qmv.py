@@ -18,7 +18,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qmv.h")
 
 QMV_OK, QMV_ERR_INVALID_ARG, QMV_ERR_UNSUPPORTED = 0, -1, -2
 QMV_ERR_ALIGNMENT, QMV_ERR_WORKSPACE, QMV_ERR_HIP = -3, -4, -5
-LAYOUT_GGUF, LAYOUT_PLANAR = 0, 1
+LAYOUT_GGUF, LAYOUT_PLANAR, LAYOUT_TILED = 0, 1, 2
 
 _lib = None
 
@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
             "mmvq_q5k": [P, P, P, I64, I64, I, P],
             "repack_q6k_planar": [P, P, I64, I64, P],
             "unpack_q6k_planar": [P, P, I64, I64, P],
+            "repack_q6k_tiled": [P, P, I64, I64, P],
+            "unpack_q6k_tiled": [P, P, I64, I64, P],
             "mmvq_q6k_isums": [P, I, P, P, I64, I64, I, P],
             "mmvq_q4k_isums": [P, P, P, I64, I64, I, P],
             "mmvq_q5k_isums": [P, P, P, I64, I64, I, P],
@@ -128,6 +130,14 @@ def repack_q6k_planar(src, dst, rows: int, K: int, stream=None) -> None:
 
 def unpack_q6k_planar(src, dst, rows: int, K: int, stream=None) -> None:
     _check(lib().unpack_q6k_planar(_ptr(src), _ptr(dst), rows, K, _stream(stream)), "unpack_q6k_planar")
+
+
+def repack_q6k_tiled(src, dst, rows: int, K: int, stream=None) -> None:
+    _check(lib().repack_q6k_tiled(_ptr(src), _ptr(dst), rows, K, _stream(stream)), "repack_q6k_tiled")
+
+
+def unpack_q6k_tiled(src, dst, rows: int, K: int, stream=None) -> None:
+    _check(lib().unpack_q6k_tiled(_ptr(src), _ptr(dst), rows, K, _stream(stream)), "unpack_q6k_tiled")
 
 
 def mmvq_q6k_isums(w, layout: int, xq, isums, rows: int, K: int, ncols: int, stream=None) -> None:

@@ -90,6 +90,12 @@ def planar(w: torch.Tensor, rows: int, K: int) -> torch.Tensor:
     return p
 
 
+def tiled(w: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    t = torch.empty_like(w)
+    qmv.repack_q6k_tiled(w, t, rows, K)
+    return t
+
+
 def assert_close(got: np.ndarray, ref: np.ndarray, absum: np.ndarray, what: str = "") -> None:
     got = got.astype(np.float64)
     err = np.abs(got - ref)

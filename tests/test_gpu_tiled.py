@@ -1,0 +1,194 @@
+"""GPU parity of the tiled Q6_K layout and its matrix-core kernel, through
+the C ABI, against the CPU oracle.
+
+Bars: bit-exact for the conversion (against the oracle's tiled layout and
+back to GGUF), the per-sub-block int32 sums and the column-count identities;
+fp32 outputs within 1e-5 of the oracle relative to the sum of absolute terms.
+The sizes cover every workgroup shape the kernel picks by tile count (1, 2,
+4, 8 and 16 waves along K), partial last tiles and workgroups, ragged and
+multi-chunk rows, each against the oracle on sampled rows at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from quant_mat_vec_amd import qmv, synth
+from tests.gpu_util import DEV, assert_close, dev, host, isums, mmvq, note, planar, quantize, tiled
+
+pytestmark = pytest.mark.gpu
+
+TL, PL, GG = qmv.LAYOUT_TILED, qmv.LAYOUT_PLANAR, qmv.LAYOUT_GGUF
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    qmv.lib()                      # fails loudly if the HIP library is missing
+
+
+def sampled(rows, g, n=40):
+    return sorted(set(g.choice(rows, size=min(n, rows), replace=False).tolist()) | {0, rows - 1})
+
+
+def rows_of(w, rs, K):
+    nb = K // 256 * 210
+    return np.concatenate([w[r * nb:(r + 1) * nb] for r in rs])
+
+
+# ------------------------------------------------------------ conversion
+@pytest.mark.parametrize("rows,K", [(1, 256), (7, 768), (16, 512), (33, 2560), (50, 10240)])
+def test_tiled_repack_bytes_and_roundtrip(rows, K):
+    note(f"repack_q6k_tiled rows={rows} K={K}")
+    w = synth.q6k_blocks(synth.rng(900 + rows), rows, K)
+    wd = dev(w)
+    t = tiled(wd, rows, K)
+    assert np.array_equal(host(t), orc.q6k_to_tiled(w, rows, K))
+    back = torch.empty_like(wd)
+    qmv.unpack_q6k_tiled(t, back, rows, K)
+    assert np.array_equal(host(back), w)
+
+
+# ------------------------------------------------------- small, all rows
+SMALL = [(1, 256, 1), (37, 768, 3), (19, 2560, 8), (9, 10240, 2), (70, 512, 5), (5, 1280, 8),
+         (40, 3584, 5), (130, 2560, 4), (17, 20480, 6)]
+
+
+@pytest.mark.parametrize("rows,K,ncols", SMALL)
+def test_tiled_isums_bitexact(rows, K, ncols):
+    note(f"mmvq_q6k_isums tiled rows={rows} K={K} ncols={ncols}")
+    g = synth.rng(910 + rows + K + ncols)
+    w = synth.q6k_blocks(g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    got = isums("q6k", tiled(dev(w), rows, K), xq, rows, K, ncols, TL)
+    assert np.array_equal(got, orc.q6k_isums(w, xq_np, rows, K))
+
+
+@pytest.mark.parametrize("rows,K,ncols", SMALL)
+def test_tiled_outputs_vs_oracle(rows, K, ncols):
+    note(f"mmvq_q6k tiled rows={rows} K={K} ncols={ncols}")
+    g = synth.rng(920 + rows + K + ncols)
+    w = synth.q6k_blocks(g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    ref, ab = orc.mmvq("q6k", w, xq_np, rows, K)
+    got = mmvq("q6k", tiled(dev(w), rows, K), xq, rows, K, ncols, TL)
+    assert_close(got, ref, ab, f"tiled {rows}x{K} N={ncols}")
+
+
+def test_tiled_exact_arithmetic_configuration_bitexact():
+    """Weights and activations whose every fp32 product and partial sum is
+    exact: the tiled kernel must then return the oracle's value exactly."""
+    note("exact-arithmetic q6k tiled")
+    g = synth.rng(500)
+    rows, K, ncols = 45, 2560, 8
+    w = synth.exact_q6k_blocks(g, rows, K)
+    xq_np = synth.exact_q8_1(g, ncols, K)
+    ref, _ = orc.mmvq("q6k", w, xq_np, rows, K)
+    got = mmvq("q6k", tiled(dev(w), rows, K), dev(xq_np), rows, K, ncols, TL)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("rows,K", [(64, 768), (64, 2560), (64, 10240), (8200, 2560)])
+def test_tiled_column_count_invariance(rows, K):
+    """Column c of an N-column call has the bits of a 1-column call on c."""
+    note(f"column invariance tiled {rows}x{K}")
+    g = synth.rng(930 + K)
+    w = tiled(dev(synth.q6k_blocks(g, rows, K)), rows, K)
+    xq, _ = quantize(synth.activations(g, 8, K))
+    full = mmvq("q6k", w, xq, rows, K, 8, TL)
+    for n in (2, 3, 5, 7):
+        part = mmvq("q6k", w, xq, rows, K, n, TL)
+        assert np.array_equal(part.view(np.uint32), full[:n].view(np.uint32)), n
+    nb = K // 32 * 36
+    for c in (0, 3, 4, 7):
+        one = mmvq("q6k", w, xq[c * nb:(c + 1) * nb], rows, K, 1, TL)
+        assert np.array_equal(one[0].view(np.uint32), full[c].view(np.uint32)), c
+
+
+# ------------------------------------------ full sizes, every launch shape
+# (rows, K, column counts): tiles >= 2048 -> one wave along K, four tiles per
+# workgroup (32805 rows: a partial tile and a workgroup with an empty tile
+# slot; 151936: the LM head); >= 1024 -> two waves, two tiles; >= 512 -> four
+# waves (10240 x 2560; 8200 x 10240: four chunks per row, a half tile);
+# >= 256 -> eight waves (4100 x 1280: a ragged chunk in which most waves have
+# no step); below -> sixteen waves (2560 x 10240).
+FULL = [(32805, 256, (8, 1)), (151936, 2560, (4, 1)), (16405, 512, (5, 2)), (10240, 2560, (8, 6, 4, 2, 1)),
+        (8200, 10240, (8, 3)), (4100, 1280, (3, 8)), (2560, 10240, (8, 4, 1))]
+
+
+@pytest.mark.parametrize("rows,K,cols", FULL)
+def test_tiled_full_size_sampled(rows, K, cols):
+    note(f"tiled full size {rows}x{K} N={cols}")
+    g = synth.rng(synth.seed_for(4, rows % 101, 8))
+    w = synth.q6k_blocks(g, rows, K)
+    wt = tiled(dev(w), rows, K)
+    xq, xq_np = quantize(synth.activations(g, 8, K))
+    rs = sampled(rows, g)
+    ws = rows_of(w, rs, K)
+    ref, ab = orc.mmvq("q6k", ws, xq_np, len(rs), K)
+    nb = K // 32 * 36
+    first = None
+    for n in cols:
+        got = mmvq("q6k", wt, xq[:n * nb], rows, K, n, TL)
+        assert_close(got[:, rs], ref[:n], ab[:n], f"tiled {rows}x{K} N={n} sampled rows")
+        if first is None:
+            first = got
+        else:
+            m = min(n, first.shape[0])
+            assert np.array_equal(got[:m].view(np.uint32), first[:m].view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,K,ncols", [(10240, 2560, 8), (2560, 10240, 4), (32805, 256, 3)])
+def test_tiled_isums_full_size_sampled(rows, K, ncols):
+    note(f"tiled isums full size {rows}x{K} N={ncols}")
+    g = synth.rng(synth.seed_for(5, rows % 101, ncols))
+    w = synth.q6k_blocks(g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    got = isums("q6k", tiled(dev(w), rows, K), xq, rows, K, ncols, TL)
+    rs = sampled(rows, g)
+    assert np.array_equal(got[:, rs], orc.q6k_isums(rows_of(w, rs, K), xq_np, len(rs), K))
+
+
+def test_tiled_agrees_with_planar():
+    """Same matrix in both planar layouts: outputs within fp32 rounding of
+    each other (different summation orders), integer sums identical."""
+    rows, K, ncols = 3000, 2560, 8
+    note(f"tiled vs planar {rows}x{K} N={ncols}")
+    g = synth.rng(940)
+    w = synth.q6k_blocks(g, rows, K)
+    wd = dev(w)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    pt, pp = tiled(wd, rows, K), planar(wd, rows, K)
+    assert np.array_equal(isums("q6k", pt, xq, rows, K, ncols, TL), isums("q6k", pp, xq, rows, K, ncols, PL))
+    a, b = mmvq("q6k", pt, xq, rows, K, ncols, TL), mmvq("q6k", pp, xq, rows, K, ncols, PL)
+    rs = sampled(rows, g)
+    ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np, len(rs), K)
+    assert_close(a[:, rs], ref, ab, "tiled")
+    assert np.all(np.abs(a.astype(np.float64) - b) <= 3e-5 * np.abs(b).max(axis=-1, keepdims=True))
+
+
+def test_tiled_graph_replay_matches_eager():
+    note("graph capture of quantize + tiled mmvq_q6k")
+    rows, K, ncols = 2048, 2560, 4
+    g = synth.rng(950)
+    w = tiled(dev(synth.q6k_blocks(g, rows, K)), rows, K)
+    x = dev(synth.activations(g, ncols, K))
+    xq = torch.empty(ncols * K // 32 * 36, dtype=torch.uint8, device=DEV)
+    out = torch.empty(ncols * rows, dtype=torch.float32, device=DEV)
+    qmv.quantize_q8_1(x, xq, K, ncols)
+    qmv.mmvq_q6k(w, TL, xq, out, rows, K, ncols)
+    eager = host(out).copy()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            qmv.quantize_q8_1(x, xq, K, ncols, stream=s)
+            qmv.mmvq_q6k(w, TL, xq, out, rows, K, ncols, stream=s)
+    for i in range(5):
+        out.fill_(float("nan"))
+        xq.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), eager.view(np.uint32)), f"replay {i}"
+        _ = (x * 2).sum().item()               # eager work between replays

@@ -24,7 +24,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = qmv.declared_symbols()
     expected = {"quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
-                "unpack_q6k_planar", "mmvq_q6k_isums", "mmvq_q4k_isums", "mmvq_q5k_isums",
+                "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "mmvq_q6k_isums",
+                "mmvq_q4k_isums", "mmvq_q5k_isums",
                 "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "qmv_strerror",
                 "qmv_last_hip_error", "qmv_stream_read"}
     assert expected <= set(names), set(names) ^ expected
@@ -77,16 +78,20 @@ def test_mmvq_rejects(L, name):
     assert call(xq=P + 2) == E_ALN
     assert call(out=P + 2) == E_ALN
     if q6:
-        assert call(layout=2) == E_UNS
+        assert call(layout=3) == E_UNS
         assert call(layout=-1) == E_UNS
         assert call(w=P + 8, layout=qmv.LAYOUT_PLANAR) == E_ALN
+        assert call(w=P + 8, layout=qmv.LAYOUT_TILED) == E_ALN
+        assert call(K=300, layout=qmv.LAYOUT_TILED) == E_UNS
+        assert call(ncols=9, layout=qmv.LAYOUT_TILED) == E_UNS
         assert call(w=P + 2, layout=qmv.LAYOUT_GGUF) == E_ALN
     else:
         assert call(w=P + 8) == E_ALN
 
 
 def test_repack_rejects(L):
-    for fn, a_src, a_dst in ((L.repack_q6k_planar, 2, 16), (L.unpack_q6k_planar, 16, 2)):
+    for fn, a_src, a_dst in ((L.repack_q6k_planar, 2, 16), (L.unpack_q6k_planar, 16, 2),
+                             (L.repack_q6k_tiled, 2, 16), (L.unpack_q6k_tiled, 16, 2)):
         assert fn(None, P, 4, 256, None) == E_INV
         assert fn(P, None, 4, 256, None) == E_INV
         assert fn(P, P + 4096, 0, 256, None) == E_INV
@@ -122,6 +127,7 @@ def test_moe_rejects_and_workspace(L):
     assert call(dm=2500) == E_UNS
     assert call(dff=700) == E_UNS
     assert call(lay=5) == E_UNS
+    assert call(lay=qmv.LAYOUT_TILED) == E_UNS     # the expert path takes GGUF or planar
     assert call(ws=None) == E_WS
     assert call(wsb=ws_size - 1) == E_WS
     assert call(ws=P + 64) == E_ALN

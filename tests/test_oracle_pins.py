@@ -423,6 +423,32 @@ def test_planar_layout_pins():
         assert flips == 1
 
 
+def test_tiled_layout_pins():
+    """The tiled layout is the (pinned) planar one with the entries of every
+    16-row group interleaved: for one row it is the planar layout itself,
+    and for any row count each plane is the planar plane with [row][position]
+    turned into [position][row] inside every tile (a numpy transpose, the
+    last tile R = rows % 16 rows high)."""
+    for rows, K in [(1, 512), (16, 256), (37, 768)]:
+        w = synth.q6k_blocks(synth.rng(72 + rows), rows, K)
+        P = orc.q6k_to_planar(w, rows, K)
+        T = orc.q6k_to_tiled(w, rows, K)
+        assert T.size == P.size
+        if rows == 1:
+            assert np.array_equal(T, P)
+        NB, nsb, nb = rows * K // 256, K // 32, K // 256
+        for lo, hi, esz, npos in [(0, 128 * NB, 16, nsb), (128 * NB, 192 * NB, 8, nsb),
+                                  (192 * NB, 208 * NB, 8, nsb // 4), (208 * NB, 210 * NB, 2, nb)]:
+            p = P[lo:hi].reshape(rows, npos, esz)
+            t = T[lo:hi]
+            off = 0
+            for r0 in range(0, rows, 16):
+                part = p[r0:r0 + 16].transpose(1, 0, 2).reshape(-1)
+                assert np.array_equal(t[off:off + part.size], part), (rows, K, lo, r0)
+                off += part.size
+            assert off == hi - lo
+
+
 # ----------------------------------------------------------------- MoE
 def test_moe_chain_vs_fp64_bruteforce():
     g = synth.rng(81)
