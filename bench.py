@@ -4,8 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 
 Workload (one "step"): quantize 13 fp32 activation columns to Q8_1 in one
-launch, then run the planar Q6_K MMVQ of a 10240 x 2560 (rows x cols) matrix
-at N = 1, 4 and 8 columns (each product on its own columns: 1 + 4 + 8 = 13)
+launch, then run the Q6_K MMVQ of a 10240 x 2560 (rows x cols) matrix in the
+tiled layout (int8 matrix-core kernel) at N = 1, 4 and 8 columns (each product on its own columns: 1 + 4 + 8 = 13)
 -- the decode matrix the pages measure as "2560 x 10240" (n_in x n_out).  Weights are resident in HBM before timing and
 each launch reads a different one of 26 copies (559 MB, more than twice the
 256 MB Infinity Cache), so every weight byte comes from HBM.
@@ -36,7 +36,7 @@ ROWS, K = 10240, 2560
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on a
 # plain copy of known size (FETCH_SIZE x 1.9977, WRITE_SIZE x 1.0); to be
 # emptied whenever the kernel changes after the counters were taken.
-TRAFFIC = {1: 21656205, 4: 21876219, 8: 22173025}
+TRAFFIC = {1: 21680957, 4: 21877155, 8: 22159641}
 NCOLS = (1, 4, 8)
 XCOLS = sum(NCOLS)          # distinct activation columns quantized per step
 COL0 = {1: 0, 4: 1, 8: 5}   # first activation column of each product
@@ -123,7 +123,7 @@ def main():
     # all work on one non-default stream (graph capture needs one; default
     # priority, like every stream here)
     torch.cuda.set_stream(torch.cuda.Stream())
-    PL = qmv.LAYOUT_PLANAR
+    TL = qmv.LAYOUT_TILED
     g = synth.rng(synth.seed_for(1, 1, 8))
     w_np = synth.q6k_blocks(g, ROWS, K)
     x_np = synth.activations(g, XCOLS, K)
@@ -131,7 +131,7 @@ def main():
     ncopies = max(2, math.ceil(2 * MALL_BYTES / wb) + 1)
     w_gguf = torch.from_numpy(w_np).to(dev)
     base = torch.empty_like(w_gguf)
-    qmv.repack_q6k_planar(w_gguf, base, ROWS, K)
+    qmv.repack_q6k_tiled(w_gguf, base, ROWS, K)
     copies = [base.clone() for _ in range(ncopies)]
     xd = torch.from_numpy(x_np).to(dev)
     xq_all = torch.empty(XCOLS * (K // 32) * 36, dtype=torch.uint8, device=dev)
@@ -153,7 +153,7 @@ def main():
         qmv.quantize_q8_1(xd, xq_all, K, XCOLS)
         for n in NCOLS:
             for i in range(30):
-                qmv.mmvq_q6k(copies[i % ncopies], PL, xq_of(n), out, ROWS, K, n)
+                qmv.mmvq_q6k(copies[i % ncopies], TL, xq_of(n), out, ROWS, K, n)
         dst = torch.empty_like(base)
         for i in range(30):
             dst.copy_(copies[i % ncopies])
@@ -164,7 +164,7 @@ def main():
         qmv.quantize_q8_1(xd, xq_all, K, XCOLS)
         for j, n in enumerate(NCOLS):
             c = copies[(len(NCOLS) * i + j) % ncopies]
-            qmv.mmvq_q6k(c, PL, xq_of(n), out, ROWS, K, n)
+            qmv.mmvq_q6k(c, TL, xq_of(n), out, ROWS, K, n)
 
     # Step i uses weight copies at rotation offset i % ncopies.  HIP graphs:
     # one holding `ncopies` consecutive steps (offsets 0 .. ncopies-1, so the
@@ -223,7 +223,7 @@ def main():
         gph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gph, stream=stream):
             for i in range(per_graph):
-                qmv.mmvq_q6k(copies[i % ncopies], PL, xq_of(n), out, ROWS, K, n)
+                qmv.mmvq_q6k(copies[i % ncopies], TL, xq_of(n), out, ROWS, K, n)
         gph.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -233,7 +233,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         mean = a.elapsed_time(b) * 1e3 / (reps * per_graph)
-        per_n[n] = {"kernel": f"qmv::k_mmvq_dense<qmv::Q6Planar, {n}, 16, 4, 5, false>",
+        per_n[n] = {"kernel": f"qmv::k_mmvq_q6_tiled<{n}, 4, 1, 5, false>",
                     "avg_launch_us": round(mean, 3),
                     "weight_GBps": round(wb / (mean * 1e-6) / 1e9, 1),
                     "weight_frac_of_8TBps": round(wb / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -250,7 +250,7 @@ def main():
     # eager launches with per-launch events (host launch path included)
     eager = {}
     for n in NCOLS:
-        r = timed_launches(torch, lambda c, n=n: qmv.mmvq_q6k(c, PL, xq_of(n), out, ROWS, K, n), 100, copies)
+        r = timed_launches(torch, lambda c, n=n: qmv.mmvq_q6k(c, TL, xq_of(n), out, ROWS, K, n), 100, copies)
         eager[str(n)] = round(r["mean_us"], 3)
 
     # checksum of the last step's N=8 output bits (FNV-1a 32)
@@ -284,7 +284,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": round(value / pages_gbs, 2), "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "Q6_K MMVQ 10240x2560 (rows x cols), planar weights, 1/4/8 columns, "
+        "config": {"workload": "Q6_K MMVQ 10240x2560 (rows x cols), tiled weights (matrix cores), 1/4/8 columns, "
                                "one Q8_1 quantize of the 13 activation columns + the three MMVQs, "
                                f"weights rotated over {ncopies} HBM copies",
                    "rows": ROWS, "cols": K, "ncols": list(NCOLS),
@@ -298,14 +298,14 @@ def main():
 
 
 def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
-    PL, GG = qmv.LAYOUT_PLANAR, qmv.LAYOUT_GGUF
+    PL, GG, TL = qmv.LAYOUT_PLANAR, qmv.LAYOUT_GGUF, qmv.LAYOUT_TILED
     ex = {}
     it = 200
     # cache-warm: the same buffer every launch (Infinity Cache / L2 resident)
     warm = {}
     for n in NCOLS:
         qmv.quantize_q8_1(xd, xq, K, n)
-        us = graph_avg_us(torch, [lambda n=n: qmv.mmvq_q6k(base, PL, xq, out, ROWS, K, n)] * 52)
+        us = graph_avg_us(torch, [lambda n=n: qmv.mmvq_q6k(base, TL, xq, out, ROWS, K, n)] * 52)
         warm[str(n)] = {"avg_launch_us": round(us, 3),
                         "weight_GBps_not_hbm": round(weight_bytes(ROWS, K) / (us * 1e-6) / 1e9, 1)}
     ex["cache_warm_not_hbm"] = warm
@@ -321,14 +321,14 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
     ex["copy_calibration"] = {"bytes_read": wb, "avg_launch_us": round(us, 3),
                               "read_plus_write_GBps": round(2 * wb / (us * 1e-6) / 1e9, 1)}
 
-    def shape_case(kind, rows, k, ncols_list, layout=PL, seed=0):
+    def shape_case(kind, rows, k, ncols_list, layout=TL, seed=0):
         g = synth.rng(seed)
         per = {"q6k": 210, "q4k": 144, "q5k": 176}[kind]
         w = torch.from_numpy(synth.blocks(kind, g, rows, k)).to(dev)
         wbytes = weight_bytes(rows, k, per)
-        if kind == "q6k" and layout == PL:
+        if kind == "q6k" and layout != GG:
             p = torch.empty_like(w)
-            qmv.repack_q6k_planar(w, p, rows, k)
+            (qmv.repack_q6k_planar if layout == PL else qmv.repack_q6k_tiled)(w, p, rows, k)
             w = p
         nc = max(2, math.ceil(2 * MALL_BYTES / wbytes) + 1)
         cs = [w] + [w.clone() for _ in range(nc - 1)]
@@ -352,10 +352,13 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
         torch.cuda.empty_cache()
         return res
 
-    ex["q6k_2560x10240"] = shape_case("q6k", 2560, 10240, (1, 2, 4, 6, 8), seed=11)
+    ex["q6k_10240x2560_planar_dot4"] = shape_case("q6k", 10240, 2560, (1, 2, 4, 6, 8), layout=PL, seed=12)
     ex["q6k_10240x2560_2_6cols"] = shape_case("q6k", 10240, 2560, (2, 6), seed=12)
+    ex["q6k_2560x10240"] = shape_case("q6k", 2560, 10240, (1, 2, 4, 6, 8), seed=11)
+    ex["q6k_2560x10240_planar_dot4"] = shape_case("q6k", 2560, 10240, (1, 2, 4, 6, 8), layout=PL, seed=11)
     ex["q6k_2560x2560"] = shape_case("q6k", 2560, 2560, (1,), seed=13)
     ex["q6k_lm_head_151936x2560"] = shape_case("q6k", 151936, 2560, (1, 4), seed=14)
+    ex["q6k_lm_head_151936x2560_planar_dot4"] = shape_case("q6k", 151936, 2560, (1, 4), layout=PL, seed=14)
     ex["q6k_lm_head_151936x2560_gguf"] = shape_case("q6k", 151936, 2560, (1, 4), layout=GG, seed=14)
     for kind in ("q4k", "q5k"):
         for (r_, k_) in ((12288, 2560), (6144, 2560), (2560, 6144), (512, 2560)):

@@ -289,17 +289,17 @@ hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *
     return hipGetLastError();
 }
 
-// Waves along K per row tile: about ten waves per CU in all, at most sixteen
-// per workgroup; workgroups of at least four waves.  A function of the row
-// count only, so every column count sums a row in the same order.
+// Waves along K per row tile: enough waves of five steps to cover a row in
+// one chunk (at most sixteen), and workgroups of at least four waves.  A
+// function of K only, so every column count sums a row in the same order.
 template <int N, bool DUMP>
 hipError_t launch_tiled_n(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                           hipStream_t s) {
-    const int64_t tiles = (rows + 15) / 16;
-    if (tiles >= 2048) return launch_tiled_cfg<N, 1, 4, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    if (tiles >= 1024) return launch_tiled_cfg<N, 2, 2, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    if (tiles >= 512) return launch_tiled_cfg<N, 4, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    if (tiles >= 256) return launch_tiled_cfg<N, 8, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    const int64_t need = (K / 128 + 4) / 5;
+    if (need <= 1) return launch_tiled_cfg<N, 1, 4, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (need <= 2) return launch_tiled_cfg<N, 2, 2, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
     return launch_tiled_cfg<N, 16, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
 }
 

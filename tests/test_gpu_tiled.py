@@ -4,7 +4,7 @@ the C ABI, against the CPU oracle.
 Bars: bit-exact for the conversion (against the oracle's tiled layout and
 back to GGUF), the per-sub-block int32 sums and the column-count identities;
 fp32 outputs within 1e-5 of the oracle relative to the sum of absolute terms.
-The sizes cover every workgroup shape the kernel picks by tile count (1, 2,
+The sizes cover every workgroup shape the kernel picks by row length (1, 2,
 4, 8 and 16 waves along K), partial last tiles and workgroups, ragged and
 multi-chunk rows, each against the oracle on sampled rows at full size.
 """
@@ -106,14 +106,16 @@ def test_tiled_column_count_invariance(rows, K):
 
 
 # ------------------------------------------ full sizes, every launch shape
-# (rows, K, column counts): tiles >= 2048 -> one wave along K, four tiles per
-# workgroup (32805 rows: a partial tile and a workgroup with an empty tile
-# slot; 151936: the LM head); >= 1024 -> two waves, two tiles; >= 512 -> four
-# waves (10240 x 2560; 8200 x 10240: four chunks per row, a half tile);
-# >= 256 -> eight waves (4100 x 1280: a ragged chunk in which most waves have
-# no step); below -> sixteen waves (2560 x 10240).
-FULL = [(32805, 256, (8, 1)), (151936, 2560, (4, 1)), (16405, 512, (5, 2)), (10240, 2560, (8, 6, 4, 2, 1)),
-        (8200, 10240, (8, 3)), (4100, 1280, (3, 8)), (2560, 10240, (8, 4, 1))]
+# The kernel takes ceil(K/640) waves along K (rounded up to 1, 2, 4, 8, 16):
+# K = 256, 512 -> one wave, four tiles per workgroup (32805 rows: a partial
+# tile and a workgroup with an empty tile slot); K = 768, 1280 -> two waves,
+# two tiles (4100 x 1280: a ragged chunk); K = 2560 -> four waves (10240 x
+# 2560, the LM head, 2560 x 2560); K = 5120 -> eight; K = 10240 -> sixteen
+# (2560 x 10240); K = 20480 -> sixteen with two chunks per row (8200 rows: a
+# half tile).
+FULL = [(32805, 256, (8, 1)), (16405, 512, (5, 2)), (4100, 1280, (3, 8)), (10240, 2560, (8, 6, 4, 2, 1)),
+        (151936, 2560, (4, 1)), (2560, 2560, (1, 7)), (3000, 5120, (8, 2)), (2560, 10240, (8, 4, 1)),
+        (8200, 20480, (8, 3))]
 
 
 @pytest.mark.parametrize("rows,K,cols", FULL)
