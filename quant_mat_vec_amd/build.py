@@ -17,9 +17,11 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqmv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# -packed-fp32-ops off: no v_pk_*_f32 in any kernel.
+# -packed-fp32-ops off: no v_pk_*_f32 in any kernel.  amdgpu-mfma-vgpr-form:
+# matrix-core results go straight to VGPRs (no accumulation-register copies).
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-command-line-argument",
          "-I", os.path.join(os.path.dirname(HERE), "include")]
 

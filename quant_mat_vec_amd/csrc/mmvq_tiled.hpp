@@ -71,12 +71,15 @@ struct TiledCfg {
     static constexpr int PRE = kTiledPre < IT ? kTiledPre : IT;
 };
 
-// Per-lane position in the tiled planes.
+// Position of a lane in the tiled planes: a wave-uniform base per plane (the
+// first entry of the wave's tile) and the tile height R, which the compiler
+// keeps in scalar registers, plus fixed 32-bit lane offsets, so that every
+// load is a scalar base + the same vector offset (no per-step vector address
+// arithmetic).
 struct TiledLane {
-    int64_t piece0;    // A/B entry of (row, sub-block 0)
-    int64_t sc0;       // SC entry of (row, step 0)
-    int64_t d0;        // D entry of (row, block 0)
-    int R;             // rows of the lane's tile: entry stride between positions
+    const uint8_t *a, *b, *sc, *d;   // tile bases of planes A, B, SC, D
+    int R;                            // rows of the tile: entry stride between positions
+    uint32_t oa, ob, osc, od;         // lane byte offsets: (row, k-group) in A/B, row in SC/D
 };
 
 // One chunk of CZ steps starting at step zc0: wave ks of the row tile takes
@@ -87,7 +90,8 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane &t
                                             float (&acc)[TiledCfg<N, KS, RTW, IT>::NCG]) {
     using C = TiledCfg<N, KS, RTW, IT>;
     constexpr int TNB = C::TNB, NTHR = C::NTHR;
-    const int tid = threadIdx.x, l = tid & (kWave - 1), ks = (tid / kWave) % KS, kg = l >> 4;
+    const int tid = threadIdx.x, l = tid & (kWave - 1), kg = l >> 4;
+    const int ks = __builtin_amdgcn_readfirstlane(tid / kWave) % KS;    // wave-uniform
     const int64_t nsb = f.nsb;
     const int nblk = FULL ? TNB : min(TNB, (int)(nsb - 4 * (int64_t)zc0));
 
@@ -112,17 +116,18 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane &t
     for (int it = 0; it < IT; it++) {
         const int z = zc0 + ks * IT + it;
         zs[it] = FULL ? z : min(z, ZS - 1);
-        wsc[it] = f.SC[tl.sc0 + (int64_t)zs[it] * tl.R];
-        wd[it] = f.D[tl.d0 + (int64_t)(zs[it] >> 1) * tl.R];
+        const int64_t zr = (int64_t)zs[it] * tl.R;                 // wave-uniform
+        wsc[it] = *reinterpret_cast<const uint2 *>(tl.sc + 8 * zr + tl.osc);
+        wd[it] = *reinterpret_cast<const uint16_t *>(tl.d + 2 * ((int64_t)(zs[it] >> 1) * tl.R) + tl.od);
     }
     __builtin_amdgcn_sched_barrier(0);
     auto load_ab = [&](auto lo_c, auto hi_c) {
         constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
 #pragma unroll
         for (int it = LO; it < HI; it++) {
-            const int64_t e = tl.piece0 + (int64_t)(4 * zs[it] + kg) * tl.R;
-            wa[it] = f.A[e];
-            wb[it] = f.B[e];
+            const int64_t zr = (int64_t)zs[it] * tl.R;             // wave-uniform
+            wa[it] = *reinterpret_cast<const uint4 *>(tl.a + 64 * zr + tl.oa);
+            wb[it] = *reinterpret_cast<const uint2 *>(tl.b + 32 * zr + tl.ob);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -212,21 +217,27 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
     extern __shared__ __align__(16) uint8_t lds[];
     Q6Tiled f;
     f.init(w, a.rows, a.K);
-    const int tid = threadIdx.x, l = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, l = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int ks = wave % KS, rt = wave / KS;
-    // the lane's tile and row; lanes past the last row load from a row that
-    // exists and store nothing
+    // the wave's tile and the lane's row; lanes past the last row load from a
+    // row that exists and store nothing
     const int64_t ntiles = (a.rows + 15) / 16;
     const int64_t tile = (int64_t)blockIdx.x * RTW + rt, tc = min(tile, ntiles - 1);
     const int R = (int)min((int64_t)16, a.rows - 16 * tc);
-    const int r = l & 15, rr = min(r, R - 1);
+    const int r = l & 15, rr = min(r, R - 1), kg = l >> 4;
     const int64_t row = 16 * tile + r;
     const bool rok = tile < ntiles && r < R;
     TiledLane tl;
     tl.R = R;
-    tl.piece0 = 16 * tc * f.nsb + rr;
-    tl.sc0 = 16 * tc * (f.nsb / 4) + rr;
-    tl.d0 = 16 * tc * f.nb + rr;
+    tl.a = reinterpret_cast<const uint8_t *>(f.A + 16 * tc * f.nsb);
+    tl.b = reinterpret_cast<const uint8_t *>(f.B + 16 * tc * f.nsb);
+    tl.sc = reinterpret_cast<const uint8_t *>(f.SC + 16 * tc * (f.nsb / 4));
+    tl.d = reinterpret_cast<const uint8_t *>(f.D + 16 * tc * f.nb);
+    tl.oa = 16u * (uint32_t)(kg * R + rr);
+    tl.ob = 8u * (uint32_t)(kg * R + rr);
+    tl.osc = 8u * (uint32_t)rr;
+    tl.od = 2u * (uint32_t)rr;
     const int ZS = (int)(a.K / 128);
     float acc[C::NCG];
 #pragma unroll
