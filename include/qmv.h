@@ -156,6 +156,33 @@ int unpack_q6k_planar(const void *src, void *dst, int64_t rows, int64_t K, void 
 int repack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
 int unpack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *stream);
 
+/* Row gather within one layout (the draft head's row subset taken from the
+ * converted LM head, PR #2340 "What it changes"): dst is the nout x K Q6_K
+ * matrix, in the same `layout` as src (rows x K), whose row j is src row
+ * ids[j].  ids: int32 [nout], device memory, 4-byte aligned; an id outside
+ * [0, rows) yields an all-zero row (device data, so not checked on the host).
+ * src/dst: GGUF any alignment, planar and tiled 16-byte aligned; they must
+ * not overlap.  Load-time only. */
+int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const int32_t *ids,
+                    int64_t nout, void *dst, void *stream);
+
+/* Greedy argmax over the rows of the product (the verify window's next-token
+ * choice over an LM head, without writing rows x ncols outputs): for each
+ * column n, idx[n] = the row r with the largest out[n][r] of mmvq_q6k and
+ * val[n] = that value, bit for bit the fp32 output mmvq_q6k gives for the
+ * same inputs; among equal values the lowest row wins, -0 counts as +0.
+ * Tiled layout only (QMV_LAYOUT_TILED; others: QMV_ERR_UNSUPPORTED).
+ * idx int32 [ncols], val fp32 [ncols] (4-byte aligned); ws: device
+ * workspace of at least mmvq_q6k_argmax_workspace(rows, ncols) bytes,
+ * 8-byte aligned, overwritten (one 8-byte key per 16-row tile and column).
+ * Other arguments and checks as for mmvq_q6k.  Two launches: the product
+ * with per-tile maxima, then one reduction per column.  Outputs must be
+ * finite. */
+int mmvq_q6k_argmax(const void *w, int layout, const void *xq, int64_t rows, int64_t K,
+                    int ncols, int32_t *idx, float *val, void *ws, size_t ws_bytes,
+                    void *stream);
+size_t mmvq_q6k_argmax_workspace(int64_t rows, int ncols);
+
 /* Per-sub-block integer sums of the same kernels (for verification):
  * isums int32 [ncols][rows][K/32].  Q6_K: sum over the sub-block's two
  * 16-weight groups of scale * sum (q6-32)*q8.  Q4_K/Q5_K: sum q*q8 of the

@@ -55,6 +55,7 @@ def lib():
         for name in ("orc_dequant_q6k", "orc_dequant_q4k", "orc_dequant_q5k",
                      "orc_q6k_to_planar", "orc_q6k_to_tiled"):
             getattr(L, name).argtypes = [P, P, I64, I64]
+        L.orc_q6k_gather.argtypes = [P, I, I64, I64, P, I64, P]
         L.orc_quantize_q8_1.argtypes = [P, P, I64, I]
         L.orc_dequant_q8_1.argtypes = [P, P, I64, I]
         for name in ("orc_q6k_isums", "orc_q4k_dots", "orc_q5k_dots"):
@@ -189,6 +190,16 @@ def q6k_to_tiled(w, rows: int, K: int):
     w = _u8(w)
     dst = np.zeros(w.size, np.uint8)
     lib().orc_q6k_to_tiled(_p(w), _p(dst), rows, K)
+    return dst
+
+
+def q6k_gather(w, layout: int, rows: int, K: int, ids):
+    """Rows ids of the GGUF matrix w, in `layout` (0 GGUF, 1 planar, 2 tiled);
+    ids outside [0, rows) give all-zero rows."""
+    w = _u8(w)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    dst = np.zeros(ids.size * (K // 256) * Q6K_BYTES, np.uint8)
+    lib().orc_q6k_gather(_p(w), layout, rows, K, _p(ids), ids.size, _p(dst))
     return dst
 
 

@@ -510,6 +510,52 @@ void orc_q6k_to_tiled(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K)
     free(pl);
 }
 
+/* ----------------------------------------------------------- row gather
+ * Row subset of a converted matrix (the draft head gathered from the planar
+ * LM head, P2340 "What it changes"): output row j is source row ids[j], in
+ * the same layout (0 GGUF, 1 planar, 2 tiled); an id outside [0, rows)
+ * gives a row whose bytes are all zero in that layout.  Computed from the
+ * GGUF source: gather the GGUF rows, convert, then clear the entries of the
+ * rows with a bad id (positions as in the layout text above). */
+static void orc_zero_row(uint8_t *dst, int layout, int64_t rows, int64_t K, int64_t row) {
+    const int64_t nb = K / QK, nsb = K / 32, NB = rows * nb;
+    if (layout == 0) {
+        memset(dst + row * nb * Q6K_BYTES, 0, (size_t)(nb * Q6K_BYTES));
+        return;
+    }
+    const int64_t T = row / 16, r = row % 16, R = layout == 2 ? (rows - 16 * T < 16 ? rows - 16 * T : 16) : 0;
+    for (int64_t s = 0; s < nsb; s++) {
+        const int64_t e = layout == 2 ? 16 * T * nsb + s * R + r : row * nsb + s;
+        memset(dst + 16 * e, 0, 16);
+        memset(dst + 128 * NB + 8 * e, 0, 8);
+    }
+    for (int64_t z = 0; z < nsb / 4; z++) {
+        const int64_t e = layout == 2 ? 16 * T * (nsb / 4) + z * R + r : row * (nsb / 4) + z;
+        memset(dst + 192 * NB + 8 * e, 0, 8);
+    }
+    for (int64_t b = 0; b < nb; b++) {
+        const int64_t e = layout == 2 ? 16 * T * nb + b * R + r : row * nb + b;
+        memset(dst + 208 * NB + 2 * e, 0, 2);
+    }
+}
+
+void orc_q6k_gather(const uint8_t *src, int layout, int64_t rows, int64_t K, const int32_t *ids, int64_t nout,
+                    uint8_t *dst) {
+    const int64_t rb = K / QK * Q6K_BYTES;
+    uint8_t *g = (uint8_t *)malloc((size_t)(rb * nout));
+    if (!g) abort();
+    for (int64_t j = 0; j < nout; j++) {
+        if (ids[j] >= 0 && ids[j] < rows) memcpy(g + j * rb, src + (int64_t)ids[j] * rb, (size_t)rb);
+        else memset(g + j * rb, 0, (size_t)rb);
+    }
+    if (layout == 1) orc_q6k_to_planar(g, dst, nout, K);
+    else if (layout == 2) orc_q6k_to_tiled(g, dst, nout, K);
+    else memcpy(dst, g, (size_t)(rb * nout));
+    for (int64_t j = 0; j < nout; j++)
+        if (!(ids[j] >= 0 && ids[j] < rows)) orc_zero_row(dst, layout, nout, K, j);
+    free(g);
+}
+
 /* ------------------------------------------------------ grouped MoE
  * Routed-expert chain over a window of T tokens [I2801; P2746 "B70
  * validation"], for each token t and slot k (slot index t*topk + k):

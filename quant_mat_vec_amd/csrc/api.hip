@@ -152,6 +152,43 @@ int unpack_q6k_tiled(const void *src, void *dst, int64_t rows, int64_t K, void *
                                        rows, K, true, as_stream(stream)));
 }
 
+int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const int32_t *ids, int64_t nout,
+                    void *dst, void *stream) {
+    if (!src || !dst || !ids) return QMV_ERR_INVALID_ARG;
+    if (rows <= 0 || K <= 0 || nout <= 0) return QMV_ERR_INVALID_ARG;
+    if (layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR && layout != QMV_LAYOUT_TILED)
+        return QMV_ERR_UNSUPPORTED;
+    if (K % 256 != 0 || K > kMaxK || rows > kMaxRows || nout > kMaxRows) return QMV_ERR_UNSUPPORTED;
+    const int64_t sb = rows * (K / 256) * 210, db = nout * (K / 256) * 210;
+    if (sb >= kMaxBytes || db >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
+    const uintptr_t al = layout == QMV_LAYOUT_GGUF ? 1 : 16;
+    if (!aligned(src, al) || !aligned(dst, al) || !aligned(ids, 4)) return QMV_ERR_ALIGNMENT;
+    const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
+    if (s < d + (uintptr_t)db && d < s + (uintptr_t)sb) return QMV_ERR_INVALID_ARG;   // overlap
+    return from_hip(qmv::launch_gather(reinterpret_cast<const uint8_t *>(src), reinterpret_cast<uint8_t *>(dst), ids,
+                                       rows, nout, K, layout, as_stream(stream)));
+}
+
+size_t mmvq_q6k_argmax_workspace(int64_t rows, int ncols) {
+    if (rows <= 0 || rows > kMaxRows || ncols < 1 || ncols > 8) return 0;
+    return (size_t)((((rows + 15) / 16) * ncols * 8 + 255) & ~int64_t(255));
+}
+
+int mmvq_q6k_argmax(const void *w, int layout, const void *xq, int64_t rows, int64_t K, int ncols, int32_t *idx,
+                    float *val, void *ws, size_t ws_bytes, void *stream) {
+    if (!idx || !val || !ws) return QMV_ERR_INVALID_ARG;
+    if (layout != QMV_LAYOUT_TILED) {
+        if (!w || !xq) return QMV_ERR_INVALID_ARG;
+        return QMV_ERR_UNSUPPORTED;
+    }
+    int rc = check_mmvq(w, xq, idx, rows, K, ncols, 210, 16);
+    if (rc) return rc;
+    if (!aligned(val, 4) || !aligned(ws, 8)) return QMV_ERR_ALIGNMENT;
+    if (ws_bytes < mmvq_q6k_argmax_workspace(rows, ncols)) return QMV_ERR_WORKSPACE;
+    return from_hip(qmv::launch_mmvq_q6_tiled_argmax(w, xq, reinterpret_cast<uint64_t *>(ws), rows, K, ncols, idx,
+                                                     val, as_stream(stream)));
+}
+
 size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff) {
     if (E < 1 || T < 1 || T > 8 || topk < 1 || topk > 8 || d_model < 256 || d_ff < 256 || d_model % 256 ||
         d_ff % 256 || d_model > kMaxK || d_ff > kMaxK)

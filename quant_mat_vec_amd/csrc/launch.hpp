@@ -22,11 +22,16 @@ hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hi
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s);
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s);
 hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s);
+// Q6_K row gather within one layout (0 GGUF, 1 planar, 2 tiled)
+hipError_t launch_gather(const uint8_t *src, uint8_t *dst, const int32_t *ids, int64_t rows, int64_t nout,
+                         int64_t K, int layout, hipStream_t s);
 
 hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int32_t *dump,
                                  int64_t rows, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump,
                                 int64_t rows, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
+                                       int ncols, int32_t *idx, float *val, hipStream_t s);
 hipError_t launch_mmvq_q6_gguf(const void *w, const void *xq, float *out, int32_t *dump,
                                int64_t rows, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_mmvq_q4(const void *w, const void *xq, float *out, int32_t *dump,

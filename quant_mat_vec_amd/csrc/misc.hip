@@ -206,6 +206,61 @@ hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, in
     return hipGetLastError();
 }
 
+// Row gather in one layout: output row j is source row ids[j] (a draft head
+// taken from the planar LM head).  One thread per (output row, block): the
+// block's eight A and B pieces, its two scale halves and d.  GGUF layout
+// (LAYOUT 0): the 210-byte block is copied as it is.  An id outside
+// [0, rows) gives an all-zero output row.
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void k_gather_q6k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
+                                                    const int32_t *__restrict__ ids, int64_t rows, int64_t nout,
+                                                    int64_t nb) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= nout * nb) return;
+    const int64_t j = gid / nb, b = gid - j * nb;
+    const int32_t id = ids[j];
+    const bool ok = id >= 0 && id < rows;
+    const int64_t ts = (ok ? id : 0) * nb + b, td = j * nb + b;   // source and output block
+    if constexpr (LAYOUT == 0) {
+        const uint8_t *ps = src + ts * kQ6Bytes;
+        uint8_t *pd = dst + td * kQ6Bytes;
+        for (int k = 0; k < kQ6Bytes; k++) pd[k] = ok ? ps[k] : 0;
+    } else {
+        constexpr bool TILED = LAYOUT == 2;
+        const int64_t NBs = rows * nb, NBd = nout * nb;
+        int64_t sp, sps, sh, shs, sd, dp, dps, dh, dhs, dd;
+        PlaneIndex<TILED>{rows, nb}.at(ts, sp, sps, sh, shs, sd);
+        PlaneIndex<TILED>{nout, nb}.at(td, dp, dps, dh, dhs, dd);
+        const uint4 z4 = make_uint4(0, 0, 0, 0);
+        const uint2 z2 = make_uint2(0, 0);
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            reinterpret_cast<uint4 *>(dst)[dp + k * dps] = ok ? reinterpret_cast<const uint4 *>(src)[sp + k * sps] : z4;
+            reinterpret_cast<uint2 *>(dst + 128 * NBd)[dp + k * dps] =
+                ok ? reinterpret_cast<const uint2 *>(src + 128 * NBs)[sp + k * sps] : z2;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; h++)
+            reinterpret_cast<uint2 *>(dst + 192 * NBd)[dh + h * dhs] =
+                ok ? reinterpret_cast<const uint2 *>(src + 192 * NBs)[sh + h * shs] : z2;
+        reinterpret_cast<uint16_t *>(dst + 208 * NBd)[dd] =
+            ok ? reinterpret_cast<const uint16_t *>(src + 208 * NBs)[sd] : (uint16_t)0;
+    }
+}
+
+hipError_t launch_gather(const uint8_t *src, uint8_t *dst, const int32_t *ids, int64_t rows, int64_t nout,
+                         int64_t K, int layout, hipStream_t s) {
+    const int64_t nb = K / 256;
+    const dim3 grid((unsigned)((nout * nb + 255) / 256));
+    if (layout == 2)
+        hipLaunchKernelGGL(k_gather_q6k<2>, grid, dim3(256), 0, s, src, dst, ids, rows, nout, nb);
+    else if (layout == 1)
+        hipLaunchKernelGGL(k_gather_q6k<1>, grid, dim3(256), 0, s, src, dst, ids, rows, nout, nb);
+    else
+        hipLaunchKernelGGL(k_gather_q6k<0>, grid, dim3(256), 0, s, src, dst, ids, rows, nout, nb);
+    return hipGetLastError();
+}
+
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s) {
     const int64_t nb = K / 256, NB = rows * nb;
     const dim3 grid((unsigned)((NB * 8 + 255) / 256));

@@ -23,4 +23,26 @@ hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32
     return dump ? tiled_cols<true>(w, xq, out, dump, rows, K, ncols, s)
                 : tiled_cols<false>(w, xq, out, dump, rows, K, ncols, s);
 }
+
+// Fused greedy argmax: the product's per-tile column maxima into keys, then
+// one reduction launch.
+hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
+                                       int ncols, int32_t *idx, float *val, hipStream_t s) {
+    float *k = reinterpret_cast<float *>(keys);
+    hipError_t e;
+    switch (ncols) {
+    case 1: e = launch_tiled_n<1, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 2: e = launch_tiled_n<2, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 3: e = launch_tiled_n<3, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 4: e = launch_tiled_n<4, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 5: e = launch_tiled_n<5, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 6: e = launch_tiled_n<6, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 7: e = launch_tiled_n<7, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 8: e = launch_tiled_n<8, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_argmax_reduce, dim3(ncols), dim3(256), 0, s, keys, (rows + 15) / 16, ncols, idx, val);
+    return hipGetLastError();
+}
 }  // namespace qmv

@@ -210,7 +210,20 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane &t
     }
 }
 
-template <int N, int KS, int RTW, int IT, bool DUMP>
+// Greedy-argmax key of an output: the float's bits made order-preserving as
+// an unsigned integer (-0 taken as +0) above the complement of the row, so
+// the largest key is the largest value and, among equal values, the lowest
+// row.
+__device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
+    uint32_t b = __float_as_uint(v + 0.0f);
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)row);
+}
+
+// AMAX: instead of the outputs, each row tile writes, per column n, the
+// largest argmax_key over its rows to keys[tile * N + n] (out is then a
+// uint64 array of ceil(rows/16) * N keys).
+template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false>
 __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
                                                                     float *__restrict__ out) {
     using C = TiledCfg<N, KS, RTW, IT>;
@@ -273,13 +286,51 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
 #pragma unroll
             for (int cg = 0; cg < C::NCG; cg++) {
                 const int no = 4 * cg + (l >> 4);
-                if (rok && no < N) out[(int64_t)no * a.rows + row] = acc[cg];
+                if constexpr (AMAX) {
+                    // largest key over the 16 lanes (rows) of this column
+                    uint64_t key = argmax_key(rok ? acc[cg] : -__builtin_inff(), row);
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1) {
+                        const uint32_t lo = __shfl_xor((uint32_t)key, m), hi = __shfl_xor((uint32_t)(key >> 32), m);
+                        const uint64_t o = ((uint64_t)hi << 32) | lo;
+                        key = o > key ? o : key;
+                    }
+                    if ((l & 15) == 0 && no < N && tile < ntiles)
+                        reinterpret_cast<uint64_t *>(out)[tile * N + no] = key;
+                } else {
+                    if (rok && no < N) out[(int64_t)no * a.rows + row] = acc[cg];
+                }
             }
         }
     }
 }
 
-template <int N, int KS, int RTW, int IT, bool DUMP>
+// Per column n (one workgroup each): the largest of the ntiles keys
+// keys[t * N + n], decoded into the row and its value.
+__global__ __launch_bounds__(256) void k_argmax_reduce(const uint64_t *__restrict__ keys, int64_t ntiles, int N,
+                                                       int32_t *__restrict__ idx, float *__restrict__ val) {
+    __shared__ uint64_t red[256];
+    const int n = blockIdx.x, t = threadIdx.x;
+    uint64_t k = 0;
+    for (int64_t i = t; i < ntiles; i += 256) {
+        const uint64_t o = keys[i * N + n];
+        k = o > k ? o : k;
+    }
+    red[t] = k;
+    __syncthreads();
+    for (int m = 128; m > 0; m >>= 1) {
+        if (t < m) red[t] = red[t + m] > red[t] ? red[t + m] : red[t];
+        __syncthreads();
+    }
+    if (t == 0) {
+        const uint64_t best = red[0];
+        const uint32_t b = (uint32_t)(best >> 32);
+        idx[n] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+        val[n] = __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
+    }
+}
+
+template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false>
 hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                             hipStream_t s) {
     using C = TiledCfg<N, KS, RTW, IT>;
@@ -293,25 +344,25 @@ hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *
     a.its = IT;
     const int64_t tiles = (rows + 15) / 16;
     const int64_t grid = (tiles + RTW - 1) / RTW;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP>), C::LDS);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX>), C::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP>), dim3((unsigned)grid), dim3(C::NTHR), C::LDS, s, w,
-                       a, out);
+    hipLaunchKernelGGL((k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX>), dim3((unsigned)grid), dim3(C::NTHR), C::LDS,
+                       s, w, a, out);
     return hipGetLastError();
 }
 
 // Waves along K per row tile: enough waves of five steps to cover a row in
 // one chunk (at most sixteen), and workgroups of at least four waves.  A
 // function of K only, so every column count sums a row in the same order.
-template <int N, bool DUMP>
+template <int N, bool DUMP, bool AMAX = false>
 hipError_t launch_tiled_n(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                           hipStream_t s) {
     const int64_t need = (K / 128 + 4) / 5;
-    if (need <= 1) return launch_tiled_cfg<N, 1, 4, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    if (need <= 2) return launch_tiled_cfg<N, 2, 2, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
-    return launch_tiled_cfg<N, 16, 1, 5, DUMP>(w, xq, out, dump, rows, K, s);
+    if (need <= 1) return launch_tiled_cfg<N, 1, 4, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
+    if (need <= 2) return launch_tiled_cfg<N, 2, 2, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
+    if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
+    if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
+    return launch_tiled_cfg<N, 16, 1, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
 }
 
 }  // namespace qmv

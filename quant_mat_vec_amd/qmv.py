@@ -48,6 +48,8 @@ def lib() -> ctypes.CDLL:
             "unpack_q6k_planar": [P, P, I64, I64, P],
             "repack_q6k_tiled": [P, P, I64, I64, P],
             "unpack_q6k_tiled": [P, P, I64, I64, P],
+            "gather_q6k_rows": [P, I, I64, I64, P, I64, P, P],
+            "mmvq_q6k_argmax": [P, I, P, I64, I64, I, P, P, P, SZ, P],
             "mmvq_q6k_isums": [P, I, P, P, I64, I64, I, P],
             "mmvq_q4k_isums": [P, P, P, I64, I64, I, P],
             "mmvq_q5k_isums": [P, P, P, I64, I64, I, P],
@@ -59,6 +61,8 @@ def lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = I
         L.grouped_expert_mmvq_workspace.argtypes = [I, I, I, I64, I64]
+        L.mmvq_q6k_argmax_workspace.restype = SZ
+        L.mmvq_q6k_argmax_workspace.argtypes = [I64, I]
         L.grouped_expert_mmvq_workspace.restype = SZ
         L.qmv_strerror.argtypes = [I]
         L.qmv_strerror.restype = ctypes.c_char_p
@@ -138,6 +142,21 @@ def repack_q6k_tiled(src, dst, rows: int, K: int, stream=None) -> None:
 
 def unpack_q6k_tiled(src, dst, rows: int, K: int, stream=None) -> None:
     _check(lib().unpack_q6k_tiled(_ptr(src), _ptr(dst), rows, K, _stream(stream)), "unpack_q6k_tiled")
+
+
+def gather_q6k_rows(src, layout: int, rows: int, K: int, ids, nout: int, dst, stream=None) -> None:
+    _check(lib().gather_q6k_rows(_ptr(src), layout, rows, K, _ptr(ids), nout, _ptr(dst), _stream(stream)),
+           "gather_q6k_rows")
+
+
+def mmvq_q6k_argmax_workspace(rows: int, ncols: int) -> int:
+    return int(lib().mmvq_q6k_argmax_workspace(rows, ncols))
+
+
+def mmvq_q6k_argmax(w, layout: int, xq, rows: int, K: int, ncols: int, idx, val, ws, ws_bytes: int,
+                    stream=None) -> None:
+    _check(lib().mmvq_q6k_argmax(_ptr(w), layout, _ptr(xq), rows, K, ncols, _ptr(idx), _ptr(val), _ptr(ws),
+                                 ws_bytes, _stream(stream)), "mmvq_q6k_argmax")
 
 
 def mmvq_q6k_isums(w, layout: int, xq, isums, rows: int, K: int, ncols: int, stream=None) -> None:

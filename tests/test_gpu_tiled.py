@@ -194,3 +194,72 @@ def test_tiled_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert np.array_equal(host(out).view(np.uint32), eager.view(np.uint32)), f"replay {i}"
         _ = (x * 2).sum().item()               # eager work between replays
+
+
+# ------------------------------------------------------------- row gather
+@pytest.mark.parametrize("layout", [GG, PL, TL])
+def test_gather_rows_bytes_and_products(layout):
+    """A draft-head-like row subset (repeats, an out-of-range id, a partial
+    last tile) gathered on the GPU in each layout: bytes equal the oracle's,
+    and the product on the gathered matrix matches the oracle on the
+    gathered GGUF rows."""
+    rows, K, ncols = 5000, 2560, 4
+    note(f"gather_q6k_rows layout={layout} {rows}x{K}")
+    g = synth.rng(960 + layout)
+    w = synth.q6k_blocks(g, rows, K)
+    ids = g.choice(rows, size=1000, replace=True).astype(np.int32)
+    ids[[7, 500]] = [-3, rows]
+    wd = dev(w)
+    src = wd if layout == GG else (planar(wd, rows, K) if layout == PL else tiled(wd, rows, K))
+    nout = ids.size
+    dst = torch.empty(nout * (K // 256) * 210, dtype=torch.uint8, device=DEV)
+    qmv.gather_q6k_rows(src, layout, rows, K, dev(ids), nout, dst)
+    assert np.array_equal(host(dst), orc.q6k_gather(w, layout, rows, K, ids))
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    got = mmvq("q6k", dst, xq, nout, K, ncols, layout)
+    wg = orc.q6k_gather(w, GG, rows, K, ids)
+    ref, ab = orc.mmvq("q6k", wg, xq_np, nout, K)
+    ok = (ids >= 0) & (ids < rows)
+    assert_close(got[:, ok], ref[:, ok], ab[:, ok], f"gathered layout={layout}")
+    assert not np.any(got[:, ~ok])       # all-zero rows (d = 0) give exact zeros
+
+
+# ---------------------------------------------------------- greedy argmax
+@pytest.mark.parametrize("rows,K,ncols", [(151936, 2560, 4), (151936, 2560, 1), (10240, 2560, 8),
+                                          (5003, 768, 5), (32805, 256, 3), (2560, 10240, 2), (7, 512, 2)])
+def test_argmax_matches_own_outputs_and_oracle(rows, K, ncols):
+    """idx/val equal numpy's first-occurrence argmax of the same kernel's fp32
+    outputs (bits of the value included); the chosen row is a maximum of the
+    oracle's outputs within the fp32 tolerance; a copy of the winning row
+    planted at a lower index then wins the tie."""
+    note(f"mmvq_q6k_argmax {rows}x{K} N={ncols}")
+    g = synth.rng(synth.seed_for(6, rows % 101, ncols))
+    w = synth.q6k_blocks(g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    wb = w.reshape(rows, -1)
+
+    def run(wmat):
+        wt = tiled(dev(wmat.reshape(-1)), rows, K)
+        out = mmvq("q6k", wt, xq, rows, K, ncols, TL)
+        nws = qmv.mmvq_q6k_argmax_workspace(rows, ncols)
+        ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+        idx = torch.empty(ncols, dtype=torch.int32, device=DEV)
+        val = torch.empty(ncols, dtype=torch.float32, device=DEV)
+        qmv.mmvq_q6k_argmax(wt, TL, xq, rows, K, ncols, idx, val, ws, nws)
+        return out, host(idx), host(val)
+
+    out, idx, val = run(wb)
+    assert np.array_equal(idx, np.argmax(out, axis=1))
+    assert np.array_equal(val.view(np.uint32), out[np.arange(ncols), idx].view(np.uint32))
+    rs = sorted(set(sampled(rows, g, 20)) | set(idx.tolist()))
+    ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np, len(rs), K)
+    best = ref.max(axis=1)
+    chosen = ref[np.arange(ncols), [rs.index(i) for i in idx]]
+    assert np.all(chosen >= best - 2e-5 * ab.max(axis=1))
+    if rows > 1 and idx[0] > 0:
+        w2 = wb.copy()
+        lo = int(idx[0]) // 2
+        w2[lo] = wb[idx[0]]
+        out2, idx2, val2 = run(w2)
+        assert idx2[0] == lo and np.array_equal(val2[:1].view(np.uint32), val[:1].view(np.uint32))
+        assert np.array_equal(idx2, np.argmax(out2, axis=1))

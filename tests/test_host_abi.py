@@ -24,7 +24,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = qmv.declared_symbols()
     expected = {"quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
-                "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "mmvq_q6k_isums",
+                "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "gather_q6k_rows", "mmvq_q6k_argmax", "mmvq_q6k_argmax_workspace",
+                "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
                 "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "qmv_strerror",
                 "qmv_last_hip_error", "qmv_stream_read"}
@@ -100,6 +101,45 @@ def test_repack_rejects(L):
         if a_src > 1:
             assert fn(P + a_src // 2, P + 4096, 4, 256, None) == E_ALN
         assert fn(P, P + 4096 + a_dst // 2, 4, 256, None) == E_ALN
+
+
+def test_gather_rejects(L):
+    f = L.gather_q6k_rows
+    assert f(None, 1, 4, 256, P, 2, P + 8192, None) == E_INV
+    assert f(P, 1, 4, 256, None, 2, P + 8192, None) == E_INV
+    assert f(P, 1, 4, 256, P, 2, None, None) == E_INV
+    assert f(P, 1, 0, 256, P, 2, P + 8192, None) == E_INV
+    assert f(P, 1, 4, 256, P, 0, P + 8192, None) == E_INV
+    assert f(P, 3, 4, 256, P, 2, P + 8192, None) == E_UNS
+    assert f(P, 1, 4, 300, P, 2, P + 8192, None) == E_UNS
+    assert f(P + 8, 1, 4, 256, P, 2, P + 8192, None) == E_ALN
+    assert f(P, 2, 4, 256, P, 2, P + 8200, None) == E_ALN
+    assert f(P, 1, 4, 256, P + 2, 2, P + 8192, None) == E_ALN
+    assert f(P, 1, 4, 256, P, 2, P + 416, None) == E_INV      # overlapping buffers
+
+
+def test_argmax_rejects(L):
+    f = L.mmvq_q6k_argmax
+    TL = qmv.LAYOUT_TILED
+    nws = L.mmvq_q6k_argmax_workspace(100, 4)
+    assert nws == (7 * 4 * 8 + 255) // 256 * 256
+    assert L.mmvq_q6k_argmax_workspace(0, 4) == 0 and L.mmvq_q6k_argmax_workspace(100, 9) == 0
+
+    def call(w=P, lay=TL, xq=P, rows=100, K=512, n=4, idx=P, val=P, ws=P, wsb=nws):
+        return f(w, lay, xq, rows, K, n, idx, val, ws, wsb, None)
+
+    assert call(idx=None) == E_INV
+    assert call(val=None) == E_INV
+    assert call(ws=None) == E_INV
+    assert call(w=None) == E_INV
+    assert call(lay=qmv.LAYOUT_PLANAR) == E_UNS
+    assert call(lay=qmv.LAYOUT_GGUF) == E_UNS
+    assert call(K=300) == E_UNS
+    assert call(n=9) == E_UNS
+    assert call(w=P + 8) == E_ALN
+    assert call(val=P + 2) == E_ALN
+    assert call(ws=P + 4) == E_ALN
+    assert call(wsb=nws - 1) == E_WS
 
 
 def test_moe_rejects_and_workspace(L):

@@ -449,6 +449,41 @@ def test_tiled_layout_pins():
             assert off == hi - lo
 
 
+def test_gather_pins():
+    """Row gather: on GGUF it is numpy block indexing (zero rows for bad
+    ids); gathering every row in order is the conversion itself; on the
+    planar layout each plane of the output is the numpy row selection of the
+    full conversion's plane; the tiled output is the per-tile transpose of
+    the planar one (the pinned relation between the two layouts)."""
+    rows, K = 37, 768
+    nb, nsb = K // 256, K // 32
+    w = synth.q6k_blocks(synth.rng(73), rows, K)
+    ids = np.array([3, 36, 0, 3, -1, 40, 20, 16, 17, 5, 6, 7, 8, 9, 10, 11, 12, 30], np.int32)
+    nout = ids.size
+    ok = (ids >= 0) & (ids < rows)
+    rb = nb * 210
+    exp = np.concatenate([w[i * rb:(i + 1) * rb] if 0 <= i < rows else np.zeros(rb, np.uint8) for i in ids])
+    assert np.array_equal(orc.q6k_gather(w, 0, rows, K, ids), exp)
+    every = np.arange(rows, dtype=np.int32)
+    assert np.array_equal(orc.q6k_gather(w, 1, rows, K, every), orc.q6k_to_planar(w, rows, K))
+    assert np.array_equal(orc.q6k_gather(w, 2, rows, K, every), orc.q6k_to_tiled(w, rows, K))
+    full = orc.q6k_to_planar(w, rows, K)
+    gp = orc.q6k_gather(w, 1, rows, K, ids)
+    gt = orc.q6k_gather(w, 2, rows, K, ids)
+    NBs, NBd = rows * nb, nout * nb
+    for (lo, hi, esz, npos) in [(0, 128, 16, nsb), (128, 192, 8, nsb), (192, 208, 8, nsb // 4), (208, 210, 2, nb)]:
+        fs = full[lo * NBs:hi * NBs].reshape(rows, npos, esz)
+        pd = gp[lo * NBd:hi * NBd].reshape(nout, npos, esz)
+        assert np.array_equal(pd[ok], fs[ids[ok]])
+        assert not pd[~ok].any()
+        td = gt[lo * NBd:hi * NBd]
+        off = 0
+        for r0 in range(0, nout, 16):
+            part = pd[r0:r0 + 16].transpose(1, 0, 2).reshape(-1)
+            assert np.array_equal(td[off:off + part.size], part)
+            off += part.size
+
+
 # ----------------------------------------------------------------- MoE
 def test_moe_chain_vs_fp64_bruteforce():
     g = synth.rng(81)
