@@ -360,11 +360,58 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
     ex["q6k_lm_head_151936x2560"] = shape_case("q6k", 151936, 2560, (1, 4), seed=14)
     ex["q6k_lm_head_151936x2560_planar_dot4"] = shape_case("q6k", 151936, 2560, (1, 4), layout=PL, seed=14)
     ex["q6k_lm_head_151936x2560_gguf"] = shape_case("q6k", 151936, 2560, (1, 4), layout=GG, seed=14)
+    ex["q6k_lm_head_argmax_and_draft_gather"] = lm_head_case(torch, np, qmv, synth, dev)
     for kind in ("q4k", "q5k"):
         for (r_, k_) in ((12288, 2560), (6144, 2560), (2560, 6144), (512, 2560)):
             ex[f"{kind}_{r_}x{k_}"] = shape_case(kind, r_, k_, (1, 4), seed=15 + r_)
     ex["moe_e128_2560_768"] = moe_case(torch, np, qmv, synth, dev)
     return ex
+
+
+def lm_head_case(torch, np, qmv, synth, dev):
+    """LM head 151936x2560 (tiled): the fused greedy argmax (product with
+    per-tile maxima + one reduction launch) beside the product alone, per
+    call; and the load-time gather of a 32768-row draft head plus the
+    product on it."""
+    TL = qmv.LAYOUT_TILED
+    rows, k = 151936, 2560
+    g = synth.rng(synth.seed_for(2, 1, 4))
+    w = torch.from_numpy(synth.q6k_blocks(g, rows, k)).to(dev)
+    t0 = torch.empty_like(w)
+    qmv.repack_q6k_tiled(w, t0, rows, k)
+    del w
+    cs = [t0, t0.clone()]                      # 638 MB: more than twice the Infinity Cache
+    x = torch.from_numpy(synth.activations(g, 4, k)).to(dev)
+    q = torch.empty(4 * (k // 32) * 36, dtype=torch.uint8, device=dev)
+    o = torch.empty(4 * rows, dtype=torch.float32, device=dev)
+    idx = torch.empty(4, dtype=torch.int32, device=dev)
+    val = torch.empty(4, dtype=torch.float32, device=dev)
+    res = {}
+    for n in (1, 4):
+        qmv.quantize_q8_1(x, q, k, n)
+        nws = qmv.mmvq_q6k_argmax_workspace(rows, n)
+        ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+        fused = graph_avg_us(torch, [lambda c=c, n=n: qmv.mmvq_q6k_argmax(c, TL, q, rows, k, n, idx, val, ws, nws)
+                                     for c in cs] * 10, reps=4)
+        product = graph_avg_us(torch, [lambda c=c, n=n: qmv.mmvq_q6k(c, TL, q, o, rows, k, n) for c in cs] * 10,
+                               reps=4)
+        res[f"argmax_N{n}"] = {"fused_argmax_us": round(fused, 3), "product_alone_us": round(product, 3)}
+    ids = torch.from_numpy(np.sort(synth.rng(77).choice(rows, size=32768, replace=False)).astype(np.int32)).to(dev)
+    dh = torch.empty(32768 * (k // 256) * 210, dtype=torch.uint8, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    qmv.gather_q6k_rows(t0, TL, rows, k, ids, 32768, dh)
+    b.record()
+    torch.cuda.synchronize()
+    res["draft_head_gather_32768_rows_us_load_time"] = round(a.elapsed_time(b) * 1e3, 1)
+    dcs = [dh] + [dh.clone() for _ in range(8)]   # 619 MB
+    qmv.quantize_q8_1(x, q, k, 4)
+    us = graph_avg_us(torch, [lambda c=c: qmv.mmvq_q6k(c, TL, q, o, 32768, k, 4) for c in dcs] * 4, reps=4)
+    res["draft_head_32768x2560_N4_us"] = round(us, 3)
+    res["draft_head_weight_GBps"] = round(32768 * 10 * 210 / (us * 1e-6) / 1e9, 1)
+    del cs, dcs
+    torch.cuda.empty_cache()
+    return res
 
 
 def moe_case(torch, np, qmv, synth, dev):

@@ -174,7 +174,7 @@ int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const 
  * Tiled layout only (QMV_LAYOUT_TILED; others: QMV_ERR_UNSUPPORTED).
  * idx int32 [ncols], val fp32 [ncols] (4-byte aligned); ws: device
  * workspace of at least mmvq_q6k_argmax_workspace(rows, ncols) bytes,
- * 8-byte aligned, overwritten (one 8-byte key per 16-row tile and column).
+ * 8-byte aligned, overwritten (one 8-byte key per column and 16-row tile).
  * Other arguments and checks as for mmvq_q6k.  Two launches: the product
  * with per-tile maxima, then one reduction per column.  Outputs must be
  * finite. */

@@ -42,7 +42,7 @@ hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *
     default: return hipErrorInvalidValue;
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_argmax_reduce, dim3(ncols), dim3(256), 0, s, keys, (rows + 15) / 16, ncols, idx, val);
+    hipLaunchKernelGGL(k_argmax_reduce, dim3(ncols), dim3(kArgmaxThreads), 0, s, keys, (rows + 15) / 16, idx, val);
     return hipGetLastError();
 }
 }  // namespace qmv

@@ -221,8 +221,8 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
 }
 
 // AMAX: instead of the outputs, each row tile writes, per column n, the
-// largest argmax_key over its rows to keys[tile * N + n] (out is then a
-// uint64 array of ceil(rows/16) * N keys).
+// largest argmax_key over its rows to keys[n * ntiles + tile] (out is then
+// a uint64 array of N * ceil(rows/16) keys).
 template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false>
 __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
                                                                     float *__restrict__ out) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
                         key = o > key ? o : key;
                     }
                     if ((l & 15) == 0 && no < N && tile < ntiles)
-                        reinterpret_cast<uint64_t *>(out)[tile * N + no] = key;
+                        reinterpret_cast<uint64_t *>(out)[no * ntiles + tile] = key;
                 } else {
                     if (rok && no < N) out[(int64_t)no * a.rows + row] = acc[cg];
                 }
@@ -306,24 +306,37 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
 }
 
 // Per column n (one workgroup each): the largest of the ntiles keys
-// keys[t * N + n], decoded into the row and its value.
-__global__ __launch_bounds__(256) void k_argmax_reduce(const uint64_t *__restrict__ keys, int64_t ntiles, int N,
-                                                       int32_t *__restrict__ idx, float *__restrict__ val) {
-    __shared__ uint64_t red[256];
+// keys[n * ntiles + i], decoded into the row and its value.  Each thread
+// issues all its loads at once (kArgmaxLoads per round), then the maximum
+// is taken within each wave and over the waves.
+constexpr int kArgmaxThreads = 1024, kArgmaxLoads = 16;
+__global__ __launch_bounds__(kArgmaxThreads) void k_argmax_reduce(const uint64_t *__restrict__ keys, int64_t ntiles,
+                                                                  int32_t *__restrict__ idx, float *__restrict__ val) {
+    __shared__ uint64_t red[kArgmaxThreads / kWave];
     const int n = blockIdx.x, t = threadIdx.x;
+    const uint64_t *kc = keys + (int64_t)n * ntiles;
     uint64_t k = 0;
-    for (int64_t i = t; i < ntiles; i += 256) {
-        const uint64_t o = keys[i * N + n];
+    for (int64_t base = 0; base < ntiles; base += (int64_t)kArgmaxThreads * kArgmaxLoads) {
+        uint64_t v[kArgmaxLoads];
+#pragma unroll
+        for (int u = 0; u < kArgmaxLoads; u++) {
+            const int64_t i = base + (int64_t)u * kArgmaxThreads + t;
+            v[u] = i < ntiles ? kc[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kArgmaxLoads; u++) k = v[u] > k ? v[u] : k;
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)k, m), hi = __shfl_xor((uint32_t)(k >> 32), m);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
         k = o > k ? o : k;
     }
-    red[t] = k;
+    if ((t & (kWave - 1)) == 0) red[t / kWave] = k;
     __syncthreads();
-    for (int m = 128; m > 0; m >>= 1) {
-        if (t < m) red[t] = red[t + m] > red[t] ? red[t + m] : red[t];
-        __syncthreads();
-    }
     if (t == 0) {
-        const uint64_t best = red[0];
+        uint64_t best = red[0];
+        for (int i = 1; i < kArgmaxThreads / kWave; i++) best = red[i] > best ? red[i] : best;
         const uint32_t b = (uint32_t)(best >> 32);
         idx[n] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
         val[n] = __uint_as_float((b & 0x80000000u) ? (b & 0x7FFFFFFFu) : ~b);
