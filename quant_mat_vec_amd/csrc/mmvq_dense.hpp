@@ -11,15 +11,12 @@ namespace qmv {
 #ifndef QMV_DENSE_WAVES
 #define QMV_DENSE_WAVES 4
 #endif
-#ifndef QMV_DENSE_P2_FROM
-#define QMV_DENSE_P2_FROM 9
-#endif
 constexpr int kDenseWaves = QMV_DENSE_WAVES;
 
-// Rows per lane: two from QMV_DENSE_P2_FROM columns on, where the activation
-// reads from LDS become the limit (it changes no row's summation order).
+// Rows per lane group: one.  (The core takes P rows per lane; two rows, which
+// halve the activation reads from LDS, measured no faster at 1-8 columns.)
 template <int N>
-constexpr int kDenseP = N >= QMV_DENSE_P2_FROM ? 2 : 1;
+constexpr int kDenseP = 1;
 
 // W waves per workgroup; the kernel is compiled for up to kMaxDenseWaves.
 constexpr int kMaxDenseWaves = 10;
