@@ -80,6 +80,15 @@ struct TiledCfg {
     static constexpr int CZ = KS * IT;                 // steps per chunk
     static constexpr int TNB = 4 * CZ;                 // tile blocks per column
     static constexpr int SI = (N * TNB + NTHR - 1) / NTHR;
+    // Wave tiles: with one row tile per workgroup the KS waves read disjoint
+    // steps, so each wave can stage only its own 4*IT blocks per column and
+    // skip the workgroup barrier (a wave's LDS accesses execute in order).
+    // Measured (graph replays, rotated weights): 0.1-0.3 us faster with 16
+    // waves along K (2560x10240), 0.1-0.2 us slower with four (10240x2560
+    // at N = 4, 8), so only from eight waves on.
+    static constexpr bool WT = RTW == 1 && KS >= 8;
+    static constexpr int WB = 4 * IT;                  // blocks per column of one wave
+    static constexpr int SL = WT ? (N * WB + kWave - 1) / kWave : SI;   // load slots per lane
     // zero entries after each quant array: a masked lane reads entry
     // N*TNB + 4*it at step it, so its LDS offset follows the step like the
     // others' and the step's part of every address is an immediate
@@ -120,13 +129,30 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
     const int nblk = FULL ? TNB : min(TNB, (int)(nsb - 4 * (int64_t)zc0));
 
     // activation loads first (loads retire in order: the tile can be stored
-    // while the weight loads behind it are still in flight)
-    ActRaw ar[C::SI];
+    // while the weight loads behind it are still in flight).  Slot s of the
+    // lane is block b of column n; own_slot gives both and whether the slot
+    // exists.
+    auto own_slot = [&](int s, int &n, int &b) -> bool {
+        int i, lim;
+        if constexpr (C::WT) {
+            i = l + s * kWave;
+            lim = N * C::WB;
+            n = min(i, lim - 1) / C::WB;
+            b = 4 * ks * IT + (min(i, lim - 1) - n * C::WB);
+        } else {
+            i = tid + s * NTHR;
+            lim = N * TNB;
+            n = min(i, lim - 1) / TNB;
+            b = min(i, lim - 1) - n * TNB;
+        }
+        return i < lim && (FULL || b < nblk);
+    };
+    ActRaw ar[C::SL];
 #pragma unroll
-    for (int s = 0; s < C::SI; s++) {
-        const int i = min(tid + s * NTHR, N * TNB - 1), n = i / TNB;
-        const int b = FULL ? i - n * TNB : min(i - n * TNB, nblk - 1);
-        act_load(ar[s], a.xq, xcol_of<N>(a, n) + 4 * (int64_t)zc0 + b);
+    for (int s = 0; s < C::SL; s++) {
+        int n, b;
+        own_slot(s, n, b);
+        act_load(ar[s], a.xq, xcol_of<N>(a, n) + 4 * (int64_t)zc0 + (FULL ? b : min(b, nblk - 1)));
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -164,20 +190,30 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
     uint4 *x0 = reinterpret_cast<uint4 *>(lds);
     uint4 *x1 = x0 + C::XE;
     float *fd = reinterpret_cast<float *>(x1 + C::XE);
-    if (tid < C::ZW) {
-        x0[N * TNB + tid] = make_uint4(0, 0, 0, 0);
-        x1[N * TNB + tid] = make_uint4(0, 0, 0, 0);
+    // (with wave tiles every wave writes the zero entries itself: the same
+    // values, and then its own reads follow its own writes)
+    if ((C::WT ? l : tid) < C::ZW) {
+        const int z = C::WT ? l : tid;
+        x0[N * TNB + z] = make_uint4(0, 0, 0, 0);
+        x1[N * TNB + z] = make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int s = 0; s < C::SI; s++) {
-        const int i = tid + s * NTHR, n = i / TNB, b = i - n * TNB;
-        if (i < N * TNB && (FULL || b < nblk)) {
+    for (int s = 0; s < C::SL; s++) {
+        int n, b;
+        if (own_slot(s, n, b)) {
+            const int i = n * TNB + b;
             x0[i] = make_uint4(ar[s].w[1], ar[s].w[2], ar[s].w[3], ar[s].w[4]);
             x1[i] = make_uint4(ar[s].w[5], ar[s].w[6], ar[s].w[7], ar[s].w[8]);
             fd[i] = half_to_float(ar[s].w[0]) * 0.25f;    // the codes are 4 * (q6 - 32)
         }
     }
-    lds_barrier();
+    if constexpr (C::WT) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        lds_barrier();
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_ab(std::integral_constant<int, C::PRE>{}, std::integral_constant<int, IT>{});
 
@@ -293,11 +329,11 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
     for (int cg = 0; cg < C::NCG; cg++) acc[cg] = 0.0f;
     const int nfull = ZS / C::CZ;
     for (int c = 0; c < nfull; c++) {
-        if (c > 0) lds_barrier();
+        if (!C::WT && c > 0) lds_barrier();
         tiled_chunk<true, N, KS, RTW, IT, DUMP>(f, tl, a, lds, c * C::CZ, ZS, row, rok, acc);
     }
     if (nfull * C::CZ < ZS) {
-        if (nfull > 0) lds_barrier();
+        if (!C::WT && nfull > 0) lds_barrier();
         tiled_chunk<false, N, KS, RTW, IT, DUMP>(f, tl, a, lds, nfull * C::CZ, ZS, row, rok, acc);
     }
     if constexpr (!DUMP) {

@@ -51,7 +51,7 @@ def test_tiled_repack_bytes_and_roundtrip(rows, K):
 
 # ------------------------------------------------------- small, all rows
 SMALL = [(1, 256, 1), (37, 768, 3), (19, 2560, 8), (9, 10240, 2), (70, 512, 5), (5, 1280, 8),
-         (40, 3584, 5), (130, 2560, 4), (17, 20480, 6)]
+         (40, 3584, 5), (130, 2560, 4), (17, 20480, 6), (21, 12800, 7)]
 
 
 @pytest.mark.parametrize("rows,K,ncols", SMALL)
