@@ -3,9 +3,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 
-Workload (one "step"): quantize 13 fp32 activation columns to Q8_1 in one
-launch, then run the Q6_K MMVQ of a 10240 x 2560 (rows x cols) matrix in the
-tiled layout (int8 matrix-core kernel) at N = 1, 4 and 8 columns (each product on its own columns: 1 + 4 + 8 = 13)
+Workload (one "step"): quantize 13 fp32 activation columns to Q8_1 (the
+column-planar arrangement of its bytes) in one launch, then run the Q6_K
+MMVQ of a 10240 x 2560 (rows x cols) matrix in the tiled layout (int8
+matrix-core kernel) at N = 1, 4 and 8 columns (each product on its own
+columns: 1 + 4 + 8 = 13)
 -- the decode matrix the pages measure as "2560 x 10240" (n_in x n_out).  Weights are resident in HBM before timing and
 each launch reads a different one of 26 copies (559 MB, more than twice the
 256 MB Infinity Cache), so every weight byte comes from HBM.
@@ -36,7 +38,7 @@ ROWS, K = 10240, 2560
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on a
 # plain copy of known size (FETCH_SIZE x 1.9977, WRITE_SIZE x 1.0); to be
 # emptied whenever the kernel changes after the counters were taken.
-TRAFFIC = {1: 21655457, 4: 21866921, 8: 22141293}
+TRAFFIC = {1: 21664307, 4: 21866923, 8: 22140204}
 NCOLS = (1, 4, 8)
 XCOLS = sum(NCOLS)          # distinct activation columns quantized per step
 COL0 = {1: 0, 4: 1, 8: 5}   # first activation column of each product
@@ -123,7 +125,8 @@ def main():
     # all work on one non-default stream (graph capture needs one; default
     # priority, like every stream here)
     torch.cuda.set_stream(torch.cuda.Stream())
-    TL = qmv.LAYOUT_TILED
+    # tiled weights (matrix cores), column-planar Q8_1 activations
+    XT = qmv.LAYOUT_TILED | qmv.ACT_PLANAR
     g = synth.rng(synth.seed_for(1, 1, 8))
     w_np = synth.q6k_blocks(g, ROWS, K)
     x_np = synth.activations(g, XCOLS, K)
@@ -139,7 +142,7 @@ def main():
 
     def xq_of(n):
         return xq_all[COL0[n] * qcol:(COL0[n] + n) * qcol]
-    qmv.quantize_q8_1(xd, xq_all, K, XCOLS)
+    qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
     xq = xq_all[:8 * qcol]
     out = torch.empty(8 * ROWS, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
@@ -150,10 +153,10 @@ def main():
         # fixed workload for hardware-counter passes: the three products on
         # rotated copies, then a plain copy of the same size (its FETCH_SIZE /
         # WRITE_SIZE calibrate the counters against known bytes)
-        qmv.quantize_q8_1(xd, xq_all, K, XCOLS)
+        qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
         for n in NCOLS:
             for i in range(30):
-                qmv.mmvq_q6k(copies[i % ncopies], TL, xq_of(n), out, ROWS, K, n)
+                qmv.mmvq_q6k(copies[i % ncopies], XT, xq_of(n), out, ROWS, K, n)
         dst = torch.empty_like(base)
         for i in range(30):
             dst.copy_(copies[i % ncopies])
@@ -161,10 +164,10 @@ def main():
         return
 
     def step(i):
-        qmv.quantize_q8_1(xd, xq_all, K, XCOLS)
+        qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
         for j, n in enumerate(NCOLS):
             c = copies[(len(NCOLS) * i + j) % ncopies]
-            qmv.mmvq_q6k(c, TL, xq_of(n), out, ROWS, K, n)
+            qmv.mmvq_q6k(c, XT, xq_of(n), out, ROWS, K, n)
 
     # Step i uses weight copies at rotation offset i % ncopies.  HIP graphs:
     # one holding `ncopies` consecutive steps (offsets 0 .. ncopies-1, so the
@@ -218,12 +221,12 @@ def main():
     # per-launch time (kernel plus the dispatch gap between kernels) remains.
     per_n = {}
     reps, per_graph = 8, ncopies * 2
-    qmv.quantize_q8_1(xd, xq_all, K, XCOLS)
+    qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
     for n in NCOLS:
         gph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(gph, stream=stream):
             for i in range(per_graph):
-                qmv.mmvq_q6k(copies[i % ncopies], TL, xq_of(n), out, ROWS, K, n)
+                qmv.mmvq_q6k(copies[i % ncopies], XT, xq_of(n), out, ROWS, K, n)
         gph.replay()
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -233,7 +236,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         mean = a.elapsed_time(b) * 1e3 / (reps * per_graph)
-        per_n[n] = {"kernel": f"qmv::k_mmvq_q6_tiled<{n}, 4, 1, 5, false, false>",
+        per_n[n] = {"kernel": f"qmv::k_mmvq_q6_tiled<{n}, 4, 1, 5, false, false, true>",
                     "avg_launch_us": round(mean, 3),
                     "weight_GBps": round(wb / (mean * 1e-6) / 1e9, 1),
                     "weight_frac_of_8TBps": round(wb / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
@@ -250,7 +253,7 @@ def main():
     # eager launches with per-launch events (host launch path included)
     eager = {}
     for n in NCOLS:
-        r = timed_launches(torch, lambda c, n=n: qmv.mmvq_q6k(c, TL, xq_of(n), out, ROWS, K, n), 100, copies)
+        r = timed_launches(torch, lambda c, n=n: qmv.mmvq_q6k(c, XT, xq_of(n), out, ROWS, K, n), 100, copies)
         eager[str(n)] = round(r["mean_us"], 3)
 
     # checksum of the last step's N=8 output bits (FNV-1a 32)
@@ -285,7 +288,7 @@ def main():
         "scaling": "weak", "vs_baseline": round(value / pages_gbs, 2), "dtype": "int8",
         "data": "synthetic",
         "config": {"workload": "Q6_K MMVQ 10240x2560 (rows x cols), tiled weights (matrix cores), 1/4/8 columns, "
-                               "one Q8_1 quantize of the 13 activation columns + the three MMVQs, "
+                               "one Q8_1 quantize (column-planar layout) of the 13 activation columns + the three MMVQs, "
                                f"weights rotated over {ncopies} HBM copies",
                    "rows": ROWS, "cols": K, "ncols": list(NCOLS),
                    "vs_baseline_basis": f"pages' A770 large-GRF figures for this matrix "

@@ -77,6 +77,15 @@
  * (a different summation order), and its per-sub-block integer sums are
  * identical.
  *
+ * Column-planar Q8_1 activations (QMV_ACT_PLANAR), produced by
+ * quantize_q8_1_planar: the bytes of each column's K/32 Q8_1 blocks,
+ * rearranged inside the column (column n still starts at byte 36*(K/32)*n):
+ * the K int8 quants (block b's 32 at byte 32*b of the column), then the K/32
+ * fp16 d (block b's at byte K + 2*b), then the K/32 fp16 s (at byte
+ * K + 2*(K/32) + 2*b).  The tiled product reads it with aligned 16-byte
+ * loads and stores it to LDS unchanged; its outputs are bit-identical to
+ * those from the same values in Q8_1 blocks.
+ *
  * Conventions for every entry point.
  *   Memory: all data pointers are device pointers owned by the caller; the
  *   library never allocates, frees or synchronizes.  `stream` is a
@@ -111,6 +120,10 @@ enum {
 
 enum { QMV_LAYOUT_GGUF = 0, QMV_LAYOUT_PLANAR = 1, QMV_LAYOUT_TILED = 2 };
 
+/* OR-ed into the layout argument together with QMV_LAYOUT_TILED: the
+ * activations are column-planar (see above) instead of Q8_1 blocks. */
+enum { QMV_ACT_PLANAR = 16 };
+
 /* Largest supported sizes: rows <= 2^31-1, K <= 2^20, and every weight,
  * activation and output buffer below 2^40 bytes. */
 
@@ -123,6 +136,10 @@ enum { QMV_LAYOUT_GGUF = 0, QMV_LAYOUT_PLANAR = 1, QMV_LAYOUT_TILED = 2 };
  * 4-byte aligned.  K % 32 == 0, 1 <= ncols <= 65535. */
 int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream);
 
+/* As quantize_q8_1 (same arithmetic, same bytes), written in the
+ * column-planar layout.  xq: 4-byte aligned (16-byte for the products). */
+int quantize_q8_1_planar(const float *x, void *xq, int64_t K, int ncols, void *stream);
+
 /* Q6_K weights x Q8_1 activations (the Q6_K dense decode product of PR
  * #2340 "What it changes" and PR #2207 "How it was checked").
  * w: rows x K Q6_K matrix in `layout` (QMV_LAYOUT_GGUF: 210-byte blocks,
@@ -130,7 +147,9 @@ int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream);
  * 16-byte aligned).  xq: Q8_1 [ncols][K/32], 4-byte aligned.  out: fp32
  * [ncols][rows], 4-byte aligned.  K % 256 == 0, 1 <= ncols <= 8.
  * GGUF and planar inputs run on the vector ALU (dot4); tiled inputs on the
- * int8 matrix cores. */
+ * int8 matrix cores.  layout = QMV_LAYOUT_TILED | QMV_ACT_PLANAR takes
+ * column-planar activations (xq 16-byte aligned); any other layout with
+ * QMV_ACT_PLANAR is QMV_ERR_UNSUPPORTED. */
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out,
              int64_t rows, int64_t K, int ncols, void *stream);
 
@@ -171,7 +190,8 @@ int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const 
  * column n, idx[n] = the row r with the largest out[n][r] of mmvq_q6k and
  * val[n] = that value, bit for bit the fp32 output mmvq_q6k gives for the
  * same inputs; among equal values the lowest row wins, -0 counts as +0.
- * Tiled layout only (QMV_LAYOUT_TILED; others: QMV_ERR_UNSUPPORTED).
+ * Tiled layout only (QMV_LAYOUT_TILED, optionally | QMV_ACT_PLANAR;
+ * others: QMV_ERR_UNSUPPORTED).
  * idx int32 [ncols], val fp32 [ncols] (4-byte aligned); ws: device
  * workspace of at least mmvq_q6k_argmax_workspace(rows, ncols) bytes,
  * 8-byte aligned, overwritten (one 8-byte key per column and 16-row tile).

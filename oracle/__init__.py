@@ -57,6 +57,7 @@ def lib():
             getattr(L, name).argtypes = [P, P, I64, I64]
         L.orc_q6k_gather.argtypes = [P, I, I64, I64, P, I64, P]
         L.orc_quantize_q8_1.argtypes = [P, P, I64, I]
+        L.orc_q8_1_to_planar.argtypes = [P, P, I64, I]
         L.orc_dequant_q8_1.argtypes = [P, P, I64, I]
         for name in ("orc_q6k_isums", "orc_q4k_dots", "orc_q5k_dots"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I]
@@ -137,6 +138,15 @@ def quantize_q8_1(x):
     xq = np.zeros((ncols, K // 32 * Q81_BYTES), np.uint8)
     lib().orc_quantize_q8_1(_p(x), _p(xq), K, ncols)
     return xq
+
+
+def q8_1_to_planar(xq, K: int):
+    """Q8_1 blocks [ncols][K/32] -> the column-planar layout (same bytes)."""
+    xq = _u8(xq)
+    ncols = xq.size // (K // 32 * Q81_BYTES)
+    dst = np.zeros(xq.size, np.uint8)
+    lib().orc_q8_1_to_planar(_p(xq), _p(dst), K, ncols)
+    return dst
 
 
 def dequant_q8_1(xq, K: int):

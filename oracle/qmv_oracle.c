@@ -510,6 +510,27 @@ void orc_q6k_to_tiled(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K)
     free(pl);
 }
 
+/* ------------------------------------------- column-planar Q8_1
+ * The Q8_1 blocks of each activation column rearranged inside the column
+ * (the int4 activation loads of P2340 "What it changes", laid out so that a
+ * column's quants are one aligned run).  Restated from the GPU library's
+ * published layout text (its C header): with nb = K/32 and column n at byte
+ * 36*nb*n in both forms, block b's quants go to byte 32*b of the column,
+ * its fp16 d to byte K + 2*b and its fp16 s to byte K + 2*nb + 2*b. */
+void orc_q8_1_to_planar(const uint8_t *src, uint8_t *dst, int64_t K, int ncols) {
+    const int64_t nb = K / QB;
+    for (int64_t n = 0; n < ncols; n++) {
+        const uint8_t *cs = src + n * nb * Q81_BYTES;
+        uint8_t *cd = dst + n * nb * Q81_BYTES;
+        for (int64_t b = 0; b < nb; b++) {
+            const uint8_t *blk = cs + b * Q81_BYTES;
+            memcpy(cd + 32 * b, blk + 4, 32);
+            memcpy(cd + K + 2 * b, blk, 2);
+            memcpy(cd + K + 2 * nb + 2 * b, blk + 2, 2);
+        }
+    }
+}
+
 /* ----------------------------------------------------------- row gather
  * Row subset of a converted matrix (the draft head gathered from the planar
  * LM head, P2340 "What it changes"): output row j is source row ids[j], in

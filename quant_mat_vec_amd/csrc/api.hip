@@ -36,18 +36,22 @@ int check_mmvq(const void *w, const void *xq, const void *out, int64_t rows, int
     return QMV_OK;
 }
 
-int q6_dispatch(const void *w, int layout, const void *xq, float *out, int32_t *dump, int64_t rows,
+int q6_dispatch(const void *w, int layout_arg, const void *xq, float *out, int32_t *dump, int64_t rows,
                 int64_t K, int ncols, void *stream) {
-    if (layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR && layout != QMV_LAYOUT_TILED) {
+    const bool xp = (layout_arg & QMV_ACT_PLANAR) != 0;
+    const int layout = layout_arg & ~QMV_ACT_PLANAR;
+    if ((layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR && layout != QMV_LAYOUT_TILED) ||
+        (xp && layout != QMV_LAYOUT_TILED)) {
         if (!w || !xq || !(out || dump)) return QMV_ERR_INVALID_ARG;
         return QMV_ERR_UNSUPPORTED;
     }
     const void *o = out ? static_cast<const void *>(out) : static_cast<const void *>(dump);
     int rc = check_mmvq(w, xq, o, rows, K, ncols, 210, layout == QMV_LAYOUT_GGUF ? 4 : 16);
     if (rc) return rc;
+    if (xp && !aligned(xq, 16)) return QMV_ERR_ALIGNMENT;
     hipError_t e;
     if (layout == QMV_LAYOUT_TILED)
-        e = qmv::launch_mmvq_q6_tiled(w, xq, out, dump, rows, K, ncols, as_stream(stream));
+        e = qmv::launch_mmvq_q6_tiled(w, xq, out, dump, rows, K, ncols, xp, as_stream(stream));
     else if (layout == QMV_LAYOUT_PLANAR)
         e = qmv::launch_mmvq_q6_planar(w, xq, out, dump, rows, K, ncols, as_stream(stream));
     else
@@ -87,7 +91,15 @@ int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream) 
     if (K <= 0 || ncols <= 0) return QMV_ERR_INVALID_ARG;
     if (K % 32 != 0 || K > kMaxK || ncols > 65535) return QMV_ERR_UNSUPPORTED;
     if (!aligned(x, 4) || !aligned(xq, 4)) return QMV_ERR_ALIGNMENT;
-    return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, as_stream(stream)));
+    return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, false, as_stream(stream)));
+}
+
+int quantize_q8_1_planar(const float *x, void *xq, int64_t K, int ncols, void *stream) {
+    if (!x || !xq) return QMV_ERR_INVALID_ARG;
+    if (K <= 0 || ncols <= 0) return QMV_ERR_INVALID_ARG;
+    if (K % 32 != 0 || K > kMaxK || ncols > 65535) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(x, 4) || !aligned(xq, 4)) return QMV_ERR_ALIGNMENT;
+    return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, true, as_stream(stream)));
 }
 
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
@@ -177,16 +189,17 @@ size_t mmvq_q6k_argmax_workspace(int64_t rows, int ncols) {
 int mmvq_q6k_argmax(const void *w, int layout, const void *xq, int64_t rows, int64_t K, int ncols, int32_t *idx,
                     float *val, void *ws, size_t ws_bytes, void *stream) {
     if (!idx || !val || !ws) return QMV_ERR_INVALID_ARG;
-    if (layout != QMV_LAYOUT_TILED) {
+    const bool xp = (layout & QMV_ACT_PLANAR) != 0;
+    if ((layout & ~QMV_ACT_PLANAR) != QMV_LAYOUT_TILED) {
         if (!w || !xq) return QMV_ERR_INVALID_ARG;
         return QMV_ERR_UNSUPPORTED;
     }
     int rc = check_mmvq(w, xq, idx, rows, K, ncols, 210, 16);
     if (rc) return rc;
-    if (!aligned(val, 4) || !aligned(ws, 8)) return QMV_ERR_ALIGNMENT;
+    if (!aligned(val, 4) || !aligned(ws, 8) || (xp && !aligned(xq, 16))) return QMV_ERR_ALIGNMENT;
     if (ws_bytes < mmvq_q6k_argmax_workspace(rows, ncols)) return QMV_ERR_WORKSPACE;
     return from_hip(qmv::launch_mmvq_q6_tiled_argmax(w, xq, reinterpret_cast<uint64_t *>(ws), rows, K, ncols, idx,
-                                                     val, as_stream(stream)));
+                                                     val, xp, as_stream(stream)));
 }
 
 size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff) {

@@ -17,7 +17,7 @@ inline hipError_t allow_lds(const void *kernel, size_t bytes) {
     return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, bool planar, hipStream_t s);
 // Q6_K GGUF <-> planar (tiled = false: row-major planes; true: 16-row tiles)
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s);
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s);
@@ -28,10 +28,11 @@ hipError_t launch_gather(const uint8_t *src, uint8_t *dst, const int32_t *ids, i
 
 hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int32_t *dump,
                                  int64_t rows, int64_t K, int ncols, hipStream_t s);
+// xp: activations in the column-planar Q8_1 layout
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump,
-                                int64_t rows, int64_t K, int ncols, hipStream_t s);
+                                int64_t rows, int64_t K, int ncols, bool xp, hipStream_t s);
 hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
-                                       int ncols, int32_t *idx, float *val, hipStream_t s);
+                                       int ncols, int32_t *idx, float *val, bool xp, hipStream_t s);
 hipError_t launch_mmvq_q6_gguf(const void *w, const void *xq, float *out, int32_t *dump,
                                int64_t rows, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_mmvq_q4(const void *w, const void *xq, float *out, int32_t *dump,

@@ -9,7 +9,10 @@ namespace qmv {
 // the quant sum reduce inside each lane and then over the eight lanes with
 // DPP (no cross-row exchange), and every lane writes its own dword of four
 // quants.  x is [ncols][K], xq [ncols][K/32].  The arithmetic (max, d =
-// max / 127, round(x / d), sum) is that of q8_1_quantize32.
+// max / 127, round(x / d), sum) is that of q8_1_quantize32.  PLANAR: the
+// same bytes in the column-planar layout (per column of nb = K/32 blocks:
+// the K quants, then nb fp16 d, then nb fp16 s).
+template <bool PLANAR>
 __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__ x, uint8_t *__restrict__ xq,
                                                        int64_t K, int64_t nblocks) {
     const int64_t g = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 3;
@@ -38,22 +41,34 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
     s = dpp_iadd<0x4E>(s);
     s = dpp_iadd<0x141>(s);
     if (ok) {
-        uint32_t *blk = reinterpret_cast<uint32_t *>(xq + g * kQ81Bytes);
-        blk[1 + i] = ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) | (((uint32_t)q[2] & 0xFFu) << 16) |
-                     ((uint32_t)q[3] << 24);
-        if (i == 0) {
-            const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
-            const uint32_t sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
-            blk[0] = dbits | (sbits << 16);
+        const uint32_t qw = ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) |
+                            (((uint32_t)q[2] & 0xFFu) << 16) | ((uint32_t)q[3] << 24);
+        const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
+        const uint32_t sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+        if constexpr (PLANAR) {
+            const int64_t col = g / nb, b = g - col * nb;
+            uint8_t *c = xq + col * nb * kQ81Bytes;
+            reinterpret_cast<uint32_t *>(c + 32 * b)[i] = qw;
+            if (i == 0) {
+                reinterpret_cast<uint16_t *>(c + K)[b] = (uint16_t)dbits;
+                reinterpret_cast<uint16_t *>(c + K + 2 * nb)[b] = (uint16_t)sbits;
+            }
+        } else {
+            uint32_t *blk = reinterpret_cast<uint32_t *>(xq + g * kQ81Bytes);
+            blk[1 + i] = qw;
+            if (i == 0) blk[0] = dbits | (sbits << 16);
         }
     }
 }
 
-hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, hipStream_t s) {
+hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, bool planar, hipStream_t s) {
     const int64_t nblocks = (int64_t)ncols * (K / 32);
     const int64_t threads = nblocks * 8;
     const int64_t grid = (threads + 255) / 256;
-    hipLaunchKernelGGL(k_quantize_q8_1, dim3((unsigned)grid), dim3(256), 0, s, x, xq, K, nblocks);
+    if (planar)
+        hipLaunchKernelGGL(k_quantize_q8_1<true>, dim3((unsigned)grid), dim3(256), 0, s, x, xq, K, nblocks);
+    else
+        hipLaunchKernelGGL(k_quantize_q8_1<false>, dim3((unsigned)grid), dim3(256), 0, s, x, xq, K, nblocks);
     return hipGetLastError();
 }
 

@@ -2,45 +2,54 @@
 #include "mmvq_tiled.hpp"
 
 namespace qmv {
-template <bool DUMP>
+template <bool DUMP, bool XP>
 static hipError_t tiled_cols(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                              int ncols, hipStream_t s) {
     switch (ncols) {
-    case 1: return launch_tiled_n<1, DUMP>(w, xq, out, dump, rows, K, s);
-    case 2: return launch_tiled_n<2, DUMP>(w, xq, out, dump, rows, K, s);
-    case 3: return launch_tiled_n<3, DUMP>(w, xq, out, dump, rows, K, s);
-    case 4: return launch_tiled_n<4, DUMP>(w, xq, out, dump, rows, K, s);
-    case 5: return launch_tiled_n<5, DUMP>(w, xq, out, dump, rows, K, s);
-    case 6: return launch_tiled_n<6, DUMP>(w, xq, out, dump, rows, K, s);
-    case 7: return launch_tiled_n<7, DUMP>(w, xq, out, dump, rows, K, s);
-    case 8: return launch_tiled_n<8, DUMP>(w, xq, out, dump, rows, K, s);
+    case 1: return launch_tiled_n<1, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 2: return launch_tiled_n<2, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 3: return launch_tiled_n<3, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 4: return launch_tiled_n<4, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 5: return launch_tiled_n<5, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 6: return launch_tiled_n<6, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 7: return launch_tiled_n<7, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
+    case 8: return launch_tiled_n<8, DUMP, false, XP>(w, xq, out, dump, rows, K, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                                int ncols, hipStream_t s) {
-    return dump ? tiled_cols<true>(w, xq, out, dump, rows, K, ncols, s)
-                : tiled_cols<false>(w, xq, out, dump, rows, K, ncols, s);
+                                int ncols, bool xp, hipStream_t s) {
+    if (xp)
+        return dump ? tiled_cols<true, true>(w, xq, out, dump, rows, K, ncols, s)
+                    : tiled_cols<false, true>(w, xq, out, dump, rows, K, ncols, s);
+    return dump ? tiled_cols<true, false>(w, xq, out, dump, rows, K, ncols, s)
+                : tiled_cols<false, false>(w, xq, out, dump, rows, K, ncols, s);
 }
 
 // Fused greedy argmax: the product's per-tile column maxima into keys, then
 // one reduction launch.
-hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
-                                       int ncols, int32_t *idx, float *val, hipStream_t s) {
-    float *k = reinterpret_cast<float *>(keys);
-    hipError_t e;
+template <bool XP>
+static hipError_t tiled_argmax_cols(const void *w, const void *xq, float *k, int64_t rows, int64_t K, int ncols,
+                                    hipStream_t s) {
     switch (ncols) {
-    case 1: e = launch_tiled_n<1, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 2: e = launch_tiled_n<2, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 3: e = launch_tiled_n<3, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 4: e = launch_tiled_n<4, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 5: e = launch_tiled_n<5, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 6: e = launch_tiled_n<6, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 7: e = launch_tiled_n<7, false, true>(w, xq, k, nullptr, rows, K, s); break;
-    case 8: e = launch_tiled_n<8, false, true>(w, xq, k, nullptr, rows, K, s); break;
+    case 1: return launch_tiled_n<1, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 2: return launch_tiled_n<2, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 3: return launch_tiled_n<3, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 4: return launch_tiled_n<4, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 5: return launch_tiled_n<5, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 6: return launch_tiled_n<6, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 7: return launch_tiled_n<7, false, true, XP>(w, xq, k, nullptr, rows, K, s);
+    case 8: return launch_tiled_n<8, false, true, XP>(w, xq, k, nullptr, rows, K, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
+                                       int ncols, int32_t *idx, float *val, bool xp, hipStream_t s) {
+    float *k = reinterpret_cast<float *>(keys);
+    const hipError_t e = xp ? tiled_argmax_cols<true>(w, xq, k, rows, K, ncols, s)
+                            : tiled_argmax_cols<false>(w, xq, k, rows, K, ncols, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_argmax_reduce, dim3(ncols), dim3(kArgmaxThreads), 0, s, keys, (rows + 15) / 16, idx, val);
     return hipGetLastError();

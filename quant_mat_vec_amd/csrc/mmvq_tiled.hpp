@@ -72,7 +72,7 @@ struct Q6Tiled {
 // is stored (the rest follow it): measured best at two.
 constexpr int kTiledPre = 2;
 
-template <int N, int KS, int RTW, int IT>
+template <int N, int KS, int RTW, int IT, bool XP = false>
 struct TiledCfg {
     static constexpr int W = KS * RTW;                 // waves per workgroup
     static constexpr int NTHR = W * kWave;
@@ -89,13 +89,22 @@ struct TiledCfg {
     static constexpr bool WT = RTW == 1 && KS >= 8;
     static constexpr int WB = 4 * IT;                  // blocks per column of one wave
     static constexpr int SL = WT ? (N * WB + kWave - 1) / kWave : SI;   // load slots per lane
+    // XP: per column, 2 uint4 of quants and a quarter uint2 of d per block
+    static constexpr int SLOTW = WT ? kWave : NTHR;    // threads sharing the staging
+    static constexpr int QU = 2 * (WT ? WB : TNB);     // quant uint4 per column staged by them
+    static constexpr int DU = (WT ? WB : TNB) / 4;     // uint2 of d per column
+    static constexpr int QSL = (N * QU + SLOTW - 1) / SLOTW;
+    static constexpr int DSL = (N * DU + SLOTW - 1) / SLOTW;
     // zero entries after each quant array: a masked lane reads entry
     // N*TNB + 4*it at step it, so its LDS offset follows the step like the
     // others' and the step's part of every address is an immediate
     static constexpr int ZW = 4 * (IT - 1) + 1;
     static constexpr int XE = N * TNB + ZW;            // entries per quant array
-    // x0 | zeros | x1 | zeros (uint4) and d/4 per block (float)
-    static constexpr size_t TILE = (size_t)XE * 32 + (size_t)N * TNB * 4;
+    // Q8_1 blocks: x0 | zeros | x1 | zeros (uint4) and d/4 per block
+    // (float).  Column-planar activations (XP): quant entries of 32 B (both
+    // halves) with the zero entries after them, then d per block (fp16).
+    static constexpr size_t TILE = XP ? (size_t)XE * 32 + (size_t)N * TNB * 2
+                                      : (size_t)XE * 32 + (size_t)N * TNB * 4;
     static constexpr size_t RED = KS > 1 ? (size_t)W * NCG * kWave * 4 : 0;
     static constexpr size_t LDS = TILE > RED ? TILE : RED;
     static constexpr int PRE = kTiledPre < IT ? kTiledPre : IT;
@@ -116,12 +125,12 @@ struct TiledLane {
 
 // One chunk of CZ steps starting at step zc0: wave ks of the row tile takes
 // steps zc0 + ks*IT + it.  FULL: all steps exist (no clamping).
-template <bool FULL, int N, int KS, int RTW, int IT, bool DUMP>
+template <bool FULL, int N, int KS, int RTW, int IT, bool DUMP, bool XP>
 __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<TiledCfg<N, KS, RTW, IT>::NCG> &tl,
                                             const MmvqArgs &a, uint8_t *lds,
                                             int zc0, int ZS, int64_t row, bool rok,
                                             float (&acc)[TiledCfg<N, KS, RTW, IT>::NCG]) {
-    using C = TiledCfg<N, KS, RTW, IT>;
+    using C = TiledCfg<N, KS, RTW, IT, XP>;
     constexpr int TNB = C::TNB, NTHR = C::NTHR;
     const int tid = threadIdx.x, l = tid & (kWave - 1), kg = l >> 4;
     const int ks = __builtin_amdgcn_readfirstlane(tid / kWave) % KS;    // wave-uniform
@@ -147,12 +156,53 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
         }
         return i < lim && (FULL || b < nblk);
     };
-    ActRaw ar[C::SL];
+    // column-planar activations: column n's quants are K bytes at
+    // 36*xcol_of(n), its d values (fp16) follow them.  Quant slot s of the
+    // lane is uint4 j of column n's run for this chunk (two per block), d
+    // slot s is uint2 k (four blocks).
+    const int st = C::WT ? l : tid;
+    auto quant_slot = [&](int s, int &n, int &j) -> bool {
+        const int i = st + s * C::SLOTW, lim = N * C::QU, ic = min(i, lim - 1);
+        n = ic / C::QU;
+        j = ic - n * C::QU + (C::WT ? 8 * ks * IT : 0);
+        return i < lim && (FULL || j < 2 * nblk);
+    };
+    auto d_slot = [&](int s, int &n, int &k) -> bool {
+        const int i = st + s * C::SLOTW, lim = N * C::DU, ic = min(i, lim - 1);
+        n = ic / C::DU;
+        k = ic - n * C::DU + (C::WT ? ks * IT : 0);
+        return i < lim && (FULL || 4 * k < nblk);
+    };
+    ActRaw ar[XP ? 1 : C::SL];
+    v4u32 xv[XP ? C::QSL : 1];
+    v2u32 dv[XP ? C::DSL : 1];
+    if constexpr (XP) {
+        // the N columns are consecutive (the tiled launch passes them in
+        // order): one buffer over them, lane offsets within it, the chunk's
+        // offset in a scalar register
+        const uint32_t cstride = (uint32_t)(36 * (a.K / 32));
+        const __amdgpu_buffer_rsrc_t xr = plane_rsrc(a.xq, (int64_t)N * cstride);
 #pragma unroll
-    for (int s = 0; s < C::SL; s++) {
-        int n, b;
-        own_slot(s, n, b);
-        act_load(ar[s], a.xq, xcol_of<N>(a, n) + 4 * (int64_t)zc0 + (FULL ? b : min(b, nblk - 1)));
+        for (int s = 0; s < C::QSL; s++) {
+            int n, j;
+            quant_slot(s, n, j);
+            const uint32_t off = (uint32_t)n * cstride + 16u * (uint32_t)(FULL ? j : min(j, 2 * nblk - 1));
+            xv[s] = __builtin_amdgcn_raw_buffer_load_b128(xr, off, 128 * zc0, 0);
+        }
+#pragma unroll
+        for (int s = 0; s < C::DSL; s++) {
+            int n, k;
+            d_slot(s, n, k);
+            const uint32_t off = (uint32_t)n * cstride + (uint32_t)a.K + 8u * (uint32_t)(FULL ? k : min(k, nblk / 4 - 1));
+            dv[s] = __builtin_amdgcn_raw_buffer_load_b64(xr, off, 8 * zc0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < C::SL; s++) {
+            int n, b;
+            own_slot(s, n, b);
+            act_load(ar[s], a.xq, xcol_of<N>(a, n) + 4 * (int64_t)zc0 + (FULL ? b : min(b, nblk - 1)));
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -186,25 +236,41 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
     };
     load_ab(std::integral_constant<int, 0>{}, std::integral_constant<int, C::PRE>{});
 
-    // stage the tile: x0 (N*TNB entries + ZW zero entries), x1 (the same), fd
+    // stage the tile.  Q8_1 blocks: x0 (N*TNB entries + ZW zero entries), x1
+    // (the same), fd.  XP: q (entry e = uint4 2e, 2e+1; N*TNB entries + ZW
+    // zero entries), then dh (fp16 d per block, four to a uint2).
     uint4 *x0 = reinterpret_cast<uint4 *>(lds);
-    uint4 *x1 = x0 + C::XE;
-    float *fd = reinterpret_cast<float *>(x1 + C::XE);
+    uint4 *x1 = x0 + (XP ? 1 : C::XE);
+    constexpr int XS = XP ? 2 : 1;                     // uint4 per entry in x0/x1 indexing
+    float *fd = reinterpret_cast<float *>(x0 + 2 * C::XE);
+    uint2 *dh = reinterpret_cast<uint2 *>(x0 + 2 * C::XE);
     // (with wave tiles every wave writes the zero entries itself: the same
     // values, and then its own reads follow its own writes)
-    if ((C::WT ? l : tid) < C::ZW) {
-        const int z = C::WT ? l : tid;
-        x0[N * TNB + z] = make_uint4(0, 0, 0, 0);
-        x1[N * TNB + z] = make_uint4(0, 0, 0, 0);
+    if (st < C::ZW) {
+        x0[XS * (N * TNB + st)] = make_uint4(0, 0, 0, 0);
+        x1[XS * (N * TNB + st)] = make_uint4(0, 0, 0, 0);
     }
+    if constexpr (XP) {
 #pragma unroll
-    for (int s = 0; s < C::SL; s++) {
-        int n, b;
-        if (own_slot(s, n, b)) {
-            const int i = n * TNB + b;
-            x0[i] = make_uint4(ar[s].w[1], ar[s].w[2], ar[s].w[3], ar[s].w[4]);
-            x1[i] = make_uint4(ar[s].w[5], ar[s].w[6], ar[s].w[7], ar[s].w[8]);
-            fd[i] = half_to_float(ar[s].w[0]) * 0.25f;    // the codes are 4 * (q6 - 32)
+        for (int s = 0; s < C::QSL; s++) {
+            int n, j;
+            if (quant_slot(s, n, j)) reinterpret_cast<v4u32 *>(x0)[2 * n * TNB + j] = xv[s];
+        }
+#pragma unroll
+        for (int s = 0; s < C::DSL; s++) {
+            int n, k;
+            if (d_slot(s, n, k)) reinterpret_cast<v2u32 *>(dh)[n * (TNB / 4) + k] = dv[s];
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < C::SL; s++) {
+            int n, b;
+            if (own_slot(s, n, b)) {
+                const int i = n * TNB + b;
+                x0[i] = make_uint4(ar[s].w[1], ar[s].w[2], ar[s].w[3], ar[s].w[4]);
+                x1[i] = make_uint4(ar[s].w[5], ar[s].w[6], ar[s].w[7], ar[s].w[8]);
+                fd[i] = half_to_float(ar[s].w[0]) * 0.25f;    // the codes are 4 * (q6 - 32)
+            }
         }
     }
     if constexpr (C::WT) {
@@ -235,12 +301,14 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
             sl[i] = sext8(word, 2 * (i & 1));
             sh[i] = sext8(word, 2 * (i & 1) + 1);
         }
-        const float dw = half_to_float(wd[it]);
+        // (XP: the 1/4 of the codes 4*(q6-32) is taken on d_w instead of d_a,
+        // a power of two, so every product and sum is the same number)
+        const float dw = XP ? half_to_float(wd[it]) * 0.25f : half_to_float(wd[it]);
         v4i32 D0[C::NCG], D1[C::NCG];
 #pragma unroll
         for (int cg = 0; cg < C::NCG; cg++) {
             const int idx = tl.xb[cg] + 4 * it;
-            const uint4 X0 = x0[idx], X1 = x1[idx];
+            const uint4 X0 = x0[XS * idx], X1 = x1[XS * idx];
             const v4i32 A0 = {(int)X0.x, (int)X0.y, (int)X0.z, (int)X0.w};
             const v4i32 A1 = {(int)X1.x, (int)X1.y, (int)X1.z, (int)X1.w};
             const v4i32 Z = {0, 0, 0, 0};
@@ -250,8 +318,20 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
 #pragma unroll
         for (int cg = 0; cg < C::NCG; cg++) {
             const int no = 4 * cg + kg;            // this lane's output column
-            const float4 dx = *reinterpret_cast<const float4 *>(fd + min(no, N - 1) * TNB + zt);
-            const float dxa[4] = {dx.x, dx.y, dx.z, dx.w};
+            float dxa[4];
+            if constexpr (XP) {
+                const uint2 h = dh[(min(no, N - 1) * TNB + zt) / 4];
+                dxa[0] = half_to_float(h.x);
+                dxa[1] = half_to_float(h.x >> 16);
+                dxa[2] = half_to_float(h.y);
+                dxa[3] = half_to_float(h.y >> 16);
+            } else {
+                const float4 dx = *reinterpret_cast<const float4 *>(fd + min(no, N - 1) * TNB + zt);
+                dxa[0] = dx.x;
+                dxa[1] = dx.y;
+                dxa[2] = dx.z;
+                dxa[3] = dx.w;
+            }
             int I[4];
 #pragma unroll
             for (int i = 0; i < 4; i++) I[i] = __mul24(sl[i], D0[cg][i]) + __mul24(sh[i], D1[cg][i]);   // 4 * isum
@@ -262,7 +342,10 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
                     for (int i = 0; i < 4; i++) dp[i] = I[i] >> 2;
                 }
             } else {
-                float t = dxa[0] * (float)I[0];
+                // (an fma with +0 is the product: d_a >= 0, so no -0 arises;
+                // the fp16 d_a of column-planar tiles then feeds the fma
+                // without a conversion)
+                float t = __builtin_fmaf(dxa[0], (float)I[0], 0.0f);
 #pragma unroll
                 for (int i = 1; i < 4; i++) t = __builtin_fmaf(dxa[i], (float)I[i], t);
                 acc[cg] = __builtin_fmaf(dw, t, acc[cg]);
@@ -284,10 +367,10 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
 // AMAX: instead of the outputs, each row tile writes, per column n, the
 // largest argmax_key over its rows to keys[n * ntiles + tile] (out is then
 // a uint64 array of N * ceil(rows/16) keys).
-template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false>
+template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false, bool XP = false>
 __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
                                                                     float *__restrict__ out) {
-    using C = TiledCfg<N, KS, RTW, IT>;
+    using C = TiledCfg<N, KS, RTW, IT, XP>;
     extern __shared__ __align__(16) uint8_t lds[];
     Q6Tiled f;
     f.init(w, a.rows, a.K);
@@ -330,11 +413,11 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
     const int nfull = ZS / C::CZ;
     for (int c = 0; c < nfull; c++) {
         if (!C::WT && c > 0) lds_barrier();
-        tiled_chunk<true, N, KS, RTW, IT, DUMP>(f, tl, a, lds, c * C::CZ, ZS, row, rok, acc);
+        tiled_chunk<true, N, KS, RTW, IT, DUMP, XP>(f, tl, a, lds, c * C::CZ, ZS, row, rok, acc);
     }
     if (nfull * C::CZ < ZS) {
         if (!C::WT && nfull > 0) lds_barrier();
-        tiled_chunk<false, N, KS, RTW, IT, DUMP>(f, tl, a, lds, nfull * C::CZ, ZS, row, rok, acc);
+        tiled_chunk<false, N, KS, RTW, IT, DUMP, XP>(f, tl, a, lds, nfull * C::CZ, ZS, row, rok, acc);
     }
     if constexpr (!DUMP) {
         if constexpr (KS > 1) {
@@ -415,10 +498,10 @@ __global__ __launch_bounds__(kArgmaxThreads) void k_argmax_reduce(const uint64_t
     }
 }
 
-template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false>
+template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false, bool XP = false>
 hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                             hipStream_t s) {
-    using C = TiledCfg<N, KS, RTW, IT>;
+    using C = TiledCfg<N, KS, RTW, IT, XP>;
     MmvqArgs a;
     a.xq = reinterpret_cast<const uint8_t *>(xq);
     a.dump = dump;
@@ -429,9 +512,9 @@ hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *
     a.its = IT;
     const int64_t tiles = (rows + 15) / 16;
     const int64_t grid = (tiles + RTW - 1) / RTW;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX>), C::LDS);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX, XP>), C::LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX>), dim3((unsigned)grid), dim3(C::NTHR), C::LDS,
+    hipLaunchKernelGGL((k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX, XP>), dim3((unsigned)grid), dim3(C::NTHR), C::LDS,
                        s, w, a, out);
     return hipGetLastError();
 }
@@ -439,15 +522,15 @@ hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *
 // Waves along K per row tile: enough waves of five steps to cover a row in
 // one chunk (at most sixteen), and workgroups of at least four waves.  A
 // function of K only, so every column count sums a row in the same order.
-template <int N, bool DUMP, bool AMAX = false>
+template <int N, bool DUMP, bool AMAX = false, bool XP = false>
 hipError_t launch_tiled_n(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                           hipStream_t s) {
     const int64_t need = (K / 128 + 4) / 5;
-    if (need <= 1) return launch_tiled_cfg<N, 1, 4, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
-    if (need <= 2) return launch_tiled_cfg<N, 2, 2, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
-    if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
-    if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
-    return launch_tiled_cfg<N, 16, 1, 5, DUMP, AMAX>(w, xq, out, dump, rows, K, s);
+    if (need <= 1) return launch_tiled_cfg<N, 1, 4, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
+    if (need <= 2) return launch_tiled_cfg<N, 2, 2, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
+    if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
+    if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
+    return launch_tiled_cfg<N, 16, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
 }
 
 }  // namespace qmv

@@ -19,6 +19,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "qmv.h")
 QMV_OK, QMV_ERR_INVALID_ARG, QMV_ERR_UNSUPPORTED = 0, -1, -2
 QMV_ERR_ALIGNMENT, QMV_ERR_WORKSPACE, QMV_ERR_HIP = -3, -4, -5
 LAYOUT_GGUF, LAYOUT_PLANAR, LAYOUT_TILED = 0, 1, 2
+ACT_PLANAR = 16   # OR-ed into the layout with LAYOUT_TILED: column-planar activations
 
 _lib = None
 
@@ -41,6 +42,7 @@ def lib() -> ctypes.CDLL:
         P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
         sig = {
             "quantize_q8_1": [P, P, I64, I, P],
+            "quantize_q8_1_planar": [P, P, I64, I, P],
             "mmvq_q6k": [P, I, P, P, I64, I64, I, P],
             "mmvq_q4k": [P, P, P, I64, I64, I, P],
             "mmvq_q5k": [P, P, P, I64, I64, I, P],
@@ -113,6 +115,10 @@ def _check(rc: int, what: str) -> None:
 # ------------------------------------------------------------ entry points
 def quantize_q8_1(x, xq, K: int, ncols: int, stream=None) -> None:
     _check(lib().quantize_q8_1(_ptr(x), _ptr(xq), K, ncols, _stream(stream)), "quantize_q8_1")
+
+
+def quantize_q8_1_planar(x, xq, K: int, ncols: int, stream=None) -> None:
+    _check(lib().quantize_q8_1_planar(_ptr(x), _ptr(xq), K, ncols, _stream(stream)), "quantize_q8_1_planar")
 
 
 def mmvq_q6k(w, layout: int, xq, out, rows: int, K: int, ncols: int, stream=None) -> None:

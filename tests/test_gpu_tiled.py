@@ -263,3 +263,86 @@ def test_argmax_matches_own_outputs_and_oracle(rows, K, ncols):
         out2, idx2, val2 = run(w2)
         assert idx2[0] == lo and np.array_equal(val2[:1].view(np.uint32), val[:1].view(np.uint32))
         assert np.array_equal(idx2, np.argmax(out2, axis=1))
+
+
+# --------------------------------------------- column-planar activations
+XT = TL | qmv.ACT_PLANAR
+
+
+def quantize_planar(x: np.ndarray) -> torch.Tensor:
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    ncols, K = x.shape
+    xp = torch.empty(ncols * (K // 32) * 36, dtype=torch.uint8, device=DEV)
+    qmv.quantize_q8_1_planar(dev(x), xp, K, ncols)
+    return xp
+
+
+@pytest.mark.parametrize("K,ncols", [(32, 1), (256, 3), (2560, 13), (10240, 8), (992, 5)])
+def test_planar_quantizer_bytes(K, ncols):
+    """quantize_q8_1_planar writes the oracle's Q8_1 blocks, rearranged by the
+    oracle's column-planar permutation, byte for byte."""
+    note(f"quantize_q8_1_planar K={K} ncols={ncols}")
+    x = synth.activations(synth.rng(960 + K + ncols), ncols, K)
+    want = orc.q8_1_to_planar(orc.quantize_q8_1(x), K)
+    assert np.array_equal(host(quantize_planar(x)), want)
+
+
+@pytest.mark.parametrize("rows,K,ncols", SMALL + [(300, 1280, 8), (2100, 2560, 5)])
+def test_planar_activations_match_blocks_bitexact(rows, K, ncols):
+    """The tiled product and its integer sums from column-planar activations
+    have the bits of those from the same values in Q8_1 blocks, and the
+    isums equal the oracle's."""
+    note(f"mmvq_q6k tiled|act_planar rows={rows} K={K} ncols={ncols}")
+    g = synth.rng(970 + rows + K + ncols)
+    w = synth.q6k_blocks(g, rows, K)
+    x = synth.activations(g, ncols, K)
+    xq, xq_np = quantize(x)
+    xp = quantize_planar(x)
+    wt = tiled(dev(w), rows, K)
+    a = mmvq("q6k", wt, xq, rows, K, ncols, TL)
+    b = mmvq("q6k", wt, xp, rows, K, ncols, XT)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    ib = isums("q6k", wt, xp, rows, K, ncols, XT)
+    assert np.array_equal(ib, orc.q6k_isums(w, xq_np, rows, K))
+
+
+@pytest.mark.parametrize("rows,K,cols", [(10240, 2560, (8, 4, 1)), (2560, 10240, (8, 3)), (16405, 512, (6,)),
+                                         (8200, 20480, (2,))])
+def test_planar_activations_full_size(rows, K, cols):
+    """Full sizes (every launch shape): bits equal to the Q8_1-block path,
+    sampled rows within the oracle tolerance."""
+    g = synth.rng(980 + rows)
+    w = synth.q6k_blocks(g, rows, K)
+    wt = tiled(dev(w), rows, K)
+    x = synth.activations(g, 8, K)
+    xq, xq_np = quantize(x)
+    xp = quantize_planar(x)
+    for n in cols:
+        note(f"mmvq_q6k tiled|act_planar full {rows}x{K} N={n}")
+        a = mmvq("q6k", wt, xq, rows, K, n, TL)
+        b = mmvq("q6k", wt, xp, rows, K, n, XT)
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+        rs = sampled(rows, g, 24)
+        ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np[:n].reshape(-1), len(rs), K)
+        assert_close(b[:, rs], ref, ab, f"act_planar {rows}x{K} N={n}")
+
+
+@pytest.mark.parametrize("rows,K,ncols", [(151936, 2560, 4), (1000, 2560, 1), (37, 768, 8)])
+def test_planar_activations_argmax(rows, K, ncols):
+    """The fused argmax from column-planar activations gives the same index
+    and value bits as from Q8_1 blocks."""
+    note(f"mmvq_q6k_argmax tiled|act_planar {rows}x{K} N={ncols}")
+    g = synth.rng(990 + rows)
+    wt = tiled(dev(synth.q6k_blocks(g, rows, K)), rows, K)
+    x = synth.activations(g, ncols, K)
+    xq, _ = quantize(x)
+    xp = quantize_planar(x)
+    nws = qmv.mmvq_q6k_argmax_workspace(rows, ncols)
+    res = []
+    for lay, a in ((TL, xq), (XT, xp)):
+        ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+        idx = torch.empty(ncols, dtype=torch.int32, device=DEV)
+        val = torch.empty(ncols, dtype=torch.float32, device=DEV)
+        qmv.mmvq_q6k_argmax(wt, lay, a, rows, K, ncols, idx, val, ws, nws)
+        res.append((host(idx), host(val).view(np.uint32)))
+    assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])

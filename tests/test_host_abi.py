@@ -23,7 +23,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = qmv.declared_symbols()
-    expected = {"quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
+    expected = {"quantize_q8_1", "quantize_q8_1_planar", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
                 "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "gather_q6k_rows", "mmvq_q6k_argmax", "mmvq_q6k_argmax_workspace",
                 "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
@@ -41,8 +41,9 @@ def test_strerror_names_every_code(L):
     assert L.qmv_last_hip_error() == 0
 
 
-def test_quantize_rejects(L):
-    q = L.quantize_q8_1
+@pytest.mark.parametrize("name", ["quantize_q8_1", "quantize_q8_1_planar"])
+def test_quantize_rejects(L, name):
+    q = getattr(L, name)
     assert q(None, P, 256, 1, None) == E_INV
     assert q(P, None, 256, 1, None) == E_INV
     assert q(P, P, 0, 1, None) == E_INV
@@ -86,6 +87,16 @@ def test_mmvq_rejects(L, name):
         assert call(K=300, layout=qmv.LAYOUT_TILED) == E_UNS
         assert call(ncols=9, layout=qmv.LAYOUT_TILED) == E_UNS
         assert call(w=P + 2, layout=qmv.LAYOUT_GGUF) == E_ALN
+        # column-planar activations: only with the tiled layout, xq 16-byte aligned
+        XT = qmv.LAYOUT_TILED | qmv.ACT_PLANAR
+        assert call(layout=qmv.LAYOUT_PLANAR | qmv.ACT_PLANAR) == E_UNS
+        assert call(layout=qmv.LAYOUT_GGUF | qmv.ACT_PLANAR) == E_UNS
+        assert call(layout=3 | qmv.ACT_PLANAR) == E_UNS
+        assert call(layout=XT, xq=P + 4) == E_ALN
+        assert call(layout=XT, xq=P + 8) == E_ALN
+        assert call(layout=XT, w=P + 8) == E_ALN
+        assert call(layout=XT, xq=None) == E_INV
+        assert call(layout=XT, ncols=9) == E_UNS
     else:
         assert call(w=P + 8) == E_ALN
 
@@ -140,6 +151,10 @@ def test_argmax_rejects(L):
     assert call(val=P + 2) == E_ALN
     assert call(ws=P + 4) == E_ALN
     assert call(wsb=nws - 1) == E_WS
+    XT = TL | qmv.ACT_PLANAR
+    assert call(lay=qmv.LAYOUT_PLANAR | qmv.ACT_PLANAR) == E_UNS
+    assert call(lay=XT, xq=P + 4) == E_ALN
+    assert call(lay=XT, wsb=nws - 1) == E_WS
 
 
 def test_moe_rejects_and_workspace(L):

@@ -423,6 +423,35 @@ def test_planar_layout_pins():
         assert flips == 1
 
 
+def test_q8_1_planar_pins():
+    """Column-planar Q8_1 (the layout text of the library header): a tiny
+    case enumerated by hand, and on real activations the planar quants and d
+    dequantize to the same values as the blocks."""
+    K, ncols = 64, 2                       # two blocks per column
+    src = np.arange(144, dtype=np.uint8)
+    got = orc.q8_1_to_planar(src, K)
+    want = []
+    for c in (0, 72):                      # column base in both forms
+        want += list(range(c + 4, c + 36))     # block 0 quants
+        want += list(range(c + 40, c + 72))    # block 1 quants
+        want += [c + 0, c + 1, c + 36, c + 37]  # d of blocks 0, 1
+        want += [c + 2, c + 3, c + 38, c + 39]  # s of blocks 0, 1
+    assert got.tolist() == want
+    # semantics on quantized data: q (int8) * d (fp16) per block
+    g = synth.rng(77)
+    K, ncols = 512, 3
+    x = synth.activations(g, ncols, K)
+    xq = orc.quantize_q8_1(x)
+    pl = orc.q8_1_to_planar(xq, K).reshape(ncols, K // 32 * 36)
+    deq = orc.dequant_q8_1(xq, K)
+    q = pl[:, :K].view(np.int8).astype(np.float64)
+    d = pl[:, K:K + 2 * (K // 32)].copy().view(np.float16).astype(np.float64)
+    assert np.array_equal(q * np.repeat(d, 32, axis=1), deq)
+    s16 = pl[:, K + 2 * (K // 32):].copy().view(np.float16)
+    blk = xq.reshape(ncols, K // 32, 36)
+    assert np.array_equal(s16.view(np.uint16), blk[:, :, 2:4].copy().view(np.uint16)[:, :, 0])
+
+
 def test_tiled_layout_pins():
     """The tiled layout is the (pinned) planar one with the entries of every
     16-row group interleaved: for one row it is the planar layout itself,
