@@ -49,7 +49,11 @@ __device__ __forceinline__ bool moe_select(const MoeArgs &m, int i, int &e, uint
 }
 
 // Routing tables of the workspace (documented in qmv.h, for inspection):
-// written by one wave, each lane for its own slot.
+// written by one wave, each lane for its own slot, in one pass over the S
+// slot ids read as wave-uniform values (v_readlane; no LDS traffic).  Run
+// by a workgroup of its own so that no product workgroup waits for it
+// (from slot 0's workgroup, with two LDS shuffle passes over 64 lanes, it
+// held the gate/up launch 3-4 us longer at one token).
 __device__ void moe_write_tables(const MoeArgs &m) {
     const int s = threadIdx.x & (kWave - 1);
     int e = -1;
@@ -58,24 +62,24 @@ __device__ void moe_write_tables(const MoeArgs &m) {
         if (e < 0 || e >= m.E) e = -1;
     }
     const uint64_t valid = __ballot(e >= 0);
-    bool first_occ = e >= 0;
-    for (int t = 0; t < kWave; t++) {
-        const int et = __shfl(e, t);
-        if (et >= 0 && et == e && t < s) first_occ = false;
-    }
-    const uint64_t fo = __ballot(first_occ);
-    int before = 0, pos = 0, cnt = 0, rank = 0;
-    for (int t = 0; t < kWave; t++) {
-        const int et = __shfl(e, t);
+    // before: valid slots with a smaller expert; pos: earlier slots of this
+    // expert; cnt: slots of this expert; lt: the slots with a smaller expert
+    int before = 0, pos = 0, cnt = 0;
+    uint64_t lt = 0;
+    for (int t = 0; t < m.S; t++) {
+        const int et = __builtin_amdgcn_readlane(e, t);
         if (et < 0 || e < 0) continue;
         if (et < e) {
             before++;
-            rank += (int)((fo >> t) & 1);
+            lt |= 1ull << t;
         } else if (et == e) {
             cnt++;
             if (t < s) pos++;
         }
     }
+    const bool first_occ = e >= 0 && pos == 0;
+    const uint64_t fo = __ballot(first_occ);
+    const int rank = __popcll(lt & fo);     // distinct experts below e
     int32_t *wsi = reinterpret_cast<int32_t *>(m.ws);
     int32_t *expert = wsi + 64, *count = expert + m.S, *first = count + m.S, *slot_list = first + m.S;
     if (e >= 0) {
@@ -171,7 +175,10 @@ __global__ __launch_bounds__(U *kWave) void k_moe_gateup(MoeArgs m) {
     extern __shared__ __align__(16) uint8_t lds[];
     int e;
     uint64_t mask;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kWave) moe_write_tables(m);
+    if (blockIdx.x == gridDim.x - 1) {        // the extra column: tables only
+        if (blockIdx.y == 0 && threadIdx.x < kWave) moe_write_tables(m);
+        return;
+    }
     if (!moe_select(m, blockIdx.x, e, mask)) return;
     int done = 0;
     while (mask) {
@@ -296,8 +303,9 @@ static hipError_t launch_gateup_r(const MoeArgs &m, int smax, hipStream_t s) {
         if (b > act) act = b;
     }
     const size_t lds = 8 * kGuRows * sizeof(float) + act;
-    hipLaunchKernelGGL((k_moe_gateup<U, RAGGED>), dim3(smax, (unsigned)(m.d_ff / kGuRows)), dim3(nthr), lds, s,
-                       m);
+    // one workgroup column per slot, plus one that writes the routing tables
+    hipLaunchKernelGGL((k_moe_gateup<U, RAGGED>), dim3(smax + 1, (unsigned)(m.d_ff / kGuRows)), dim3(nthr), lds,
+                       s, m);
     return hipGetLastError();
 }
 

@@ -311,6 +311,9 @@ def test_moe_staged_parity(moe, T):
     exp_list = [s for e in hit for s in range(S) if ids.reshape(-1)[s] == e]
     assert list(wsi[64:64 + len(hit)]) == hit
     assert list(wsi[64 + 3 * S:64 + 4 * S]) == exp_list
+    cnts = [int((ids.reshape(-1) == e).sum()) for e in hit]
+    assert list(wsi[64 + S:64 + S + len(hit)]) == cnts
+    assert list(wsi[64 + 2 * S:64 + 2 * S + len(hit)]) == [int(v) for v in np.cumsum([0] + cnts[:-1])]
     h = ws[L["h"]:L["h"] + 4 * S * DFF].view(np.float32).reshape(S, DFF)
     hq = ws[L["hq"]:L["hq"] + 36 * S * DFF // 32].reshape(S, -1)
     y = ws[L["y"]:L["y"] + 4 * S * DM].view(np.float32).reshape(S, DM)
