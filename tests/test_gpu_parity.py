@@ -343,6 +343,49 @@ def test_moe_staged_parity(moe, T):
     assert rel < 1e-2
 
 
+def test_moe_graph_replay_matches_eager(moe):
+    """The routed chain captured in a HIP graph: every replay (workspace and
+    output poisoned before it, eager work between replays) gives the eager
+    output and routing tables bit for bit."""
+    note("MoE graph replay T=3")
+    T = 3
+    g = synth.rng(synth.seed_for(4, 5, T))
+    ids, rw = synth.routing(g, T, E, TOPK)
+    xq, _ = quantize(synth.activations(g, T, DM))
+    wsb = qmv.grouped_expert_mmvq_workspace(E, T, TOPK, DM, DFF)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=DEV)
+    out = torch.empty(T * DM, dtype=torch.float32, device=DEV)
+    idd, rwd = dev(ids), dev(rw)
+    L = qmv.moe_workspace_layout(T, TOPK, DM, DFF)
+
+    def call(stream=None):
+        qmv.grouped_expert_mmvq(moe["gd"], moe["ud"], moe["dp"], PL, xq, idd, rwd, out, E, T, TOPK, DM, DFF,
+                                ws, wsb, stream=stream)
+    S = T * TOPK
+    nhit = len(set(ids.reshape(-1).tolist()))
+
+    def written(wsh):                 # the table entries a call writes
+        wi = wsh[:L["h"]].view(np.int32)
+        return np.concatenate([wi[0:2], wi[64:64 + nhit], wi[64 + S:64 + S + nhit],
+                               wi[64 + 2 * S:64 + 2 * S + nhit], wi[64 + 3 * S:64 + 4 * S]])
+    call()
+    eager, tables = host(out).copy(), written(host(ws))
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            call(stream=s)
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint32), eager.view(np.uint32)), f"replay {i}"
+        assert np.array_equal(written(host(ws)), tables), f"tables, replay {i}"
+        _ = (out * 2).sum().item()             # eager work between replays
+
+
 def test_moe_unrouted_experts_unread(moe):
     """NaN scales in every expert no token is routed to leave out unchanged."""
     note("MoE poisoned unrouted experts")

@@ -169,23 +169,26 @@ def test_tiled_agrees_with_planar():
     assert np.all(np.abs(a.astype(np.float64) - b) <= 3e-5 * np.abs(b).max(axis=-1, keepdims=True))
 
 
-def test_tiled_graph_replay_matches_eager():
-    note("graph capture of quantize + tiled mmvq_q6k")
+@pytest.mark.parametrize("act_planar", [False, True])
+def test_tiled_graph_replay_matches_eager(act_planar):
+    note(f"graph capture of quantize + tiled mmvq_q6k (column-planar activations: {act_planar})")
     rows, K, ncols = 2048, 2560, 4
     g = synth.rng(950)
     w = tiled(dev(synth.q6k_blocks(g, rows, K)), rows, K)
     x = dev(synth.activations(g, ncols, K))
     xq = torch.empty(ncols * K // 32 * 36, dtype=torch.uint8, device=DEV)
     out = torch.empty(ncols * rows, dtype=torch.float32, device=DEV)
-    qmv.quantize_q8_1(x, xq, K, ncols)
-    qmv.mmvq_q6k(w, TL, xq, out, rows, K, ncols)
+    quant = qmv.quantize_q8_1_planar if act_planar else qmv.quantize_q8_1
+    lay = TL | qmv.ACT_PLANAR if act_planar else TL
+    quant(x, xq, K, ncols)
+    qmv.mmvq_q6k(w, lay, xq, out, rows, K, ncols)
     eager = host(out).copy()
     s = torch.cuda.Stream()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(graph, stream=s):
-            qmv.quantize_q8_1(x, xq, K, ncols, stream=s)
-            qmv.mmvq_q6k(w, TL, xq, out, rows, K, ncols, stream=s)
+            quant(x, xq, K, ncols, stream=s)
+            qmv.mmvq_q6k(w, lay, xq, out, rows, K, ncols, stream=s)
     for i in range(5):
         out.fill_(float("nan"))
         xq.zero_()
