@@ -368,7 +368,41 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
         for (r_, k_) in ((12288, 2560), (6144, 2560), (2560, 6144), (512, 2560)):
             ex[f"{kind}_{r_}x{k_}"] = shape_case(kind, r_, k_, (1, 4), seed=15 + r_)
     ex["moe_e128_2560_768"] = moe_case(torch, np, qmv, synth, dev)
+    ex["rmsnorm_quantize_13x2560"] = norm_case(torch, np, qmv, synth, dev)
     return ex
+
+
+def norm_case(torch, np, qmv, synth, dev):
+    """The fused RMSNorm -> Q8_1 launch on the step's 13 columns: per call
+    from graph replays, and eager beside an unfused form (the norm as plain
+    torch ops, then quantize_q8_1) for context."""
+    g = synth.rng(77)
+    x = torch.from_numpy(synth.activations(g, XCOLS, K)).to(dev)
+    gam = torch.from_numpy((0.5 + g.random(K)).astype(np.float32)).to(dev)
+    xq = torch.empty(XCOLS * (K // 32) * 36, dtype=torch.uint8, device=dev)
+    eps = 1e-6
+    fused_us = graph_avg_us(torch, [lambda: qmv.rmsnorm_quantize_q8_1(x, gam, eps, xq, K, XCOLS)] * 50)
+
+    def unfused():
+        y = x * torch.rsqrt(x.pow(2).mean(dim=1, keepdim=True) + eps) * gam
+        qmv.quantize_q8_1(y, xq, K, XCOLS)
+
+    def eager_us(fn, n=200):
+        for _ in range(10):
+            fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / n
+
+    return {"fused_graph_us": round(fused_us, 3),
+            "fused_eager_us": round(eager_us(lambda: qmv.rmsnorm_quantize_q8_1(x, gam, eps, xq, K, XCOLS)), 3),
+            "unfused_torch_norm_plus_quantize_eager_us": round(eager_us(unfused), 3),
+            "plain_quantize_graph_us": round(graph_avg_us(torch, [lambda: qmv.quantize_q8_1(x, xq, K, XCOLS)] * 50), 3)}
 
 
 def lm_head_case(torch, np, qmv, synth, dev):

@@ -140,6 +140,20 @@ int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream);
  * column-planar layout.  xq: 4-byte aligned (16-byte for the products). */
 int quantize_q8_1_planar(const float *x, void *xq, int64_t K, int ncols, void *stream);
 
+/* RMSNorm fused into the Q8_1 quantizer (the norm step ahead of the MMVQ
+ * whose fused opt-in PR #1774 "How it was checked" measures end to end; the
+ * pages do not define the norm, read here as RMSNorm).  Per column n:
+ *   r = 1 / sqrt(sum_i x[n][i]^2 / K + eps), y[i] = (x[n][i] * r) * gamma[i]
+ * in fp32 (the sum in a fixed order; IEEE division and square root), then
+ * y is quantized exactly as quantize_q8_1 quantizes its input.  One launch,
+ * no y in memory.  x: fp32 [ncols][K], gamma: fp32 [K], both 16-byte
+ * aligned; eps >= 0 (finite; with eps = 0 an all-zero column has no
+ * defined norm); xq: 4-byte aligned, Q8_1 blocks
+ * (act_layout 0) or column-planar (act_layout QMV_ACT_PLANAR).
+ * K % 32 == 0, 1 <= ncols <= 65535. */
+int rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *xq, int64_t K, int ncols,
+                          int act_layout, void *stream);
+
 /* Q6_K weights x Q8_1 activations (the Q6_K dense decode product of PR
  * #2340 "What it changes" and PR #2207 "How it was checked").
  * w: rows x K Q6_K matrix in `layout` (QMV_LAYOUT_GGUF: 210-byte blocks,

@@ -58,6 +58,7 @@ def lib():
         L.orc_q6k_gather.argtypes = [P, I, I64, I64, P, I64, P]
         L.orc_quantize_q8_1.argtypes = [P, P, I64, I]
         L.orc_q8_1_to_planar.argtypes = [P, P, I64, I]
+        L.orc_rmsnorm.argtypes = [P, P, D, P, I64, I]
         L.orc_dequant_q8_1.argtypes = [P, P, I64, I]
         for name in ("orc_q6k_isums", "orc_q4k_dots", "orc_q5k_dots"):
             getattr(L, name).argtypes = [P, P, P, I64, I64, I]
@@ -138,6 +139,24 @@ def quantize_q8_1(x):
     xq = np.zeros((ncols, K // 32 * Q81_BYTES), np.uint8)
     lib().orc_quantize_q8_1(_p(x), _p(xq), K, ncols)
     return xq
+
+
+def rmsnorm(x, gamma, eps: float):
+    """RMSNorm per column in fp64, rounded to fp32: [ncols][K]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.ndim == 1:
+        x = x[None]
+    ncols, K = x.shape
+    gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+    assert gamma.shape == (K,)
+    y = np.zeros((ncols, K), np.float32)
+    lib().orc_rmsnorm(_p(x), _p(gamma), float(eps), _p(y), K, ncols)
+    return y
+
+
+def rmsnorm_quantize_q8_1(x, gamma, eps: float):
+    """The fused norm + quantizer: quantize_q8_1 of rmsnorm(x)."""
+    return quantize_q8_1(rmsnorm(x, gamma, eps))
 
 
 def q8_1_to_planar(xq, K: int):

@@ -253,6 +253,21 @@ void orc_quantize_q8_1(const float *x, uint8_t *xq, int64_t K, int ncols) {
         }
 }
 
+/* RMSNorm of each activation column (the norm ahead of the quantizer whose
+ * fused opt-in IQ3 "How it was checked" measures; the pages do not define
+ * the norm, read as RMSNorm): r = 1/sqrt(mean(x^2) + eps) and
+ * y = x * r * gamma, all in fp64, y rounded to fp32 once.  The fused
+ * quantization is then orc_quantize_q8_1 of y. */
+void orc_rmsnorm(const float *x, const float *gamma, double eps, float *y, int64_t K, int ncols) {
+    for (int n = 0; n < ncols; n++) {
+        const float *xc = x + (int64_t)n * K;
+        double ss = 0.0;
+        for (int64_t i = 0; i < K; i++) ss += (double)xc[i] * (double)xc[i];
+        const double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t i = 0; i < K; i++) y[(int64_t)n * K + i] = (float)((double)xc[i] * r * (double)gamma[i]);
+    }
+}
+
 /* Dequantized activation xhat = d * q (fp64), [ncols][K]. */
 void orc_dequant_q8_1(const uint8_t *xq, double *out, int64_t K, int ncols) {
     int64_t nb = K / QB;

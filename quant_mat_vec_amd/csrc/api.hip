@@ -102,6 +102,18 @@ int quantize_q8_1_planar(const float *x, void *xq, int64_t K, int ncols, void *s
     return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, true, as_stream(stream)));
 }
 
+int rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *xq, int64_t K, int ncols,
+                          int act_layout, void *stream) {
+    if (!x || !gamma || !xq) return QMV_ERR_INVALID_ARG;
+    if (K <= 0 || ncols <= 0) return QMV_ERR_INVALID_ARG;
+    if (K % 32 != 0 || K > kMaxK || ncols > 65535 || (act_layout != 0 && act_layout != QMV_ACT_PLANAR))
+        return QMV_ERR_UNSUPPORTED;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return QMV_ERR_INVALID_ARG;   // also rejects NaN
+    if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(xq, 4)) return QMV_ERR_ALIGNMENT;
+    return from_hip(qmv::launch_rmsnorm_quantize(x, gamma, eps, reinterpret_cast<uint8_t *>(xq), K, ncols,
+                                                 act_layout == QMV_ACT_PLANAR, as_stream(stream)));
+}
+
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
              void *stream) {
     if (!out) return QMV_ERR_INVALID_ARG;

@@ -18,6 +18,8 @@ inline hipError_t allow_lds(const void *kernel, size_t bytes) {
 }
 
 hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, bool planar, hipStream_t s);
+hipError_t launch_rmsnorm_quantize(const float *x, const float *gamma, float eps, uint8_t *xq, int64_t K, int ncols,
+                                   bool planar, hipStream_t s);
 // Q6_K GGUF <-> planar (tiled = false: row-major planes; true: 16-row tiles)
 hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s);
 hipError_t launch_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, hipStream_t s);

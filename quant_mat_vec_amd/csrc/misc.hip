@@ -72,6 +72,92 @@ hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, bo
     return hipGetLastError();
 }
 
+// Fused RMSNorm -> Q8_1: one workgroup per column.  Pass 1 sums x^2 (fp32,
+// fixed order: each thread's float4s in sequence, a 64-lane butterfly, the
+// four waves in order, so every thread holds the same sum); r =
+// 1/sqrt(sum/K + eps) (IEEE division and square root); pass 2 forms
+// y = (x*r)*gamma and quantizes it with the arithmetic of k_quantize_q8_1
+// (eight lanes per block), in the Q8_1 blocks or the column-planar layout.
+// One read of x for the sum, one (from L2) for the codes; no intermediate
+// y in memory and one launch instead of a norm pass plus a quantize pass.
+template <bool PLANAR>
+__global__ __launch_bounds__(256) void k_rmsnorm_q8_1(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                      float eps, uint8_t *__restrict__ xq, int64_t K) {
+    __shared__ float part[4];
+    const int64_t col = blockIdx.x, nb = K / 32;
+    const float *xc = x + col * K;
+    const int tid = threadIdx.x, lane = tid & 63;
+    float ss = 0.0f;
+    for (int64_t i = tid; i < K / 4; i += 256) {
+        const float4 v = reinterpret_cast<const float4 *>(xc)[i];
+        ss = __builtin_fmaf(v.x, v.x, ss);
+        ss = __builtin_fmaf(v.y, v.y, ss);
+        ss = __builtin_fmaf(v.z, v.z, ss);
+        ss = __builtin_fmaf(v.w, v.w, ss);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    if (lane == 0) part[tid >> 6] = ss;
+    __syncthreads();
+    ss = ((part[0] + part[1]) + part[2]) + part[3];
+    const float r = 1.0f / sqrtf(ss / (float)K + eps);
+    uint8_t *c = xq + col * nb * kQ81Bytes;
+    const int i = tid & 7;
+    for (int64_t b0 = 0; b0 < nb; b0 += 32) {
+        const int64_t b = b0 + (tid >> 3);
+        const bool ok = b < nb;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (ok) {
+            const float4 xv = reinterpret_cast<const float4 *>(xc + 32 * b)[i];
+            const float4 gv = reinterpret_cast<const float4 *>(gamma + 32 * b)[i];
+            v[0] = (xv.x * r) * gv.x;
+            v[1] = (xv.y * r) * gv.y;
+            v[2] = (xv.z * r) * gv.z;
+            v[3] = (xv.w * r) * gv.w;
+        }
+        float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        a = dpp_max<0xB1>(a);
+        a = dpp_max<0x4E>(a);
+        a = dpp_max<0x141>(a);
+        const float d = a / 127.0f;
+        int q[4] = {0, 0, 0, 0};
+        if (d != 0.0f) {
+#pragma unroll
+            for (int k = 0; k < 4; k++) q[k] = (int)fminf(fmaxf(roundf(v[k] / d), -127.0f), 127.0f);
+        }
+        int s = q[0] + q[1] + q[2] + q[3];
+        s = dpp_iadd<0xB1>(s);
+        s = dpp_iadd<0x4E>(s);
+        s = dpp_iadd<0x141>(s);
+        if (ok) {
+            const uint32_t qw = ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) |
+                                (((uint32_t)q[2] & 0xFFu) << 16) | ((uint32_t)q[3] << 24);
+            const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
+            const uint32_t sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+            if constexpr (PLANAR) {
+                reinterpret_cast<uint32_t *>(c + 32 * b)[i] = qw;
+                if (i == 0) {
+                    reinterpret_cast<uint16_t *>(c + K)[b] = (uint16_t)dbits;
+                    reinterpret_cast<uint16_t *>(c + K + 2 * nb)[b] = (uint16_t)sbits;
+                }
+            } else {
+                uint32_t *blk = reinterpret_cast<uint32_t *>(c + b * kQ81Bytes);
+                blk[1 + i] = qw;
+                if (i == 0) blk[0] = dbits | (sbits << 16);
+            }
+        }
+    }
+}
+
+hipError_t launch_rmsnorm_quantize(const float *x, const float *gamma, float eps, uint8_t *xq, int64_t K, int ncols,
+                                   bool planar, hipStream_t s) {
+    if (planar)
+        hipLaunchKernelGGL(k_rmsnorm_q8_1<true>, dim3((unsigned)ncols), dim3(256), 0, s, x, gamma, eps, xq, K);
+    else
+        hipLaunchKernelGGL(k_rmsnorm_q8_1<false>, dim3((unsigned)ncols), dim3(256), 0, s, x, gamma, eps, xq, K);
+    return hipGetLastError();
+}
+
 // Where the parts of GGUF block t (row t / nb, block t % nb of the row) go
 // in the planar layouts, in units of the part's size: 16-byte A and 8-byte B
 // pieces of sub-block j, the two 8-byte halves of the scales, the 2-byte d.

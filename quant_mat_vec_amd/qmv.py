@@ -43,6 +43,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "quantize_q8_1": [P, P, I64, I, P],
             "quantize_q8_1_planar": [P, P, I64, I, P],
+            "rmsnorm_quantize_q8_1": [P, P, ctypes.c_float, P, I64, I, I, P],
             "mmvq_q6k": [P, I, P, P, I64, I64, I, P],
             "mmvq_q4k": [P, P, P, I64, I64, I, P],
             "mmvq_q5k": [P, P, P, I64, I64, I, P],
@@ -119,6 +120,12 @@ def quantize_q8_1(x, xq, K: int, ncols: int, stream=None) -> None:
 
 def quantize_q8_1_planar(x, xq, K: int, ncols: int, stream=None) -> None:
     _check(lib().quantize_q8_1_planar(_ptr(x), _ptr(xq), K, ncols, _stream(stream)), "quantize_q8_1_planar")
+
+
+def rmsnorm_quantize_q8_1(x, gamma, eps: float, xq, K: int, ncols: int, act_layout: int = 0,
+                          stream=None) -> None:
+    _check(lib().rmsnorm_quantize_q8_1(_ptr(x), _ptr(gamma), float(eps), _ptr(xq), K, ncols, act_layout,
+                                       _stream(stream)), "rmsnorm_quantize_q8_1")
 
 
 def mmvq_q6k(w, layout: int, xq, out, rows: int, K: int, ncols: int, stream=None) -> None:

@@ -23,7 +23,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = qmv.declared_symbols()
-    expected = {"quantize_q8_1", "quantize_q8_1_planar", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
+    expected = {"quantize_q8_1", "quantize_q8_1_planar", "rmsnorm_quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
                 "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "gather_q6k_rows", "mmvq_q6k_argmax", "mmvq_q6k_argmax_workspace",
                 "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
@@ -53,6 +53,20 @@ def test_quantize_rejects(L, name):
     assert q(P, P, 256, 65536, None) == E_UNS
     assert q(P + 2, P, 256, 1, None) == E_ALN
     assert q(P, P + 1, 256, 1, None) == E_ALN
+
+
+def test_rmsnorm_quantize_rejects(L):
+    f = L.rmsnorm_quantize_q8_1
+
+    def call(x=P, g=P, eps=1e-6, xq=P, K=256, n=1, lay=0):
+        return f(x, g, eps, xq, K, n, lay, None)
+
+    assert call(x=None) == E_INV and call(g=None) == E_INV and call(xq=None) == E_INV
+    assert call(K=0) == E_INV and call(n=0) == E_INV
+    assert call(eps=-1.0) == E_INV and call(eps=float("nan")) == E_INV and call(eps=float("inf")) == E_INV
+    assert call(K=100) == E_UNS and call(K=(1 << 20) + 32) == E_UNS and call(n=65536) == E_UNS
+    assert call(lay=1) == E_UNS and call(lay=qmv.LAYOUT_TILED | qmv.ACT_PLANAR) == E_UNS
+    assert call(x=P + 4) == E_ALN and call(g=P + 8) == E_ALN and call(xq=P + 2) == E_ALN
 
 
 @pytest.mark.parametrize("name", ["mmvq_q6k", "mmvq_q4k", "mmvq_q5k",

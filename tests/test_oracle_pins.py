@@ -576,3 +576,42 @@ def test_moe_rejects_bad_ids():
     with pytest.raises(ValueError):
         orc.grouped_expert(gate, up, down, xq, np.array([[2]], np.int32),
                            np.array([[1.0]], np.float32), 2, 1, 1, 256, 256)
+
+
+def test_rmsnorm_pins():
+    """RMSNorm oracle (the norm ahead of the fused quantizer): a hand-worked
+    block, exact invariances of the definition, unit RMS, the eps limit."""
+    # x = 2 everywhere: mean x^2 = 4, r = 1/2, y = 1 -> every code 127
+    K = 32
+    x = np.full((1, K), 2.0, np.float32)
+    g = np.ones(K, np.float32)
+    assert np.array_equal(orc.rmsnorm(x, g, 0.0), np.ones((1, K), np.float32))
+    q = orc.rmsnorm_quantize_q8_1(x, g, 0.0)[0]
+    assert np.all(q[4:].view(np.int8) == 127)
+    assert q[0:2].view(np.float16)[0] == np.float16(np.float32(1.0) / np.float32(127.0))
+    # random columns
+    r = synth.rng(4242)
+    K, n = 2560, 3
+    x = (r.standard_normal((n, K)) * 3.0).astype(np.float32)
+    g = (0.5 + r.random(K)).astype(np.float32)
+    y = orc.rmsnorm(x, g, 0.0)
+    # invariant under x -> 4x with eps = 0 (every step scales exactly)
+    assert np.array_equal(orc.rmsnorm(x * np.float32(4.0), g, 0.0), y)
+    # linear in gamma: 2*gamma doubles y exactly; the codes stay, d doubles
+    y2 = orc.rmsnorm(x, g * np.float32(2.0), 0.0)
+    assert np.array_equal(y2, 2 * y)
+    qa = orc.quantize_q8_1(y).reshape(n, -1, 36)
+    qb = orc.quantize_q8_1(y2).reshape(n, -1, 36)
+    assert np.array_equal(qa[:, :, 4:], qb[:, :, 4:])
+    assert np.array_equal(qa[:, :, 0:2].copy().view(np.float16).astype(np.float64) * 2,
+                          qb[:, :, 0:2].copy().view(np.float16).astype(np.float64))
+    # unit root-mean-square of y / gamma when eps = 0
+    rms = np.sqrt(np.mean((y.astype(np.float64) / g) ** 2, axis=1))
+    assert np.all(np.abs(rms - 1.0) < 1e-6)
+    # eps far above mean(x^2): y -> x * gamma / sqrt(eps)
+    xs = (x * np.float32(1e-4)).astype(np.float32)
+    ye = orc.rmsnorm(xs, g, 1.0e4)
+    want = xs.astype(np.float64) * g / 100.0
+    assert np.all(np.abs(ye - want) <= 1e-6 * np.abs(want) + 1e-12)
+    # the fused form is the quantizer of y, block for block
+    assert np.array_equal(orc.rmsnorm_quantize_q8_1(x, g, 1e-6), orc.quantize_q8_1(orc.rmsnorm(x, g, 1e-6)))
