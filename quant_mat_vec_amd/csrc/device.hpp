@@ -38,6 +38,14 @@ __host__ __device__ constexpr int choose_u(int units, int cap = 64) {
     return 8;
 }
 
+// The largest of 64, 32, 16 lanes per row that gives every lane at least two
+// units (not necessarily the same number), else 8.
+__host__ __device__ constexpr int choose_u_min2(int units) {
+    for (int U = 64; U >= 16; U /= 2)
+        if (units >= 2 * U) return U;
+    return 8;
+}
+
 // Activation tile limits: bytes of LDS per workgroup (the device allows
 // 160 KB) and Q8_1 blocks each thread loads ahead of the weights.
 constexpr int kMaxTileBytes = 120 * 1024;

@@ -121,7 +121,13 @@ template <class F, bool DUMP>
 hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                         int ncols, hipStream_t s) {
     const int units = (int)(K / 32 / F::SBPU);
-    switch (choose_u(units)) {
+    // Q4_K/Q5_K (a unit is a 32-byte pair of sub-blocks): the most lanes per
+    // row that leave each lane at least two units, the last chunk ragged if
+    // need be -- at K = 2560, 16 lanes and 2.5 units measured 7-15 % faster
+    // than 8 lanes and 5 units (twice the waves; 6144 and 12288 rows, N = 1
+    // and 4).  Q6_K keeps choose_u.  Either way a function of K only.
+    const int u = F::SBPU == 2 ? choose_u_min2(units) : choose_u(units);
+    switch (u) {
     case 8: return launch_dense_u<F, 8, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     case 16: return launch_dense_u<F, 16, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     case 32: return launch_dense_u<F, 32, DUMP>(w, xq, out, dump, rows, K, ncols, s);
