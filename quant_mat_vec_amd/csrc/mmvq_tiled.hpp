@@ -98,6 +98,11 @@ struct TiledCfg {
     // (2560x10240), within +-0.03 us at N = 1, 8 but 0.14 us slower at N = 4
     // with four (10240x2560), so only from eight waves on.
     static constexpr bool SCS = KS >= 8;
+    // d alone shared the same way (one load instead of five): with four
+    // waves along K 0.11 us faster at N = 8 and 0.1 us slower at N = 1, 4
+    // (10240x2560).  The values, and so every output bit, are the same
+    // either way.
+    static constexpr bool DS = SCS || N >= 8;
     // XP: per column, 2 uint4 of quants and a quarter uint2 of d per block
     static constexpr int SLOTW = WT ? kWave : NTHR;    // threads sharing the staging
     static constexpr int QU = 2 * (WT ? WB : TNB);     // quant uint4 per column staged by them
@@ -219,7 +224,7 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
     // first PRE steps; the rest after the tile is stored
     uint4 wa[IT];
     uint2 wb[IT], wsc[C::SCS ? 1 : IT];
-    uint32_t wd[C::SCS ? 1 : IT];
+    uint32_t wd[C::DS ? 1 : IT];
     int zs[IT];
 #pragma unroll
     for (int it = 0; it < IT; it++) {
@@ -230,18 +235,19 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
     const int z0 = zs[0], rr = min(l & 15, tl.R - 1);
     v2u32 scA = {0u, 0u}, scB = {0u, 0u};
     uint32_t dsh = 0;
+    // (entries past the tile's planes read as zero and are never used)
+    if constexpr (C::DS) dsh = __builtin_amdgcn_raw_buffer_load_b16(tl.d, tl.ob >> 2, 2 * ((z0 >> 1) * tl.R), 0);
     if constexpr (C::SCS) {
-        // entries past the tile's planes read as zero and are never used
         scA = __builtin_amdgcn_raw_buffer_load_b64(tl.sc, tl.ob, 8 * z0 * tl.R, 0);
         if constexpr (IT > 4) scB = __builtin_amdgcn_raw_buffer_load_b64(tl.sc, tl.ob, 8 * (z0 + 4) * tl.R, 0);
-        dsh = __builtin_amdgcn_raw_buffer_load_b16(tl.d, tl.ob >> 2, 2 * ((z0 >> 1) * tl.R), 0);
     } else {
 #pragma unroll
         for (int it = 0; it < IT; it++) {
             const int zr = zs[it] * tl.R;                          // wave-uniform
             const v2u32 sc = __builtin_amdgcn_raw_buffer_load_b64(tl.sc, tl.osc, 8 * zr, 0);
             wsc[it] = make_uint2(sc.x, sc.y);
-            wd[it] = __builtin_amdgcn_raw_buffer_load_b16(tl.d, tl.od, 2 * ((zs[it] >> 1) * tl.R), 0);
+            if constexpr (!C::DS)
+                wd[it] = __builtin_amdgcn_raw_buffer_load_b16(tl.d, tl.od, 2 * ((zs[it] >> 1) * tl.R), 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -324,11 +330,13 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
             const v2u32 src = dz < 4 ? scA : scB;
             const int from = rr + 16 * (dz & 3);
             sct = make_uint2((uint32_t)__shfl((int)src.x, from), (uint32_t)__shfl((int)src.y, from));
-            dt = (uint32_t)__shfl((int)dsh, rr + 16 * ((zs[it] >> 1) - (z0 >> 1)));
         } else {
             sct = wsc[it];
-            dt = wd[it];
         }
+        if constexpr (C::DS)
+            dt = (uint32_t)__shfl((int)dsh, rr + 16 * ((zs[it] >> 1) - (z0 >> 1)));
+        else
+            dt = wd[it];
         int sl[4], sh[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
