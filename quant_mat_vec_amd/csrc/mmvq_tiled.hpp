@@ -69,8 +69,10 @@ struct Q6Tiled {
 };
 
 // Weight steps whose code-plane loads are issued before the activation tile
-// is stored (the rest follow it): measured best at two.
-constexpr int kTiledPre = 2;
+// is stored (the rest follow it): measured best at two, and at three with
+// eight or more waves along K (of 1, 2, 3 and all five; 2560x10240:
+// 0.05-0.1 us faster than two).
+constexpr int kTiledPre = 2, kTiledPreLong = 3;
 
 
 template <int N, int KS, int RTW, int IT, bool XP = false>
@@ -121,7 +123,7 @@ struct TiledCfg {
                                       : (size_t)XE * 32 + (size_t)N * TNB * 4;
     static constexpr size_t RED = KS > 1 ? (size_t)W * NCG * kWave * 4 : 0;
     static constexpr size_t LDS = TILE > RED ? TILE : RED;
-    static constexpr int PRE = kTiledPre < IT ? kTiledPre : IT;
+    static constexpr int PRE = (KS >= 8 ? kTiledPreLong : kTiledPre) < IT ? (KS >= 8 ? kTiledPreLong : kTiledPre) : IT;
 };
 
 // Position of a lane in the tiled planes: one buffer resource per plane over
