@@ -111,7 +111,7 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs on one GPU only (the MMVQ would shard by output rows "
+        print("bench.py: this benchmark runs on one GPU only (the MMVQ would shard by output rows "
               "across GPUs; no multi-GPU path is built). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
