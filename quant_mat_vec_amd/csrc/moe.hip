@@ -291,6 +291,118 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs m) {
     m.out[(int64_t)t * m.d_model + i] = acc;
 }
 
+// ------------------------------------------------ down + combine, short window
+// For windows of at most kDcMaxS slots (one token at top-8) and planar down
+// weights: a workgroup
+// owns kDcRows rows of d_model and holds one wave per slot position; wave w
+// takes the w-th distinct expert (in order of first slot) and, for the
+// workgroup's rows, forms y for that expert's slots (in passes of two, in
+// ascending slot order) with its activation blocks held in registers -- the
+// Q6_K planar dot product and fp32 scaling of the dense kernel.  After one
+// barrier the workgroup sums out[t] for its rows: the same ascending-k fp32
+// sum as k_moe_combine, without the third launch.  y is also written to the
+// workspace.  Measured per call (E = 128, d_model 2560, d_ff 768): one token
+// 14.0 -> 12.9 us; at two tokens (16 slots) the three-launch chain was
+// faster (19.9 against 21.7 us), hence the limit.
+constexpr int kDcRows = 8;      // rows per workgroup: eight lanes per row, one wave
+constexpr int kDcMaxS = 8;      // slots (and waves) at most
+constexpr int kDcUnits = 3;     // sub-blocks per lane per pass over a row
+
+__global__ __launch_bounds__(kDcMaxS *kWave) void k_moe_down_combine(MoeArgs m) {
+    __shared__ float ylds[kDcMaxS][kDcRows];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x & (kWave - 1);
+    int id = -1;
+    if (lane < m.S) {
+        id = m.ids[lane];
+        if (id < 0 || id >= m.E) id = -1;
+    }
+    const uint64_t valid = __ballot(id >= 0);
+    int pos = 0;                                  // earlier slots of the same expert
+    for (int t = 0; t < m.S; t++) {
+        const int et = __builtin_amdgcn_readlane(id, t);
+        if (et >= 0 && et == id && t < lane) pos++;
+    }
+    const uint64_t fo = __ballot(id >= 0 && pos == 0);   // first slot of each expert
+    const int64_t row0 = (int64_t)blockIdx.x * kDcRows;
+    const int r = lane >> 3, u = lane & 7;
+    const int nsb = (int)(m.d_ff / 32);
+    float *yws = reinterpret_cast<float *>(m.ws + m.off_y);
+    const uint8_t *hq = m.ws + m.off_hq;
+    if (wave < __popcll(fo)) {
+        uint64_t f = fo;
+        for (int k = 0; k < wave; k++) f &= f - 1;
+        const int e = __builtin_amdgcn_readlane(id, (int)__ffsll((long long)f) - 1);
+        uint64_t mm = __ballot(id == e);
+        Q6Planar fmt;
+        fmt.init(m.w_down, (int64_t)m.E * m.d_model, m.d_ff);
+        const int64_t wrow = (int64_t)e * m.d_model + row0 + r;
+        while (mm) {
+            const int s0 = (int)__ffsll((long long)mm) - 1;
+            mm &= mm - 1;
+            const int s1 = mm ? (int)__ffsll((long long)mm) - 1 : -1;
+            if (s1 >= 0) mm &= mm - 1;
+            float a0 = 0.0f, a1 = 0.0f;
+            for (int c = 0; c < nsb; c += 8 * kDcUnits) {
+                Q6Planar::Raw w[kDcUnits];
+                ActRaw x0[kDcUnits], x1[kDcUnits];
+#pragma unroll
+                for (int k = 0; k < kDcUnits; k++) {
+                    const int sb = min(c + u + 8 * k, nsb - 1);
+                    fmt.load(w[k], wrow, sb);
+                    act_load(x0[k], hq, (int64_t)s0 * nsb + sb);
+                    if (s1 >= 0) act_load(x1[k], hq, (int64_t)s1 * nsb + sb);   // wave-uniform
+                }
+#pragma unroll
+                for (int k = 0; k < kDcUnits; k++) {
+                    if (c + u + 8 * k >= nsb) continue;
+                    int v[8];
+                    Q6Planar::codes(w[k], v);
+                    const int sc0 = sext8(w[k].sc, 0), sc1 = sext8(w[k].sc, 1);
+                    const float dw = half_to_float(w[k].d);
+#pragma unroll
+                    for (int n = 0; n < 2; n++) {
+                        if (n == 1 && s1 < 0) break;
+                        const ActRaw &x = n == 0 ? x0[k] : x1[k];
+                        int d0 = sdot4(v[0], (int)x.w[1], 0);
+                        d0 = sdot4(v[1], (int)x.w[2], d0);
+                        d0 = sdot4(v[2], (int)x.w[3], d0);
+                        d0 = sdot4(v[3], (int)x.w[4], d0);
+                        int d1 = sdot4(v[4], (int)x.w[5], 0);
+                        d1 = sdot4(v[5], (int)x.w[6], d1);
+                        d1 = sdot4(v[6], (int)x.w[7], d1);
+                        d1 = sdot4(v[7], (int)x.w[8], d1);
+                        const int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact
+                        const float da = half_to_float(x.w[0]) * 0.25f;
+                        if (n == 0) a0 = __builtin_fmaf(dw * da, (float)isum4, a0);
+                        else a1 = __builtin_fmaf(dw * da, (float)isum4, a1);
+                    }
+                }
+            }
+            a0 = group_sum<8>(a0);
+            a1 = group_sum<8>(a1);
+            if (u == 0) {
+                ylds[s0][r] = a0;
+                yws[(int64_t)s0 * m.d_model + row0 + r] = a0;
+                if (s1 >= 0) {
+                    ylds[s1][r] = a1;
+                    yws[(int64_t)s1 * m.d_model + row0 + r] = a1;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    const int j = threadIdx.x;
+    if (j < m.T * kDcRows) {
+        const int t = j / kDcRows, rr = j % kDcRows;
+        float acc = 0.0f;
+        for (int k = 0; k < m.topk; k++) {
+            const int sl = t * m.topk + k;
+            if ((valid >> sl) & 1) acc = __builtin_fmaf(m.route_w[sl], ylds[sl][rr], acc);
+        }
+        m.out[(int64_t)t * m.d_model + row0 + rr] = acc;
+    }
+}
+
 // ------------------------------------------------------------------ host
 template <int U, bool RAGGED>
 static hipError_t launch_gateup_r(const MoeArgs &m, int smax, hipStream_t s) {
@@ -367,6 +479,11 @@ hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s) {
     // keep the register budget of two waves per SIMD)
     hipError_t err = launch_gateup<8>(m, smax, s);
     if (err != hipSuccess) return err;
+    if (down_layout == 1 && m.S <= kDcMaxS && m.T * kDcRows <= m.S * kWave && m.d_model % kDcRows == 0) {
+        // short window: down and the weighted sum in one launch
+        hipLaunchKernelGGL(k_moe_down_combine, dim3((unsigned)(m.d_model / kDcRows)), dim3(m.S * kWave), 0, s, m);
+        return hipGetLastError();
+    }
     err = down_layout == 1 ? launch_down<Q6Planar>(m, smax, s) : launch_down<Q6Gguf>(m, smax, s);
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(k_moe_combine, dim3((unsigned)((m.d_model + 255) / 256), m.T), dim3(256), 0, s, m);

@@ -343,12 +343,13 @@ def test_moe_staged_parity(moe, T):
     assert rel < 1e-2
 
 
-def test_moe_graph_replay_matches_eager(moe):
+@pytest.mark.parametrize("T", [1, 3])
+def test_moe_graph_replay_matches_eager(moe, T):
     """The routed chain captured in a HIP graph: every replay (workspace and
     output poisoned before it, eager work between replays) gives the eager
-    output and routing tables bit for bit."""
-    note("MoE graph replay T=3")
-    T = 3
+    output and routing tables bit for bit (T = 1: the short-window launch
+    pair; T = 3: the three-launch chain)."""
+    note(f"MoE graph replay T={T}")
     g = synth.rng(synth.seed_for(4, 5, T))
     ids, rw = synth.routing(g, T, E, TOPK)
     xq, _ = quantize(synth.activations(g, T, DM))
@@ -428,11 +429,13 @@ def test_moe_out_of_range_id_is_skipped(moe):
     assert np.abs(out - res["out"]).max() <= 1e-2 * np.abs(res["out"]).max()
 
 
-def test_moe_small_ragged_topk4():
+@pytest.mark.parametrize("T", [2, 3])
+def test_moe_small_ragged_topk4(T):
     """Rows that are not whole register chunks (the ragged kernels) and a
-    routing width of 4: E = 6, d_model = 512, d_ff = 256, T = 3."""
-    note("grouped_expert_mmvq small: E=6 d_model=512 d_ff=256 T=3 topk=4")
-    e_, dm, dff, tk, T = 6, 512, 256, 4, 3
+    routing width of 4: E = 6, d_model = 512, d_ff = 256, T = 2 (eight
+    slots: the short-window down+combine launch) and T = 3."""
+    note(f"grouped_expert_mmvq small: E=6 d_model=512 d_ff=256 T={T} topk=4")
+    e_, dm, dff, tk = 6, 512, 256, 4
     g = synth.rng(730)
     gate, up, down = synth.moe_weights(g, e_, dm, dff)
     ids, rw = synth.routing(g, T, e_, tk)
