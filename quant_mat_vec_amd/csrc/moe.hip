@@ -9,6 +9,8 @@
 //   down    : the same selection, with a row tile of d_model: Q6_K MMVQ over
 //             the expert's requantized slots, y written per slot;
 //   combine : out[t] = sum over k, ascending, of route_w[t][k] * y[t][k].
+// Windows of at most eight slots with planar down weights run down and
+// combine as one launch (k_moe_down_combine, below).
 // The selection is one wave ballot over the slot ids (S <= 64 = one wave),
 // and an expert's slots are taken in ascending slot order.  No workgroup
 // reads the weights of an expert no slot is routed to.
