@@ -208,7 +208,9 @@ int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const 
  * others: QMV_ERR_UNSUPPORTED).
  * idx int32 [ncols], val fp32 [ncols] (4-byte aligned); ws: device
  * workspace of at least mmvq_q6k_argmax_workspace(rows, ncols) bytes,
- * 8-byte aligned, overwritten (one 8-byte key per column and 16-row tile).
+ * 8-byte aligned, overwritten (one 8-byte key per column and 16-row tile,
+ * then 256 bytes of per-column reduction state; calls sharing a workspace
+ * must not overlap).
  * Other arguments and checks as for mmvq_q6k.  Two launches: the product
  * with per-tile maxima, then one reduction per column.  Outputs must be
  * finite. */

@@ -195,7 +195,7 @@ int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const 
 
 size_t mmvq_q6k_argmax_workspace(int64_t rows, int ncols) {
     if (rows <= 0 || rows > kMaxRows || ncols < 1 || ncols > 8) return 0;
-    return (size_t)((((rows + 15) / 16) * ncols * 8 + 255) & ~int64_t(255));
+    return (size_t)(qmv::argmax_tail((rows + 15) / 16, ncols) + 256);
 }
 
 int mmvq_q6k_argmax(const void *w, int layout, const void *xq, int64_t rows, int64_t K, int ncols, int32_t *idx,

@@ -33,6 +33,13 @@ hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int3
 // xp: activations in the column-planar Q8_1 layout
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump,
                                 int64_t rows, int64_t K, int ncols, bool xp, hipStream_t s);
+// The argmax workspace: the keys, keys[n * ntiles + tile], then (256-byte
+// aligned) per column the running maximum key (8 bytes, at most 8 columns)
+// and, 64 bytes further, the count of reduction workgroups done (4 bytes).
+// Both are cleared by the product launch, which runs first.
+__host__ __device__ inline int64_t argmax_tail(int64_t ntiles, int ncols) {
+    return (ntiles * ncols * 8 + 255) & ~(int64_t)255;
+}
 hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
                                        int ncols, int32_t *idx, float *val, bool xp, hipStream_t s);
 hipError_t launch_mmvq_q6_gguf(const void *w, const void *xq, float *out, int32_t *dump,

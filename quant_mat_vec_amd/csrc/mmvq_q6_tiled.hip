@@ -51,7 +51,9 @@ hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *
     const hipError_t e = xp ? tiled_argmax_cols<true>(w, xq, k, rows, K, ncols, s)
                             : tiled_argmax_cols<false>(w, xq, k, rows, K, ncols, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_argmax_reduce, dim3(ncols), dim3(kArgmaxThreads), 0, s, keys, (rows + 15) / 16, idx, val);
+    const int64_t ntiles = (rows + 15) / 16;
+    hipLaunchKernelGGL(k_argmax_reduce, dim3(ncols, (unsigned)((ntiles + kArgmaxSpan - 1) / kArgmaxSpan)),
+                       dim3(kArgmaxThreads), 0, s, keys, ntiles, ncols, idx, val);
     return hipGetLastError();
 }
 }  // namespace qmv

@@ -147,7 +147,7 @@ def test_argmax_rejects(L):
     f = L.mmvq_q6k_argmax
     TL = qmv.LAYOUT_TILED
     nws = L.mmvq_q6k_argmax_workspace(100, 4)
-    assert nws == (7 * 4 * 8 + 255) // 256 * 256
+    assert nws == (7 * 4 * 8 + 255) // 256 * 256 + 256
     assert L.mmvq_q6k_argmax_workspace(0, 4) == 0 and L.mmvq_q6k_argmax_workspace(100, 9) == 0
 
     def call(w=P, lay=TL, xq=P, rows=100, K=512, n=4, idx=P, val=P, ws=P, wsb=nws):
