@@ -349,3 +349,32 @@ def test_planar_activations_argmax(rows, K, ncols):
         qmv.mmvq_q6k_argmax(wt, lay, a, rows, K, ncols, idx, val, ws, nws)
         res.append((host(idx), host(val).view(np.uint32)))
     assert np.array_equal(res[0][0], res[1][0]) and np.array_equal(res[0][1], res[1][1])
+
+
+def test_argmax_graph_replay_poisoned_workspace():
+    """The fused argmax captured in a HIP graph: with the workspace poisoned
+    before every replay (the per-column reduction state included) each
+    replay gives the eager index and value bits."""
+    note("mmvq_q6k_argmax graph replay")
+    rows, K, ncols = 40000, 2560, 4
+    g = synth.rng(1500)
+    wt = tiled(dev(synth.q6k_blocks(g, rows, K)), rows, K)
+    xq, _ = quantize(synth.activations(g, ncols, K))
+    nws = qmv.mmvq_q6k_argmax_workspace(rows, ncols)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    idx = torch.empty(ncols, dtype=torch.int32, device=DEV)
+    val = torch.empty(ncols, dtype=torch.float32, device=DEV)
+    qmv.mmvq_q6k_argmax(wt, TL, xq, rows, K, ncols, idx, val, ws, nws)
+    e_idx, e_val = host(idx).copy(), host(val).view(np.uint32).copy()
+    s = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            qmv.mmvq_q6k_argmax(wt, TL, xq, rows, K, ncols, idx, val, ws, nws, stream=s)
+    for i in range(4):
+        ws.fill_(0xFF)
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx), e_idx) and np.array_equal(host(val).view(np.uint32), e_val), f"replay {i}"
