@@ -369,7 +369,44 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
             ex[f"{kind}_{r_}x{k_}"] = shape_case(kind, r_, k_, (1, 4), seed=15 + r_)
     ex["moe_e128_2560_768"] = moe_case(torch, np, qmv, synth, dev)
     ex["rmsnorm_quantize_13x2560"] = norm_case(torch, np, qmv, synth, dev)
+    ex["q6k_many_columns_mmq"] = {f"{r_}x{k_}": prefill_case(torch, qmv, synth, dev, r_, k_)
+                                  for (r_, k_) in ((10240, 2560), (2560, 10240))}
     return ex
+
+
+def prefill_case(torch, qmv, synth, dev, rows, k, ncols_list=(16, 64, 128, 512)):
+    """The many-column product (mmq_q6k, column-planar activations) on tiled
+    weights rotated over HBM copies: per call, the int8 multiply-adds it
+    computes against the int8 matrix-core peak, and the same columns as
+    decode products of eight columns for context."""
+    XT = qmv.LAYOUT_TILED | qmv.ACT_PLANAR
+    g = synth.rng(synth.seed_for(6, rows % 101, k % 101))
+    w = torch.from_numpy(synth.q6k_blocks(g, rows, k)).to(dev)
+    t0 = torch.empty_like(w)
+    qmv.repack_q6k_tiled(w, t0, rows, k)
+    del w
+    wbytes = weight_bytes(rows, k)
+    cs = [t0] + [t0.clone() for _ in range(max(1, math.ceil(2 * MALL_BYTES / wbytes)))]
+    nmax = max(ncols_list)
+    x = torch.from_numpy(synth.activations(g, nmax, k)).to(dev)
+    q = torch.empty(nmax * (k // 32) * 36, dtype=torch.uint8, device=dev)
+    o = torch.empty(nmax * rows, dtype=torch.float32, device=dev)
+    qmv.quantize_q8_1_planar(x, q, k, nmax)
+    cb = 36 * (k // 32)
+    res = {}
+    for n in ncols_list:
+        us = graph_avg_us(torch, [lambda c=c, n=n: qmv.mmq_q6k(c, XT, q, o, rows, k, n) for c in cs], reps=3)
+        dec = graph_avg_us(torch, [lambda c=c, n=n: [qmv.mmvq_q6k(c, XT, q[i * cb:], o[i * rows:], rows, k,
+                                                                  min(8, n - i)) for i in range(0, n, 8)]
+                                   for c in cs[:8]], reps=2)
+        ops = 2.0 * rows * k * n
+        res[str(n)] = {"avg_call_us": round(us, 3), "int8_TOPs": round(ops / (us * 1e-6) / 1e12, 1),
+                       "frac_of_int8_mfma_peak": round(ops / (us * 1e-6) / 5.0e15, 4),
+                       "weight_GBps": round(wbytes / (us * 1e-6) / 1e9, 1),
+                       "as_8col_decode_products_us": round(dec, 3)}
+    del cs
+    torch.cuda.empty_cache()
+    return res
 
 
 def norm_case(torch, np, qmv, synth, dev):

@@ -167,6 +167,16 @@ int rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *x
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out,
              int64_t rows, int64_t K, int ncols, void *stream);
 
+/* The same Q6_K x Q8_1 product for many columns at once (the prompt path,
+ * which PR #2340 "What it changes" leaves as it is; the arithmetic is the
+ * decode product's).  Tiled weights only: layout = QMV_LAYOUT_TILED,
+ * optionally | QMV_ACT_PLANAR, with w, xq, out as for mmvq_q6k, and
+ * 1 <= ncols <= 65535.  Every output column is bit-for-bit what mmvq_q6k
+ * gives for that column alone.  QMV_ERR_UNSUPPORTED also when
+ * (ceil(rows/16) + 32) * ceil(ncols/12) >= 2^22. */
+int mmq_q6k(const void *w, int layout, const void *xq, float *out,
+            int64_t rows, int64_t K, int ncols, void *stream);
+
 /* Q4_K / Q5_K weights (GGUF blocks, 16-byte aligned; 144 and 176 B blocks
  * keep every field aligned, so no planar form is needed) x Q8_1 activations
  * (PR #2340 "What it changes" and PR #2207 "How it was checked" measure

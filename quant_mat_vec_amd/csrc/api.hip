@@ -26,11 +26,11 @@ hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Checks shared by the MMVQ entry points.
 int check_mmvq(const void *w, const void *xq, const void *out, int64_t rows, int64_t K, int ncols,
-               int64_t block_bytes, uintptr_t w_align) {
+               int64_t block_bytes, uintptr_t w_align, int max_cols = 8) {
     if (!w || !xq || !out) return QMV_ERR_INVALID_ARG;
     if (rows <= 0 || K <= 0) return QMV_ERR_INVALID_ARG;
     if (K % 256 != 0 || K > kMaxK || rows > kMaxRows) return QMV_ERR_UNSUPPORTED;
-    if (ncols < 1 || ncols > 8) return QMV_ERR_UNSUPPORTED;
+    if (ncols < 1 || ncols > max_cols) return QMV_ERR_UNSUPPORTED;
     if (rows * (K / 256) * block_bytes >= kMaxBytes || rows * ncols * 4 >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
     if (!aligned(w, w_align) || !aligned(xq, 4) || !aligned(out, 4)) return QMV_ERR_ALIGNMENT;
     return QMV_OK;
@@ -118,6 +118,22 @@ int mmvq_q6k(const void *w, int layout, const void *xq, float *out, int64_t rows
              void *stream) {
     if (!out) return QMV_ERR_INVALID_ARG;
     return q6_dispatch(w, layout, xq, out, nullptr, rows, K, ncols, stream);
+}
+
+int mmq_q6k(const void *w, int layout, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
+            void *stream) {
+    if (!out) return QMV_ERR_INVALID_ARG;
+    const bool xp = (layout & QMV_ACT_PLANAR) != 0;
+    if ((layout & ~QMV_ACT_PLANAR) != QMV_LAYOUT_TILED) {
+        if (!w || !xq) return QMV_ERR_INVALID_ARG;
+        return QMV_ERR_UNSUPPORTED;
+    }
+    int rc = check_mmvq(w, xq, out, rows, K, ncols, 210, 16, 65535);
+    if (rc) return rc;
+    // the batched launch's grid stays under 2^32 threads
+    if (((rows + 15) / 16 + 32) * ((ncols + 11) / 12) >= (1LL << 22)) return QMV_ERR_UNSUPPORTED;
+    if (xp && !aligned(xq, 16)) return QMV_ERR_ALIGNMENT;
+    return from_hip(qmv::launch_mmq_q6_tiled(w, xq, out, rows, K, ncols, xp, as_stream(stream)));
 }
 
 int mmvq_q4k(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols, void *stream) {

@@ -644,8 +644,11 @@ struct MmvqArgs {
 };
 
 // First Q8_1 block of column n.
+// (more than eight columns: only the batched tiled product, whose columns
+// are consecutive)
 template <int N>
 __device__ __forceinline__ int64_t xcol_of(const MmvqArgs &a, int n) {
+    if constexpr (N > 8) return (int64_t)n * a.xstride;
     return (int64_t)((a.colpack >> (8 * n)) & 255u) * a.xstride;
 }
 

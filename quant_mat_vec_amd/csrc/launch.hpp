@@ -33,6 +33,9 @@ hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int3
 // xp: activations in the column-planar Q8_1 layout
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump,
                                 int64_t rows, int64_t K, int ncols, bool xp, hipStream_t s);
+// any number of columns (batches of twelve or sixteen, then at most eight)
+hipError_t launch_mmq_q6_tiled(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
+                               bool xp, hipStream_t s);
 // The argmax workspace: the keys, keys[n * ntiles + tile], then (256-byte
 // aligned) per column the running maximum key (8 bytes, at most 8 columns)
 // and, 64 bytes further, the count of reduction workgroups done (4 bytes).

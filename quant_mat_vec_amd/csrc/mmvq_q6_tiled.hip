@@ -27,6 +27,28 @@ hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32
                 : tiled_cols<false, false>(w, xq, out, dump, rows, K, ncols, s);
 }
 
+// Batched product of any number of columns: full batches in one launch,
+// the rest (fewer than a batch) as products of at most eight columns.
+hipError_t launch_mmq_q6_tiled(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
+                               bool xp, hipStream_t s) {
+    const int B = tiled_batch_cols(K);
+    const int64_t nbat = ncols / B, cstride = 36 * (K / 32);
+    if (nbat > 0) {
+        const hipError_t e = xp ? launch_tiled_batched<true>(w, xq, out, rows, K, nbat, s)
+                                : launch_tiled_batched<false>(w, xq, out, rows, K, nbat, s);
+        if (e != hipSuccess) return e;
+    }
+    for (int n0 = (int)nbat * B; n0 < ncols; n0 += 8) {
+        const int n = ncols - n0 < 8 ? ncols - n0 : 8;
+        const void *x = static_cast<const uint8_t *>(xq) + n0 * cstride;
+        float *o = out + n0 * rows;
+        const hipError_t e = xp ? tiled_cols<false, true>(w, x, o, nullptr, rows, K, n, s)
+                                : tiled_cols<false, false>(w, x, o, nullptr, rows, K, n, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 // Fused greedy argmax: the product's per-tile column maxima into keys, then
 // one reduction launch.
 template <bool XP>

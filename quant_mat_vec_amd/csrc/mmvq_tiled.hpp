@@ -36,7 +36,8 @@ typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 // Cache-policy bit of a buffer load: non-temporal.  The code planes are read
 // once per product, so they are streamed past the caches (measured ~0.1 us
 // faster per launch at eight columns than the default policy); the scales
-// and d keep the default.
+// and d keep the default.  (The batched product, which reads each row
+// tile's planes once per batch, measured the same with the default policy.)
 constexpr int kNonTemporal = 2;
 
 // Buffer resource for `bytes` bytes at `base` (raw, unformatted dword
@@ -412,10 +413,19 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
 // AMAX: instead of the outputs, each row tile writes, per column n, the
 // largest argmax_key over its rows to keys[n * ntiles + tile] (out is then
 // a uint64 array of N * ceil(rows/16) keys).
+//
+// More than eight columns (N = 12 or 16): the batched product.  The grid
+// covers every row workgroup once per batch of N consecutive columns, and
+// workgroup b takes batch (b/8) % nbat of row workgroup 8*((b/8)/nbat) +
+// b%8: workgroups are handed to the eight XCDs in turn, so the batches of
+// one row workgroup run on one XCD close together in time and read its
+// weights from that XCD's L2 after the first.  Every column goes through the
+// same arithmetic as in a product of eight or fewer columns.
 template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false, bool XP = false>
 __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
                                                                     float *__restrict__ out) {
     using C = TiledCfg<N, KS, RTW, IT, XP>;
+    static_assert(N <= 8 || (!DUMP && !AMAX), "batched products write outputs only");
     extern __shared__ __align__(16) uint8_t lds[];
     Q6Tiled f;
     f.init(w, a.rows, a.K);
@@ -425,6 +435,16 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
     // the wave's tile and the lane's row; lanes past the last row load from a
     // row that exists and store nothing
     const int64_t ntiles = (a.rows + 15) / 16;
+    int64_t wg = blockIdx.x;
+    if constexpr (N > 8) {
+        const int64_t nrw = (ntiles + RTW - 1) / RTW, g8 = (nrw + 7) / 8;
+        const int64_t nbat = gridDim.x / (8 * g8), j = blockIdx.x >> 3;
+        const int64_t cb = j % nbat;
+        wg = (j / nbat) * 8 + (blockIdx.x & 7);
+        if (wg >= nrw) return;                              // the whole workgroup
+        a.xq += cb * N * 36 * (a.K / 32);
+        out += cb * N * a.rows;
+    }
     if constexpr (AMAX) {
         // clear the reduction's running maxima and counts (k_argmax_reduce)
         if (blockIdx.x == 0 && tid < N) {
@@ -433,7 +453,7 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
             reinterpret_cast<uint32_t *>(tail + 64)[tid] = 0;
         }
     }
-    const int64_t tile = (int64_t)blockIdx.x * RTW + rt, tc = min(tile, ntiles - 1);
+    const int64_t tile = wg * RTW + rt, tc = min(tile, ntiles - 1);
     const int R = (int)min((int64_t)16, a.rows - 16 * tc);
     const int r = l & 15, rr = min(r, R - 1), kg = l >> 4;
     const int64_t row = 16 * tile + r;
@@ -562,9 +582,10 @@ __global__ __launch_bounds__(kArgmaxThreads) void k_argmax_reduce(uint64_t *__re
     }
 }
 
+// nbat: batches of N columns (N > 8 only)
 template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false, bool XP = false>
 hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                            hipStream_t s) {
+                            hipStream_t s, int64_t nbat = 1) {
     using C = TiledCfg<N, KS, RTW, IT, XP>;
     MmvqArgs a;
     a.xq = reinterpret_cast<const uint8_t *>(xq);
@@ -575,7 +596,9 @@ hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *
     a.xstride = K / 32;
     a.its = IT;
     const int64_t tiles = (rows + 15) / 16;
-    const int64_t grid = (tiles + RTW - 1) / RTW;
+    int64_t grid = (tiles + RTW - 1) / RTW;
+    if constexpr (N > 8) grid = 8 * ((grid + 7) / 8) * nbat;
+    if (grid * C::NTHR > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX, XP>), C::LDS);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_mmvq_q6_tiled<N, KS, RTW, IT, DUMP, AMAX, XP>), dim3((unsigned)grid), dim3(C::NTHR), C::LDS,
@@ -595,6 +618,25 @@ hipError_t launch_tiled_n(const void *w, const void *xq, float *out, int32_t *du
     if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
     if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
     return launch_tiled_cfg<N, 16, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
+}
+
+// Columns per batch of the batched product: sixteen, twelve with sixteen
+// waves along K (sixteen columns of that chunk do not fit the 160 KB of LDS).
+inline int tiled_batch_cols(int64_t K) { return (K / 128 + 4) / 5 > 8 ? 12 : 16; }
+
+// nbat batches of tiled_batch_cols(K) columns, with the waves along K that
+// launch_tiled_n takes for the same K (so the same sums in the same order).
+// (Twice the row tiles per workgroup, staging each activation tile for
+// twice the rows, measured within +-10 % either way.)
+template <bool XP>
+hipError_t launch_tiled_batched(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int64_t nbat,
+                                hipStream_t s) {
+    const int64_t need = (K / 128 + 4) / 5;
+    if (need <= 1) return launch_tiled_cfg<16, 1, 4, 5, false, false, XP>(w, xq, out, nullptr, rows, K, s, nbat);
+    if (need <= 2) return launch_tiled_cfg<16, 2, 2, 5, false, false, XP>(w, xq, out, nullptr, rows, K, s, nbat);
+    if (need <= 4) return launch_tiled_cfg<16, 4, 1, 5, false, false, XP>(w, xq, out, nullptr, rows, K, s, nbat);
+    if (need <= 8) return launch_tiled_cfg<16, 8, 1, 5, false, false, XP>(w, xq, out, nullptr, rows, K, s, nbat);
+    return launch_tiled_cfg<12, 16, 1, 5, false, false, XP>(w, xq, out, nullptr, rows, K, s, nbat);
 }
 
 }  // namespace qmv

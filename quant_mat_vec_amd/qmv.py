@@ -45,6 +45,7 @@ def lib() -> ctypes.CDLL:
             "quantize_q8_1_planar": [P, P, I64, I, P],
             "rmsnorm_quantize_q8_1": [P, P, ctypes.c_float, P, I64, I, I, P],
             "mmvq_q6k": [P, I, P, P, I64, I64, I, P],
+            "mmq_q6k": [P, I, P, P, I64, I64, I, P],
             "mmvq_q4k": [P, P, P, I64, I64, I, P],
             "mmvq_q5k": [P, P, P, I64, I64, I, P],
             "repack_q6k_planar": [P, P, I64, I64, P],
@@ -131,6 +132,10 @@ def rmsnorm_quantize_q8_1(x, gamma, eps: float, xq, K: int, ncols: int, act_layo
 def mmvq_q6k(w, layout: int, xq, out, rows: int, K: int, ncols: int, stream=None) -> None:
     _check(lib().mmvq_q6k(_ptr(w), layout, _ptr(xq), _ptr(out), rows, K, ncols, _stream(stream)),
            "mmvq_q6k")
+
+
+def mmq_q6k(w, layout: int, xq, out, rows: int, K: int, ncols: int, stream=None) -> None:
+    _check(lib().mmq_q6k(_ptr(w), layout, _ptr(xq), _ptr(out), rows, K, ncols, _stream(stream)), "mmq_q6k")
 
 
 def mmvq_q4k(w, xq, out, rows: int, K: int, ncols: int, stream=None) -> None:

@@ -23,7 +23,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = qmv.declared_symbols()
-    expected = {"quantize_q8_1", "quantize_q8_1_planar", "rmsnorm_quantize_q8_1", "mmvq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
+    expected = {"quantize_q8_1", "quantize_q8_1_planar", "rmsnorm_quantize_q8_1", "mmvq_q6k", "mmq_q6k", "mmvq_q4k", "mmvq_q5k", "repack_q6k_planar",
                 "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "gather_q6k_rows", "mmvq_q6k_argmax", "mmvq_q6k_argmax_workspace",
                 "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
@@ -67,6 +67,25 @@ def test_rmsnorm_quantize_rejects(L):
     assert call(K=100) == E_UNS and call(K=(1 << 20) + 32) == E_UNS and call(n=65536) == E_UNS
     assert call(lay=1) == E_UNS and call(lay=qmv.LAYOUT_TILED | qmv.ACT_PLANAR) == E_UNS
     assert call(x=P + 4) == E_ALN and call(g=P + 8) == E_ALN and call(xq=P + 2) == E_ALN
+
+
+def test_mmq_rejects(L):
+    T, XT = qmv.LAYOUT_TILED, qmv.LAYOUT_TILED | qmv.ACT_PLANAR
+
+    def call(w=P, xq=P, out=P, rows=16, K=512, ncols=1, layout=T):
+        return L.mmq_q6k(w, layout, xq, out, rows, K, ncols, None)
+
+    assert call(w=None) == E_INV and call(xq=None) == E_INV and call(out=None) == E_INV
+    assert call(rows=0) == E_INV and call(K=0) == E_INV
+    assert call(K=300) == E_UNS and call(K=1 << 21) == E_UNS and call(rows=1 << 31) == E_UNS
+    assert call(ncols=0) == E_UNS and call(ncols=65536) == E_UNS
+    # tiled weights only
+    for lay in (qmv.LAYOUT_GGUF, qmv.LAYOUT_PLANAR, qmv.LAYOUT_PLANAR | qmv.ACT_PLANAR, 3, -1):
+        assert call(layout=lay) == E_UNS, lay
+    # the grid bound: (ceil(rows/16) + 32) * ceil(ncols/12) < 2^22
+    assert call(rows=16 * ((1 << 22) // 12 - 32), ncols=12 * 13) == E_UNS
+    assert call(w=P + 8) == E_ALN and call(xq=P + 2) == E_ALN and call(out=P + 2) == E_ALN
+    assert call(layout=XT, xq=P + 4) == E_ALN and call(layout=XT, xq=P + 8) == E_ALN
 
 
 @pytest.mark.parametrize("name", ["mmvq_q6k", "mmvq_q4k", "mmvq_q5k",
