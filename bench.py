@@ -38,7 +38,7 @@ ROWS, K = 10240, 2560
 # FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on a
 # plain copy of known size (FETCH_SIZE x 1.9977, WRITE_SIZE x 1.0); to be
 # emptied whenever the kernel changes after the counters were taken.
-TRAFFIC = {1: 21660350, 4: 21857725, 8: 22143280}
+TRAFFIC = {1: 21671337, 4: 21862779, 8: 22143220}
 NCOLS = (1, 4, 8)
 XCOLS = sum(NCOLS)          # distinct activation columns quantized per step
 COL0 = {1: 0, 4: 1, 8: 5}   # first activation column of each product
@@ -71,6 +71,9 @@ def parse():
     p.add_argument("--pmc-workload", action="store_true",
                    help="only run 30 launches each of the N=1/4/8 products and of a 21.5 MB device "
                         "copy (for rocprofv3 --pmc passes), print nothing")
+    p.add_argument("--pmc-mmq", action="store_true",
+                   help="only run 8 launches of the 512-column product mmq_q6k on the same matrix "
+                        "(for rocprofv3 --pmc passes), print nothing")
     return p.parse_args()
 
 
@@ -148,6 +151,17 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
+
+    if args.pmc_mmq:
+        n = 512
+        xm = torch.from_numpy(synth.activations(g, n, K)).to(dev)
+        qm = torch.empty(n * qcol, dtype=torch.uint8, device=dev)
+        om = torch.empty(n * ROWS, dtype=torch.float32, device=dev)
+        qmv.quantize_q8_1_planar(xm, qm, K, n)
+        for i in range(8):
+            qmv.mmq_q6k(copies[i % ncopies], XT, qm, om, ROWS, K, n)
+        torch.cuda.synchronize()
+        return
 
     if args.pmc_workload:
         # fixed workload for hardware-counter passes: the three products on

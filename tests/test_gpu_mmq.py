@@ -82,6 +82,28 @@ def test_mmq_vs_oracle_and_decode(rows, K, ncols):
     assert np.array_equal(gp.view(np.uint32), got.view(np.uint32))
 
 
+# edge cases: one column (no batch), exactly one batch, a one-row matrix,
+# and the most columns the entry point takes (4095 batches + 15 columns)
+EDGE = [(300, 2560, 1), (5, 512, 16), (1, 256, 17), (16, 256, 65535)]
+
+
+@pytest.mark.parametrize("rows,K,ncols", EDGE)
+def test_mmq_edge_cases(rows, K, ncols):
+    note(f"mmq_q6k edge rows={rows} K={K} ncols={ncols}")
+    g = synth.rng(1330 + rows + ncols)
+    w = synth.q6k_blocks(g, rows, K)
+    xq, xq_np = quantize(synth.activations(g, ncols, K))
+    wt = tiled(dev(w), rows, K)
+    got = mmq(wt, xq, rows, K, ncols)
+    ref, ab = orc.mmvq("q6k", w, xq_np, rows, K)
+    assert_close(got, ref, ab, f"mmq {rows}x{K} N={ncols}")
+    cs = sorted(set(g.choice(ncols, size=min(24, ncols), replace=False).tolist()) | {0, ncols - 1})
+    nb = K // 32 * 36
+    for c in cs:
+        one = mmvq("q6k", wt, xq[c * nb:(c + 1) * nb], rows, K, 1, TL)
+        assert np.array_equal(one[0].view(np.uint32), got[c].view(np.uint32)), c
+
+
 def test_mmq_exact_arithmetic_bitexact():
     """Inputs whose every fp32 product and partial sum is exact: the
     batched product must return the oracle's value exactly."""
