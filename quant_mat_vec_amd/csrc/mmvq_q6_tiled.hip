@@ -1,4 +1,5 @@
 // mmvq_q6_tiled.hip -- instantiations of the tiled-layout Q6_K MMVQ.
+#include "mmq_tiled.hpp"
 #include "mmvq_tiled.hpp"
 
 namespace qmv {
@@ -34,8 +35,11 @@ hipError_t launch_mmq_q6_tiled(const void *w, const void *xq, float *out, int64_
     const int B = tiled_batch_cols(K);
     const int64_t nbat = ncols / B, cstride = 36 * (K / 32);
     if (nbat > 0) {
-        const hipError_t e = xp ? launch_tiled_batched<true>(w, xq, out, rows, K, nbat, s)
-                                : launch_tiled_batched<false>(w, xq, out, rows, K, nbat, s);
+        // weights held across batches where K is one whole chunk (column-
+        // planar activations); else one workgroup per (row tiles, batch)
+        const hipError_t e = xp && mmq_ws_batch_cols(K, nbat) == B ? launch_mmq_ws(w, xq, out, rows, K, (int)nbat, s)
+                             : xp                           ? launch_tiled_batched<true>(w, xq, out, rows, K, nbat, s)
+                                                            : launch_tiled_batched<false>(w, xq, out, rows, K, nbat, s);
         if (e != hipSuccess) return e;
     }
     for (int n0 = (int)nbat * B; n0 < ncols; n0 += 8) {

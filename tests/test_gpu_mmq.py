@@ -7,7 +7,8 @@ column bit-for-bit equal to the decode product (mmvq_q6k, at most eight
 columns) of the same column; column-planar activations bit-for-bit equal to
 Q8_1 blocks.  The shapes take every batch width and launch shape (16
 columns with 1, 2, 4 and 8 waves along K, 12 columns with 16 waves, one and
-two chunks per row) with ragged rests of 1 to 11 columns after the batches.
+two chunks per row; the weights-stationary launch with full and partial
+groups of batches) with ragged rests of 1 to 13 columns after the batches.
 """
 import numpy as np
 import pytest
@@ -61,9 +62,12 @@ def rows_of(w, rs, K):
 
 # (rows, K, ncols): K = 512 one wave along K (two batches + 1), 768 two
 # waves (1 + 3), 2560 four (2 + 8, 3 + 0), 5120 eight (1 + 0, 1 + 11),
-# 10240 sixteen at twelve columns (2 + 5), 20480 two chunks (2 + 1)
+# 10240 sixteen at twelve columns (2 + 5), 20480 two chunks (2 + 1); from
+# eight batches on, K = 2560 and 5120 take the launch that holds the
+# weights across four batches per workgroup: 8 + 13 (two groups), 9 + 6
+# (a last group of one batch), 12 + 8 (three groups)
 SMALL = [(70, 512, 33), (37, 768, 19), (19, 2560, 40), (130, 2560, 48), (40, 5120, 16), (23, 5120, 27),
-         (9, 10240, 29), (17, 20480, 25)]
+         (9, 10240, 29), (17, 20480, 25), (19, 2560, 141), (21, 2560, 150), (40, 5120, 200)]
 
 
 @pytest.mark.parametrize("rows,K,ncols", SMALL)
@@ -120,7 +124,7 @@ def test_mmq_exact_arithmetic_bitexact():
 # full sizes: the decode matrices at prompt widths, the LM head, and
 # partial last row tiles / row workgroups (32805 x 256, 4100 x 1280)
 FULL = [(10240, 2560, 512), (10240, 2560, 70), (2560, 10240, 100), (151936, 2560, 20), (32805, 256, 45),
-        (4100, 1280, 17), (3000, 5120, 40), (8200, 20480, 13)]
+        (4100, 1280, 17), (3000, 5120, 40), (3000, 5120, 130), (8200, 20480, 13)]
 
 
 @pytest.mark.parametrize("rows,K,ncols", FULL)
@@ -143,7 +147,7 @@ def test_mmq_full_size_sampled(rows, K, ncols):
 
 def test_mmq_graph_replay_matches_eager():
     note("graph capture of quantize_q8_1_planar + mmq_q6k")
-    rows, K, ncols = 2048, 2560, 37
+    rows, K, ncols = 2048, 2560, 137
     g = synth.rng(1320)
     w = tiled(dev(synth.q6k_blocks(g, rows, K)), rows, K)
     x = dev(synth.activations(g, ncols, K))
