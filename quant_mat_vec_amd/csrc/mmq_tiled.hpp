@@ -18,12 +18,21 @@
 
 namespace qmv {
 
-// Batches of columns per workgroup (measured at 512 columns of 10240x2560:
-// two 145 us, four 127 us, eight 123 us but slower from 128 to 256
-// columns), and the fewest batches for which this launch is taken (below
-// it, the one-batch-per-workgroup launch is as fast or faster: 16 columns
-// 9.6 against 10.6 us).
-constexpr int kMmqBatchesPerWg = 4, kMmqMinBatches = 8;
+// Columns per batch, batches per workgroup and the fewest batches for which
+// this launch is taken (128 columns; below that the one-batch-per-workgroup
+// launch is as fast or faster: 16 columns 9.6 against 10.6 us).  Measured
+// at 512 columns, 10240x2560 / 3000x5120: 8 x 8 116 / 76 us, 8 x 4 121 /
+// 78 us, 16 x 4 119 / 92 us, 16 x 8 123 us, 16 x 2 145 us; the same bits
+// whatever the split.  Eight-column batches halve the LDS tile and the
+// staging registers (121 VGPRs: four waves per SIMD).
+#ifndef QMV_MMQ_B
+#define QMV_MMQ_B 8
+#endif
+#ifndef QMV_MMQ_BPW
+#define QMV_MMQ_BPW 8
+#endif
+constexpr int kMmqB = QMV_MMQ_B;
+constexpr int kMmqBatchesPerWg = QMV_MMQ_BPW, kMmqMinBatches = 128 / QMV_MMQ_B;
 
 template <int B, int KS, int IT>
 struct MmqCfg {
@@ -228,14 +237,14 @@ hipError_t launch_mmq_ws_cfg(const void *w, const void *xq, float *out, int64_t 
 // use the batched tiled launch).  The
 // same waves along K as launch_tiled_n, so the same sums.  (Sixteen waves,
 // K = 10240, would have 128 VGPRs per lane and spill.)
-inline int mmq_ws_batch_cols(int64_t K, int64_t nbat) {
-    return (K == 128 * 4 * 5 || K == 128 * 8 * 5) && nbat >= kMmqMinBatches ? 16 : 0;
+inline int mmq_ws_batch_cols(int64_t K, int64_t ncols) {
+    return (K == 128 * 4 * 5 || K == 128 * 8 * 5) && ncols / kMmqB >= kMmqMinBatches ? kMmqB : 0;
 }
 
 inline hipError_t launch_mmq_ws(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int nbat,
                                 hipStream_t s) {
-    if (K == 128 * 4 * 5) return launch_mmq_ws_cfg<16, 4, 5>(w, xq, out, rows, K, nbat, s);
-    return launch_mmq_ws_cfg<16, 8, 5>(w, xq, out, rows, K, nbat, s);
+    if (K == 128 * 4 * 5) return launch_mmq_ws_cfg<kMmqB, 4, 5>(w, xq, out, rows, K, nbat, s);
+    return launch_mmq_ws_cfg<kMmqB, 8, 5>(w, xq, out, rows, K, nbat, s);
 }
 
 }  // namespace qmv

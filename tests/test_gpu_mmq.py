@@ -63,9 +63,9 @@ def rows_of(w, rs, K):
 # (rows, K, ncols): K = 512 one wave along K (two batches + 1), 768 two
 # waves (1 + 3), 2560 four (2 + 8, 3 + 0), 5120 eight (1 + 0, 1 + 11),
 # 10240 sixteen at twelve columns (2 + 5), 20480 two chunks (2 + 1); from
-# eight batches on, K = 2560 and 5120 take the launch that holds the
-# weights across four batches per workgroup: 8 + 13 (two groups), 9 + 6
-# (a last group of one batch), 12 + 8 (three groups)
+# 128 columns on, K = 2560 and 5120 take the launch that holds the weights
+# across eight batches of eight columns per workgroup: 17 batches + 5
+# (groups of 8, 8, 1), 18 + 6 (8, 8, 2), 25 + 0 (8, 8, 8, 1)
 SMALL = [(70, 512, 33), (37, 768, 19), (19, 2560, 40), (130, 2560, 48), (40, 5120, 16), (23, 5120, 27),
          (9, 10240, 29), (17, 20480, 25), (19, 2560, 141), (21, 2560, 150), (40, 5120, 200)]
 
