@@ -232,19 +232,20 @@ hipError_t launch_mmq_ws_cfg(const void *w, const void *xq, float *out, int64_t 
     return hipGetLastError();
 }
 
-// The batch width of the weights-stationary launch for K and nbat batches
-// (0: K is not one whole chunk of four or eight waves, or too few batches;
-// use the batched tiled launch).  The
-// same waves along K as launch_tiled_n, so the same sums.  (Sixteen waves,
-// K = 10240, would have 128 VGPRs per lane and spill.)
+// The batch width of the weights-stationary launch for K and ncols (0: K
+// is not one whole chunk of four, eight or sixteen waves, or too few
+// columns; use the batched tiled launch).  The same waves along K as
+// launch_tiled_n, so the same sums.
 inline int mmq_ws_batch_cols(int64_t K, int64_t ncols) {
-    return (K == 128 * 4 * 5 || K == 128 * 8 * 5) && ncols / kMmqB >= kMmqMinBatches ? kMmqB : 0;
+    return (K == 128 * 4 * 5 || K == 128 * 8 * 5 || K == 128 * 16 * 5) && ncols / kMmqB >= kMmqMinBatches ? kMmqB
+                                                                                                         : 0;
 }
 
 inline hipError_t launch_mmq_ws(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int nbat,
                                 hipStream_t s) {
     if (K == 128 * 4 * 5) return launch_mmq_ws_cfg<kMmqB, 4, 5>(w, xq, out, rows, K, nbat, s);
-    return launch_mmq_ws_cfg<kMmqB, 8, 5>(w, xq, out, rows, K, nbat, s);
+    if (K == 128 * 8 * 5) return launch_mmq_ws_cfg<kMmqB, 8, 5>(w, xq, out, rows, K, nbat, s);
+    return launch_mmq_ws_cfg<kMmqB, 16, 5>(w, xq, out, rows, K, nbat, s);
 }
 
 }  // namespace qmv

@@ -65,9 +65,10 @@ def rows_of(w, rs, K):
 # 10240 sixteen at twelve columns (2 + 5), 20480 two chunks (2 + 1); from
 # 128 columns on, K = 2560 and 5120 take the launch that holds the weights
 # across eight batches of eight columns per workgroup: 17 batches + 5
-# (groups of 8, 8, 1), 18 + 6 (8, 8, 2), 25 + 0 (8, 8, 8, 1)
+# (groups of 8, 8, 1), 18 + 6 (8, 8, 2), 25 + 0 (8, 8, 8, 1); K = 10240
+# (sixteen waves) 16 + 2 (8, 8)
 SMALL = [(70, 512, 33), (37, 768, 19), (19, 2560, 40), (130, 2560, 48), (40, 5120, 16), (23, 5120, 27),
-         (9, 10240, 29), (17, 20480, 25), (19, 2560, 141), (21, 2560, 150), (40, 5120, 200)]
+         (9, 10240, 29), (17, 20480, 25), (19, 2560, 141), (21, 2560, 150), (40, 5120, 200), (9, 10240, 130)]
 
 
 @pytest.mark.parametrize("rows,K,ncols", SMALL)
@@ -124,7 +125,7 @@ def test_mmq_exact_arithmetic_bitexact():
 # full sizes: the decode matrices at prompt widths, the LM head, and
 # partial last row tiles / row workgroups (32805 x 256, 4100 x 1280)
 FULL = [(10240, 2560, 512), (10240, 2560, 70), (2560, 10240, 100), (151936, 2560, 20), (32805, 256, 45),
-        (4100, 1280, 17), (3000, 5120, 40), (3000, 5120, 130), (8200, 20480, 13)]
+        (4100, 1280, 17), (3000, 5120, 40), (3000, 5120, 130), (2560, 10240, 136), (8200, 20480, 13)]
 
 
 @pytest.mark.parametrize("rows,K,ncols", FULL)
