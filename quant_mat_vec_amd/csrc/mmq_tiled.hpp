@@ -22,8 +22,9 @@ namespace qmv {
 // this launch is taken (128 columns; below that the one-batch-per-workgroup
 // launch is as fast or faster: 16 columns 9.6 against 10.6 us).  Measured
 // at 512 columns, 10240x2560 / 3000x5120: 8 x 8 116 / 76 us, 8 x 4 121 /
-// 78 us, 16 x 4 119 / 92 us, 16 x 8 123 us, 16 x 2 145 us; the same bits
-// whatever the split.  Eight-column batches halve the LDS tile and the
+// 78 us, 16 x 4 119 / 92 us, 16 x 8 123 us, 16 x 2 145 us, 8 x 16 115 /
+// 76 us but slower from 128 to 256 columns and on 2560x10240 (169 against
+// 151 us: too few workgroups); the same bits whatever the split.  Eight-column batches halve the LDS tile and the
 // staging registers (121 VGPRs: four waves per SIMD).
 #ifndef QMV_MMQ_B
 #define QMV_MMQ_B 8
