@@ -32,13 +32,14 @@ hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32
 // the rest (fewer than a batch) as products of at most eight columns.
 hipError_t launch_mmq_q6_tiled(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
                                bool xp, hipStream_t s) {
-    // weights held across batches where K is one whole chunk (column-planar
-    // activations, enough columns); else one workgroup per (row tiles, batch)
-    const int BW = xp ? mmq_ws_batch_cols(K, ncols) : 0;
+    // weights held across batches where K is one whole chunk and there are
+    // enough columns; else one workgroup per (row tiles, batch)
+    const int BW = mmq_ws_batch_cols(K, ncols, xp);
     const int B = BW ? BW : tiled_batch_cols(K);
     const int64_t nbat = ncols / B, cstride = 36 * (K / 32);
     if (nbat > 0) {
-        const hipError_t e = BW ? launch_mmq_ws(w, xq, out, rows, K, (int)nbat, s)
+        const hipError_t e = BW ? (xp ? launch_mmq_ws<true>(w, xq, out, rows, K, (int)nbat, s)
+                                      : launch_mmq_ws<false>(w, xq, out, rows, K, (int)nbat, s))
                              : xp ? launch_tiled_batched<true>(w, xq, out, rows, K, nbat, s)
                                   : launch_tiled_batched<false>(w, xq, out, rows, K, nbat, s);
         if (e != hipSuccess) return e;
