@@ -306,6 +306,207 @@ def test_q8_1_scale_and_sign_symmetry():
     assert np.array_equal(a[..., 0:2], c[..., 0:2])
 
 
+# ------------------------------------------ Q8_1 vs an independent numpy quantizer
+def numpy_q8_1(x, mode="div32"):
+    """Q8_1 written here from the quantizer reading, with numpy's IEEE fp32
+    arithmetic: amax = max|x|, d = amax/127 (fp32 division), q =
+    round-half-away-from-zero(x/d) with x/d an fp32 division, clamped to
+    +-127 (all zero when d == 0), stored d = fp16(d), s = fp16(d * sum q)
+    (fp32 product), both rounded to nearest even by numpy's cast.  `mode`
+    selects a deliberately wrong variant to show that the fixtures below tell
+    them apart: "recip" (x times the fp32 reciprocal of d), "div64" (x/d in
+    fp64) and "even" (ties to even)."""
+    x = np.ascontiguousarray(x, np.float32)
+    ncols, K = x.shape
+    xb = x.reshape(ncols, K // 32, 32)
+    amax = np.abs(xb).max(-1)
+    d = amax / np.float32(127)
+    assert d.dtype == np.float32
+    dz = np.where(d > 0, d, np.float32(1))[..., None]
+    if mode == "recip":
+        v = (xb * (np.float32(1) / dz)).astype(np.float64)
+    elif mode == "div64":
+        v = xb.astype(np.float64) / dz.astype(np.float64)
+    else:
+        v = (xb / dz).astype(np.float64)
+    if mode == "even":
+        q = np.rint(v)
+    else:
+        q = np.sign(v) * np.floor(np.abs(v) + 0.5)       # exact in fp64
+    q = np.clip(q, -127, 127)
+    q[d == 0] = 0
+    q = q.astype(np.int8)
+    s = d * q.astype(np.int32).sum(-1).astype(np.float32)
+    assert s.dtype == np.float32
+    out = np.zeros((ncols, K // 32, 36), np.uint8)
+    out[..., 0:2] = d.astype(np.float16).view(np.uint8).reshape(ncols, K // 32, 2)
+    out[..., 2:4] = s.astype(np.float16).view(np.uint8).reshape(ncols, K // 32, 2)
+    out[..., 4:] = q.view(np.uint8)
+    return out.reshape(ncols, -1)
+
+
+def near_tie_blocks(seed=31, nblocks=512):
+    """fp32 activations whose quotient x/d lies at or within a few ulps of a
+    half-integer k + 1/2, chosen where an fp32 division, a multiply by the
+    fp32 reciprocal and an fp64 division round to different codes, plus exact
+    ties for the tie rule.  Each block holds its amax first (so d is fixed)
+    and 31 such values."""
+    g = synth.rng(seed)
+    picked = []
+    while len(picked) < nblocks:
+        amax = np.float32(np.exp2(g.uniform(-8, 8)) * (1 + g.random()))
+        d = amax / np.float32(127)
+        r = np.float32(1) / d
+        vals = []
+        for k in g.integers(0, 126, 64):
+            x0 = np.float32((k + 0.5) * float(d))
+            for j in range(-3, 4):
+                x = x0
+                for _ in range(abs(j)):
+                    x = np.nextafter(x, np.float32(np.inf if j > 0 else -np.inf))
+                q32 = float(x / d)
+                a = np.floor(abs(q32) + 0.5)
+                b = np.floor(abs(float(x * r)) + 0.5)
+                c = np.floor(abs(float(x) / float(d)) + 0.5)
+                e = np.rint(abs(q32))
+                if a != b or a != c or a != e:
+                    vals.append(x if g.random() < 0.5 else -x)
+        if len(vals) >= 31:
+            blk = np.zeros(32, np.float32)
+            blk[0] = amax if g.random() < 0.5 else -amax
+            blk[1:] = np.asarray(vals[:31], np.float32)
+            picked.append(blk)
+    return np.concatenate(picked).reshape(1, -1)
+
+
+def test_q8_1_vs_independent_numpy_random():
+    g = synth.rng(41)
+    x = synth.activations(g, 6, 2560)
+    x[1] *= np.float32(1e-6)                       # small d (still normal)
+    x[2] *= np.float32(1e-39 / 3)                  # subnormal x and d
+    x[3, :64] = 0.0                                # all-zero blocks
+    x[4] = np.float32(7.25)                        # constant blocks
+    x[5] *= np.float32(2.0 ** 12)                  # large values (d and s still finite in fp16)
+    assert np.array_equal(orc.quantize_q8_1(x), numpy_q8_1(x))
+
+
+def test_q8_1_near_ties_decide_the_division_reading():
+    x = near_tie_blocks()
+    ref = numpy_q8_1(x)
+    assert np.array_equal(orc.quantize_q8_1(x), ref)
+    # the fixture separates the reading from each plausible other one, so an
+    # oracle that multiplied by the reciprocal, divided in fp64 or rounded
+    # ties to even would fail the line above
+    for mode in ("recip", "div64", "even"):
+        other = numpy_q8_1(x, mode)
+        assert not np.array_equal(other, ref), mode
+        nq = np.count_nonzero(other.reshape(-1, 36)[:, 4:] != ref.reshape(-1, 36)[:, 4:])
+        assert nq >= 50, (mode, nq)
+
+
+# ------------------------------------------ exhaustive decoders vs numpy
+def numpy_q6k_codes(blocks):
+    """q6 in [0, 63] per weight of [nb][210] GGUF Q6_K blocks, from the layout
+    reading (h = i/128, c = (i%128)/32, l = i%32)."""
+    i = np.arange(256)
+    h, c, l = i // 128, (i % 128) // 32, i % 32
+    low = (blocks[:, 64 * h + 32 * (c % 2) + l] >> (4 * (c // 2))) & 15
+    high = (blocks[:, 128 + 32 * h + l] >> (2 * c)) & 3
+    return low.astype(np.int64) | (high.astype(np.int64) << 4)
+
+
+def numpy_q45_codes(blocks, five):
+    i = np.arange(256)
+    j, l = i // 32, i % 32
+    qs0 = 48 if five else 16
+    q = (blocks[:, qs0 + 32 * (j // 2) + l] >> (4 * (j % 2))) & 15
+    q = q.astype(np.int64)
+    if five:
+        q |= ((blocks[:, 16 + l] >> j) & 1).astype(np.int64) << 4
+    return q
+
+
+def numpy_q45_scales(blocks):
+    """(sc, m) [nb][8] from the 12 packed bytes at offset 4."""
+    s = blocks[:, 4:16].astype(np.int64)
+    sc = np.zeros((len(blocks), 8), np.int64)
+    m = np.zeros((len(blocks), 8), np.int64)
+    for j in range(8):
+        if j < 4:
+            sc[:, j] = s[:, j] & 63
+            m[:, j] = s[:, j + 4] & 63
+        else:
+            sc[:, j] = (s[:, j + 4] & 15) | ((s[:, j - 4] >> 6) << 4)
+            m[:, j] = (s[:, j + 4] >> 4) | ((s[:, j] >> 6) << 4)
+    return sc, m
+
+
+def _all_pairs():
+    t = np.arange(65536)
+    return (t >> 8).astype(np.uint8), (t & 255).astype(np.uint8)
+
+
+def test_q6k_decoder_exhaustive_byte_pairs_vs_numpy():
+    """Every (ql byte, qh byte) pair at every weight position: block t holds
+    ql bytes t>>8 and qh bytes t&255 throughout, d = 1 and unit scales, so
+    the dequantized weight is q6 - 32; and random blocks (distinct bytes per
+    position) for the byte indexing."""
+    a, b = _all_pairs()
+    blk = np.zeros((65536, 210), np.uint8)
+    blk[:, :128] = a[:, None]
+    blk[:, 128:192] = b[:, None]
+    blk[:, 192:208] = 1
+    blk[:, 208], blk[:, 209] = 0x00, 0x3C                       # fp16 1.0
+    w = orc.dequant("q6k", blk.reshape(-1), 65536, 256)
+    assert np.array_equal(w, (numpy_q6k_codes(blk) - 32).astype(np.float64))
+    rnd = synth.q6k_blocks(synth.rng(51), 4096, 256).reshape(4096, 210).copy()
+    rnd[:, 192:208] = 1
+    rnd[:, 208], rnd[:, 209] = 0x00, 0x3C
+    w = orc.dequant("q6k", rnd.reshape(-1), 4096, 256)
+    assert np.array_equal(w, (numpy_q6k_codes(rnd) - 32).astype(np.float64))
+
+
+@pytest.mark.parametrize("five", [False, True])
+def test_q45_decoder_exhaustive_vs_numpy(five):
+    """Q4_K/Q5_K: every (qs byte, qh byte) pair at every position (unit
+    scales, zero mins, d = 1, dmin = 0, so w = q), and every pair of the
+    bytes each 6-bit scale and min is built from (w = sc with q = 1, and
+    w = -m with d = 0, dmin = 1)."""
+    kind, nbytes = ("q5k", 176) if five else ("q4k", 144)
+    qs0 = 48 if five else 16
+    a, b = _all_pairs()
+    ones = encode_scales(np.ones(8, int), np.zeros(8, int))
+    blk = np.zeros((65536, nbytes), np.uint8)
+    blk[:, 0], blk[:, 1] = 0x00, 0x3C                           # d = 1, dmin = 0
+    blk[:, 4:16] = ones
+    blk[:, qs0:qs0 + 128] = a[:, None]
+    if five:
+        blk[:, 16:48] = b[:, None]
+    w = orc.dequant(kind, blk.reshape(-1), 65536, 256)
+    assert np.array_equal(w, numpy_q45_codes(blk, five).astype(np.float64))
+    g = synth.rng(52)
+    # sub-blocks 4..7 take sc from bytes 8..11 and 0..3, m from bytes 8..11
+    # and 4..7 (sub-blocks 0..3 one byte each): sweep both pairs of groups,
+    # the third group random
+    for other in ((0, 4), (4, 8)):
+        sb = np.zeros((65536, nbytes), np.uint8)
+        sb[:, 4:16] = g.integers(0, 256, (65536, 12), dtype=np.uint8)
+        sb[:, 12:16] = a[:, None]
+        sb[:, 4 + other[0]:4 + other[1]] = b[:, None]
+        sc, m = numpy_q45_scales(sb)
+        one = sb.copy()
+        one[:, 0], one[:, 1] = 0x00, 0x3C                   # d = 1, dmin = 0
+        one[:, qs0:qs0 + 128] = 0x11
+        if five:
+            one[:, 16:48] = 0
+        w = orc.dequant(kind, one.reshape(-1), 65536, 256)
+        assert np.array_equal(w, np.repeat(sc, 32, axis=1).astype(np.float64))
+        mn = sb.copy()
+        mn[:, 2], mn[:, 3] = 0x00, 0x3C                     # d = 0, dmin = 1
+        w = orc.dequant(kind, mn.reshape(-1), 65536, 256)
+        assert np.array_equal(w, -np.repeat(m, 32, axis=1).astype(np.float64))
+
+
 # --------------------------------------------------------- integer sums
 def unpack_matrix(kind, w, rows, K):
     """Per-weight integer codes and per-weight integer scales from the
