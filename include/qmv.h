@@ -124,8 +124,13 @@ enum { QMV_LAYOUT_GGUF = 0, QMV_LAYOUT_PLANAR = 1, QMV_LAYOUT_TILED = 2 };
  * activations are column-planar (see above) instead of Q8_1 blocks. */
 enum { QMV_ACT_PLANAR = 16 };
 
-/* Largest supported sizes: rows <= 2^31-1, K <= 2^20, and every weight,
- * activation and output buffer below 2^40 bytes. */
+/* Largest supported sizes (larger calls return QMV_ERR_UNSUPPORTED before
+ * any HIP call; every launch then stays below 2^32 work-items along x and
+ * 65535 workgroups along y): K <= 2^20; products (and their argmax and
+ * integer-sum forms) rows <= 2^26 - 1024 = 67,107,840; conversions
+ * rows <= 2^31-1 with rows*K/256*8 < 2^32; row gathers nout*K/256 < 2^32;
+ * quantizers ncols*K/4 < 2^32; the grouped MoE call as stated there; every
+ * weight, activation and output buffer below 2^40 bytes. */
 
 /* Quantize fp32 activations to Q8_1 (PR #2340 "What it changes" names the
  * Q8_1 activation quants).  Per block of 32 values of one column:
@@ -259,7 +264,11 @@ int mmvq_q5k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows,
  *   xq: Q8_1 [T][d_model/32] (4-byte aligned); ids: int32 [T][topk] in
  *   [0, E), distinct within a token; route_w: fp32 [T][topk];
  *   out: fp32 [T][d_model], overwritten.
- *   1 <= T <= 8, 1 <= topk <= 8, d_model and d_ff multiples of 256.
+ *   1 <= T <= 8, 1 <= topk <= 8, d_model and d_ff multiples of 256 (at
+ *   most 2^20), E*d_model <= 2^31-1, and d_model/r <= 65535 with r the
+ *   down rows per workgroup (4*64/U, U = lanes per down row: the largest of
+ *   64, 32, 16 dividing d_ff/32 with at least three units each, else 8), so
+ *   d_model <= 262,140 at least.
  *   ws: device workspace of at least grouped_expert_mmvq_workspace() bytes,
  *   256-byte aligned.  Layout (all offsets from ws, S = T*topk):
  *     int32 hdr[64]: hdr[0] = number of distinct experts hit, hdr[1] = number
@@ -285,7 +294,8 @@ size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, in
 /* Streaming-read calibration: reads `bytes` (a multiple of 16) from src
  * (16-byte aligned) with 16-byte non-temporal loads, four per thread per
  * step, over `blocks` (1..65535) workgroups of 256 threads, or, when blocks
- * is 0, over one workgroup per 16 KiB so that each thread takes one step.
+ * is 0, over one workgroup per 16 KiB so that each thread takes one step
+ * (then bytes < 2^38).
  * sink (uint32, as many words as workgroups) is written only if a thread's
  * XOR of its data equals a fixed constant.  Its duration at a given size is
  * the achievable read time the MMVQ kernels are measured against. */

@@ -13,6 +13,16 @@ thread_local int g_last_hip_error = 0;
 constexpr int64_t kMaxRows = 2147483647LL;
 constexpr int64_t kMaxK = 1LL << 20;
 constexpr int64_t kMaxBytes = 1LL << 40;
+// Launch limits: work-items along x of one launch below 2^32, workgroups
+// along y at most 65535.  The products launch at most 64 work-items per row
+// (sixteen waves per 16-row tile, or one wave per row) plus one workgroup,
+// so rows up to kMaxProductRows always fit.
+constexpr int64_t kMaxItems = 0xFFFFFFFFLL;
+constexpr int64_t kMaxGridY = 65535;
+constexpr int64_t kMaxProductRows = (1LL << 26) - 1024;
+
+// work-items of a launch of ceil(items / 256) workgroups of 256
+bool items_fit(int64_t items) { return items <= kMaxItems - 255; }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -29,7 +39,7 @@ int check_mmvq(const void *w, const void *xq, const void *out, int64_t rows, int
                int64_t block_bytes, uintptr_t w_align, int max_cols = 8) {
     if (!w || !xq || !out) return QMV_ERR_INVALID_ARG;
     if (rows <= 0 || K <= 0) return QMV_ERR_INVALID_ARG;
-    if (K % 256 != 0 || K > kMaxK || rows > kMaxRows) return QMV_ERR_UNSUPPORTED;
+    if (K % 256 != 0 || K > kMaxK || rows > kMaxProductRows) return QMV_ERR_UNSUPPORTED;
     if (ncols < 1 || ncols > max_cols) return QMV_ERR_UNSUPPORTED;
     if (rows * (K / 256) * block_bytes >= kMaxBytes || rows * ncols * 4 >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
     if (!aligned(w, w_align) || !aligned(xq, 4) || !aligned(out, 4)) return QMV_ERR_ALIGNMENT;
@@ -75,7 +85,7 @@ int check_repack(const void *src, const void *dst, int64_t rows, int64_t K, uint
     if (rows <= 0 || K <= 0) return QMV_ERR_INVALID_ARG;
     if (K % 256 != 0 || K > kMaxK || rows > kMaxRows) return QMV_ERR_UNSUPPORTED;
     const int64_t bytes = rows * (K / 256) * 210;
-    if (bytes >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
+    if (bytes >= kMaxBytes || !items_fit(rows * (K / 256) * 8)) return QMV_ERR_UNSUPPORTED;   // 8 per block
     if (!aligned(src, src_align) || !aligned(dst, dst_align)) return QMV_ERR_ALIGNMENT;
     const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
     if (s < d + (uintptr_t)bytes && d < s + (uintptr_t)bytes) return QMV_ERR_INVALID_ARG;   // overlap
@@ -90,6 +100,7 @@ int quantize_q8_1(const float *x, void *xq, int64_t K, int ncols, void *stream) 
     if (!x || !xq) return QMV_ERR_INVALID_ARG;
     if (K <= 0 || ncols <= 0) return QMV_ERR_INVALID_ARG;
     if (K % 32 != 0 || K > kMaxK || ncols > 65535) return QMV_ERR_UNSUPPORTED;
+    if (!items_fit((int64_t)ncols * (K / 32) * 8)) return QMV_ERR_UNSUPPORTED;    // eight per block
     if (!aligned(x, 4) || !aligned(xq, 4)) return QMV_ERR_ALIGNMENT;
     return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, false, as_stream(stream)));
 }
@@ -98,6 +109,7 @@ int quantize_q8_1_planar(const float *x, void *xq, int64_t K, int ncols, void *s
     if (!x || !xq) return QMV_ERR_INVALID_ARG;
     if (K <= 0 || ncols <= 0) return QMV_ERR_INVALID_ARG;
     if (K % 32 != 0 || K > kMaxK || ncols > 65535) return QMV_ERR_UNSUPPORTED;
+    if (!items_fit((int64_t)ncols * (K / 32) * 8)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(x, 4) || !aligned(xq, 4)) return QMV_ERR_ALIGNMENT;
     return from_hip(qmv::launch_quantize(x, reinterpret_cast<uint8_t *>(xq), K, ncols, true, as_stream(stream)));
 }
@@ -200,7 +212,7 @@ int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const 
         return QMV_ERR_UNSUPPORTED;
     if (K % 256 != 0 || K > kMaxK || rows > kMaxRows || nout > kMaxRows) return QMV_ERR_UNSUPPORTED;
     const int64_t sb = rows * (K / 256) * 210, db = nout * (K / 256) * 210;
-    if (sb >= kMaxBytes || db >= kMaxBytes) return QMV_ERR_UNSUPPORTED;
+    if (sb >= kMaxBytes || db >= kMaxBytes || !items_fit(nout * (K / 256))) return QMV_ERR_UNSUPPORTED;
     const uintptr_t al = layout == QMV_LAYOUT_GGUF ? 1 : 16;
     if (!aligned(src, al) || !aligned(dst, al) || !aligned(ids, 4)) return QMV_ERR_ALIGNMENT;
     const uintptr_t s = reinterpret_cast<uintptr_t>(src), d = reinterpret_cast<uintptr_t>(dst);
@@ -210,7 +222,7 @@ int gather_q6k_rows(const void *src, int layout, int64_t rows, int64_t K, const 
 }
 
 size_t mmvq_q6k_argmax_workspace(int64_t rows, int ncols) {
-    if (rows <= 0 || rows > kMaxRows || ncols < 1 || ncols > 8) return 0;
+    if (rows <= 0 || rows > kMaxProductRows || ncols < 1 || ncols > 8) return 0;
     return (size_t)(qmv::argmax_tail((rows + 15) / 16, ncols) + 256);
 }
 
@@ -249,6 +261,7 @@ int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down
     const int64_t dn_bytes = (int64_t)E * d_model * (d_ff / 256) * 210;
     if (gu_bytes >= kMaxBytes || dn_bytes >= kMaxBytes || (int64_t)E * d_model > kMaxRows)
         return QMV_ERR_UNSUPPORTED;
+    if (!qmv::moe_grid_fits(T * topk, d_model, d_ff, kMaxGridY)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, down_layout == QMV_LAYOUT_PLANAR ? 16 : 4) ||
         !aligned(xq, 4) || !aligned(ids, 4) || !aligned(route_w, 4) || !aligned(out, 4))
         return QMV_ERR_ALIGNMENT;
@@ -279,6 +292,7 @@ int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down
 int qmv_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, void *stream) {
     if (!src || !sink || bytes <= 0 || blocks < 0) return QMV_ERR_INVALID_ARG;
     if (bytes % 16 != 0 || bytes >= kMaxBytes || blocks > 65535) return QMV_ERR_UNSUPPORTED;
+    if (blocks == 0 && !items_fit((bytes / 16 + 1023) / 1024 * 256)) return QMV_ERR_UNSUPPORTED;
     if (!aligned(src, 16) || !aligned(sink, 4)) return QMV_ERR_ALIGNMENT;
     return from_hip(qmv::launch_stream_read(src, bytes, sink, blocks, as_stream(stream)));
 }

@@ -71,5 +71,8 @@ struct MoeLayout {
 MoeLayout moe_layout(int T, int topk, int64_t d_model, int64_t d_ff);
 
 hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s);
+// Whether every launch of launch_moe for S slots stays within max_grid_y
+// workgroups along y (host arithmetic only).
+bool moe_grid_fits(int S, int64_t d_model, int64_t d_ff, int64_t max_grid_y);
 
 }  // namespace qmv

@@ -475,6 +475,14 @@ static hipError_t launch_down(const MoeArgs &m, int smax, hipStream_t s) {
     }
 }
 
+bool moe_grid_fits(int S, int64_t d_model, int64_t d_ff, int64_t max_grid_y) {
+    // gate/up: d_ff/32 row tiles along y; down: row blocks of kDnWaves waves
+    // along y (either down path is taken depending on the window, so both
+    // must fit); combine: the T tokens along y
+    const int64_t rpb = kDnWaves * (kWave / choose_u((int)(d_ff / 32)));
+    return d_ff / kGuRows <= max_grid_y && (d_model + rpb - 1) / rpb <= max_grid_y && S <= max_grid_y;
+}
+
 hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s) {
     const int smax = m.S;   // one workgroup column per slot; non-first slots exit
     // gate/up: eight lanes per row whatever d_model (512-thread workgroups

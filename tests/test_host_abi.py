@@ -244,3 +244,34 @@ def test_binding_raises_qmv_error(L):
     with pytest.raises(qmv.QmvError) as ei:
         qmv.mmvq_q6k(P, 1, P, P, 16, 300, 1, stream=0)
     assert ei.value.code == E_UNS
+
+
+def test_launch_size_limits_rejected_on_host(L):
+    """Calls whose launches would exceed 2^32 work-items along x or 65535
+    workgroups along y are rejected as unsupported before any HIP call."""
+    K20 = 1 << 20
+    for q in (L.quantize_q8_1, L.quantize_q8_1_planar):
+        # ncols * K / 4 work-items: 16385 columns of 2^20 exceed 2^32
+        assert q(P, P, K20, 16385, None) == E_UNS
+        assert q(P, P, K20 // 2, 32769, None) == E_UNS
+    big = (1 << 26) - 1024 + 1                     # one row past the product limit
+    for lay in (qmv.LAYOUT_GGUF, qmv.LAYOUT_PLANAR, qmv.LAYOUT_TILED, qmv.LAYOUT_TILED | qmv.ACT_PLANAR):
+        assert L.mmvq_q6k(P, lay, P, P, big, 256, 1, None) == E_UNS
+        assert L.mmvq_q6k_isums(P, lay, P, P, big, 256, 1, None) == E_UNS
+    assert L.mmvq_q4k(P, P, P, big, 256, 1, None) == E_UNS
+    assert L.mmvq_q5k(P, P, P, big, 256, 1, None) == E_UNS
+    assert L.mmvq_q4k_isums(P, P, P, big, 256, 8, None) == E_UNS
+    assert L.mmq_q6k(P, qmv.LAYOUT_TILED, P, P, big, 256, 1, None) == E_UNS
+    assert L.mmvq_q6k_argmax_workspace(big, 1) == 0
+    assert L.mmvq_q6k_argmax(P, qmv.LAYOUT_TILED, P, big, 256, 1, P, P, P, 1 << 40, None) == E_UNS
+    # conversions: eight work-items per block (2^32 blocks here)
+    for fn in (L.repack_q6k_planar, L.repack_q6k_tiled, L.unpack_q6k_planar, L.unpack_q6k_tiled):
+        assert fn(P, P + (1 << 41), 1 << 20, K20, None) == E_UNS
+    assert L.gather_q6k_rows(P, 1, 4, K20, P, 1 << 20, P + (1 << 41), None) == E_UNS
+    # grouped MoE: d_ff = 6144 runs 64 lanes per down row, four rows per
+    # workgroup, so d_model = 2^20 needs 262144 workgroups along y
+    ws = L.grouped_expert_mmvq_workspace(1, 1, 1, K20, 6144)
+    assert ws > 0
+    assert L.grouped_expert_mmvq(P, P, P, 1, P, P, P, P, 1, 1, 1, K20, 6144, P, ws, None) == E_UNS
+    # streaming read with one step per thread: bytes / 64 work-items
+    assert L.qmv_stream_read(P, 1 << 39, P, 0, None) == E_UNS
