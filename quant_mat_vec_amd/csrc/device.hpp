@@ -573,6 +573,18 @@ __device__ __forceinline__ int dpp_iadd(int v) {
     return v + __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
+// fp16 bits of the Q8_1 sum field: the fp32 product d * sum, rounded to
+// fp32, then to fp16 (both to nearest even).  The compiler would otherwise
+// fuse the multiply and the conversion into one mixed-precision fma, which
+// rounds the exact product to fp16 once -- a different result where the
+// fp32 product lands on an fp16 midpoint.  The empty register-only asm
+// makes the fp32 product a value the conversion must start from.
+__device__ __forceinline__ uint32_t q8_1_sum_bits(float d, int sum) {
+    float p = d * (float)sum;
+    asm volatile("" : "+v"(p));
+    return __builtin_bit_cast(uint16_t, (_Float16)p);
+}
+
 __device__ __forceinline__ int q8_1_quantize32(float x, uint32_t &dbits, uint32_t &sbits) {
     // max and sum over the 32 lanes: DPP inside each 16-lane row, then one
     // exchange between the two rows (both orders give the same result)
@@ -596,7 +608,7 @@ __device__ __forceinline__ int q8_1_quantize32(float x, uint32_t &dbits, uint32_
     s = dpp_iadd<0x140>(s);
     s += __shfl_xor(s, 16, 32);
     dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
-    sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+    sbits = q8_1_sum_bits(d, s);
     return q;
 }
 
@@ -641,6 +653,7 @@ struct MmvqArgs {
     uint64_t colpack;
     int64_t xstride;
     int its;              // register steps staged per LDS sub-tile
+    int nout;             // columns the dense kernel stores (its N, or fewer)
 };
 
 // First Q8_1 block of column n.

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_quantize_q8_1(const float *__restrict__
         const uint32_t qw = ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) |
                             (((uint32_t)q[2] & 0xFFu) << 16) | ((uint32_t)q[3] << 24);
         const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
-        const uint32_t sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+        const uint32_t sbits = q8_1_sum_bits(d, s);
         if constexpr (PLANAR) {
             const int64_t col = g / nb, b = g - col * nb;
             uint8_t *c = xq + col * nb * kQ81Bytes;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_q8_1(const float *__restrict__ 
             const uint32_t qw = ((uint32_t)q[0] & 0xFFu) | (((uint32_t)q[1] & 0xFFu) << 8) |
                                 (((uint32_t)q[2] & 0xFFu) << 16) | ((uint32_t)q[3] << 24);
             const uint32_t dbits = __builtin_bit_cast(uint16_t, (_Float16)d);
-            const uint32_t sbits = __builtin_bit_cast(uint16_t, (_Float16)(d * (float)s));
+            const uint32_t sbits = q8_1_sum_bits(d, s);
             if constexpr (PLANAR) {
                 reinterpret_cast<uint32_t *>(c + 32 * b)[i] = qw;
                 if (i == 0) {
@@ -236,43 +236,71 @@ __global__ __launch_bounds__(256) void k_repack_q6k(const uint8_t *__restrict__ 
     }
 }
 
-// planar or tiled -> GGUF Q6_K, one thread per block.
+// planar or tiled -> GGUF Q6_K.  Eight threads per block, one per
+// sub-block j: each decodes its 32 six-bit values from its plane-A and
+// plane-B pieces into LDS; then thread k of the block assembles GGUF bytes
+// 24k .. 24k+23 of ql/qh from the eight sub-blocks' values, and thread 0 also
+// copies the scales and d.  (One thread per whole block held 192 bytes of
+// ql/qh in registers: 256 VGPRs plus accumulation registers.)
+constexpr int kUnpackThreads = 256, kUnpackBlocks = kUnpackThreads / 8;
 template <bool TILED>
-__global__ __launch_bounds__(256) void k_unpack_q6k(const uint8_t *__restrict__ src, uint8_t *__restrict__ dst,
-                                                    int64_t NB, PlaneIndex<TILED> ix) {
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= NB) return;
-    int64_t p0, ps, h0, hs, di;
-    ix.at(t, p0, ps, h0, hs, di);
-    uint8_t *blk = dst + t * kQ6Bytes;
-    uint8_t ql[128] = {}, qh[64] = {};
-    for (int j = 0; j < 8; j++) {
+__global__ __launch_bounds__(kUnpackThreads) void k_unpack_q6k(const uint8_t *__restrict__ src,
+                                                               uint8_t *__restrict__ dst, int64_t NB,
+                                                               PlaneIndex<TILED> ix) {
+    __shared__ uint8_t vals[kUnpackBlocks][8][32];          // (q6 - 32) mod 64 per sub-block position
+    const int bl = threadIdx.x >> 3, j = threadIdx.x & 7;
+    const int64_t t = (int64_t)blockIdx.x * kUnpackBlocks + bl;
+    const bool live = t < NB;
+    int64_t p0 = 0, ps = 0, h0 = 0, hs = 0, di = 0;
+    if (live) {
+        ix.at(t, p0, ps, h0, hs, di);
         const uint4 a = reinterpret_cast<const uint4 *>(src)[p0 + j * ps];
         const uint2 b = reinterpret_cast<const uint2 *>(src + 128 * NB)[p0 + j * ps];
         const uint32_t A[4] = {a.x, a.y, a.z, a.w}, B[2] = {b.x, b.y};
-        uint32_t v[32];
-        for (int k = 0; k < 16; k++) v[k] = (A[k >> 2] >> (8 * (k & 3) + 2)) & 63u;
-        for (int k = 0; k < 8; k++) v[16 + k] = (B[k >> 2] >> (8 * (k & 3) + 2)) & 63u;
+#pragma unroll
+        for (int k = 0; k < 16; k++) vals[bl][j][k] = (uint8_t)((A[k >> 2] >> (8 * (k & 3) + 2)) & 63u);
+#pragma unroll
+        for (int k = 0; k < 8; k++) vals[bl][j][16 + k] = (uint8_t)((B[k >> 2] >> (8 * (k & 3) + 2)) & 63u);
+#pragma unroll
         for (int k = 0; k < 4; k++) {
             const int sh = 8 * k;
-            v[24 + k] = ((A[0] >> sh) & 3u) | (((A[1] >> sh) & 3u) << 2) | (((A[2] >> sh) & 3u) << 4);
-            v[28 + k] = ((A[3] >> sh) & 3u) | (((B[0] >> sh) & 3u) << 2) | (((B[1] >> sh) & 3u) << 4);
-        }
-        const int h = j >> 2, c = j & 3;
-        for (int l = 0; l < 32; l++) {
-            uint32_t q6 = v[l] ^ 32u;
-            ql[64 * h + 32 * (c & 1) + l] |= (uint8_t)((q6 & 15u) << (4 * (c >> 1)));
-            qh[32 * h + l] |= (uint8_t)((q6 >> 4) << (2 * c));
+            vals[bl][j][24 + k] =
+                (uint8_t)(((A[0] >> sh) & 3u) | (((A[1] >> sh) & 3u) << 2) | (((A[2] >> sh) & 3u) << 4));
+            vals[bl][j][28 + k] =
+                (uint8_t)(((A[3] >> sh) & 3u) | (((B[0] >> sh) & 3u) << 2) | (((B[1] >> sh) & 3u) << 4));
         }
     }
-    for (int k = 0; k < 128; k++) blk[k] = ql[k];
-    for (int k = 0; k < 64; k++) blk[128 + k] = qh[k];
-    for (int hh = 0; hh < 2; hh++) {
-        const uint8_t *sc = src + 192 * NB + 8 * (h0 + hh * hs);
-        for (int k = 0; k < 8; k++) blk[192 + 8 * hh + k] = sc[k];
+    __syncthreads();
+    if (!live) return;
+    uint8_t *blk = dst + t * kQ6Bytes;
+    for (int i = 24 * j; i < 24 * j + 24; i++) {
+        uint32_t byte;
+        if (i < 128) {
+            // ql byte 64h + 32(c%2) + l: the low nibble from c = c%2, the
+            // high one from c = c%2 + 2 (sub-blocks 4h + c)
+            const int h = i >> 6, c1 = (i >> 5) & 1, l = i & 31;
+            const uint32_t lo = (vals[bl][4 * h + c1][l] ^ 32u) & 15u;
+            const uint32_t hi = (vals[bl][4 * h + c1 + 2][l] ^ 32u) & 15u;
+            byte = lo | (hi << 4);
+        } else {
+            // qh byte 32h + l: bits 2c from sub-block 4h + c
+            const int h = (i - 128) >> 5, l = (i - 128) & 31;
+            byte = 0;
+#pragma unroll
+            for (int c = 0; c < 4; c++) byte |= (((vals[bl][4 * h + c][l] ^ 32u) >> 4) & 3u) << (2 * c);
+        }
+        blk[i] = (uint8_t)byte;
     }
-    blk[208] = src[208 * NB + 2 * di];
-    blk[209] = src[208 * NB + 2 * di + 1];
+    if (j == 0) {
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            const uint8_t *sc = src + 192 * NB + 8 * (h0 + hh * hs);
+#pragma unroll
+            for (int k = 0; k < 8; k++) blk[192 + 8 * hh + k] = sc[k];
+        }
+        blk[208] = src[208 * NB + 2 * di];
+        blk[209] = src[208 * NB + 2 * di + 1];
+    }
 }
 
 // Streaming-read calibration: the fastest plain read of a buffer found on
@@ -332,20 +360,26 @@ __global__ __launch_bounds__(256) void k_gather_q6k(const uint8_t *__restrict__ 
         int64_t sp, sps, sh, shs, sd, dp, dps, dh, dhs, dd;
         PlaneIndex<TILED>{rows, nb}.at(ts, sp, sps, sh, shs, sd);
         PlaneIndex<TILED>{nout, nb}.at(td, dp, dps, dh, dhs, dd);
-        const uint4 z4 = make_uint4(0, 0, 0, 0);
-        const uint2 z2 = make_uint2(0, 0);
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            reinterpret_cast<uint4 *>(dst)[dp + k * dps] = ok ? reinterpret_cast<const uint4 *>(src)[sp + k * sps] : z4;
-            reinterpret_cast<uint2 *>(dst + 128 * NBd)[dp + k * dps] =
-                ok ? reinterpret_cast<const uint2 *>(src + 128 * NBs)[sp + k * sps] : z2;
+            uint4 a = make_uint4(0, 0, 0, 0);
+            uint2 bb = make_uint2(0, 0);
+            if (ok) {
+                a = reinterpret_cast<const uint4 *>(src)[sp + k * sps];
+                bb = reinterpret_cast<const uint2 *>(src + 128 * NBs)[sp + k * sps];
+            }
+            reinterpret_cast<uint4 *>(dst)[dp + k * dps] = a;
+            reinterpret_cast<uint2 *>(dst + 128 * NBd)[dp + k * dps] = bb;
         }
 #pragma unroll
-        for (int h = 0; h < 2; h++)
-            reinterpret_cast<uint2 *>(dst + 192 * NBd)[dh + h * dhs] =
-                ok ? reinterpret_cast<const uint2 *>(src + 192 * NBs)[sh + h * shs] : z2;
-        reinterpret_cast<uint16_t *>(dst + 208 * NBd)[dd] =
-            ok ? reinterpret_cast<const uint16_t *>(src + 208 * NBs)[sd] : (uint16_t)0;
+        for (int h = 0; h < 2; h++) {
+            uint2 sc = make_uint2(0, 0);
+            if (ok) sc = reinterpret_cast<const uint2 *>(src + 192 * NBs)[sh + h * shs];
+            reinterpret_cast<uint2 *>(dst + 192 * NBd)[dh + h * dhs] = sc;
+        }
+        uint16_t dv = 0;
+        if (ok) dv = reinterpret_cast<const uint16_t *>(src + 208 * NBs)[sd];
+        reinterpret_cast<uint16_t *>(dst + 208 * NBd)[dd] = dv;
     }
 }
 
@@ -374,11 +408,13 @@ hipError_t launch_repack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t
 
 hipError_t launch_unpack(const uint8_t *src, uint8_t *dst, int64_t rows, int64_t K, bool tiled, hipStream_t s) {
     const int64_t nb = K / 256, NB = rows * nb;
-    const dim3 grid((unsigned)((NB + 255) / 256));
+    const dim3 grid((unsigned)((NB + kUnpackBlocks - 1) / kUnpackBlocks));
     if (tiled)
-        hipLaunchKernelGGL(k_unpack_q6k<true>, grid, dim3(256), 0, s, src, dst, NB, PlaneIndex<true>{rows, nb});
+        hipLaunchKernelGGL(k_unpack_q6k<true>, grid, dim3(kUnpackThreads), 0, s, src, dst, NB,
+                           PlaneIndex<true>{rows, nb});
     else
-        hipLaunchKernelGGL(k_unpack_q6k<false>, grid, dim3(256), 0, s, src, dst, NB, PlaneIndex<false>{rows, nb});
+        hipLaunchKernelGGL(k_unpack_q6k<false>, grid, dim3(kUnpackThreads), 0, s, src, dst, NB,
+                           PlaneIndex<false>{rows, nb});
     return hipGetLastError();
 }
 

@@ -42,14 +42,16 @@ __global__ __launch_bounds__(W * kWave) void k_mmvq_dense(const void *__restrict
             float v = acc[p][0];
 #pragma unroll
             for (int n = 1; n < N; n++) v = u == n ? acc[p][n] : v;
-            if (row < a.rows && u < N) out[(int64_t)u * a.rows + row] = v;
+            if (row < a.rows && u < N && u < a.nout) out[(int64_t)u * a.rows + row] = v;
         }
     }
 }
 
+// ncols <= N real columns: columns ncols .. N-1 of the kernel read the last
+// real column again and are not stored.
 template <class F, int N, int U, int W, int IT, bool DUMP>
 hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                            hipStream_t s) {
+                            hipStream_t s, int ncols = N) {
     constexpr int threads = W * kWave;
     constexpr int its = its_for(IT, N, U, F::SBPU, threads);
     MmvqArgs a;
@@ -57,7 +59,9 @@ hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *
     a.dump = dump;
     a.rows = rows;
     a.K = K;
-    a.colpack = 0x0706050403020100ull;
+    a.colpack = 0;
+    for (int n = 0; n < 8; n++) a.colpack |= (uint64_t)(n < ncols ? n : ncols - 1) << (8 * n);
+    a.nout = ncols;
     a.xstride = K / 32;
     a.its = its;
     const size_t lds = (size_t)N * its * U * F::SBPU * kActBytesPerBlock;
@@ -79,39 +83,69 @@ hipError_t launch_dense_nuw(const void *w, const void *xq, float *out, int32_t *
 #endif
 template <class F, int N, int U, int IT, bool DUMP>
 hipError_t launch_dense_nui(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                            hipStream_t s) {
+                            hipStream_t s, int ncols) {
     // (not for Q5_K: its registers do not fit three waves per SIMD)
     if constexpr (!DUMP && kRowsPerWave<U, kDenseP<N>> <= 2 && sizeof(typename F::Raw) <= 64) {
         constexpr int64_t rpb10 = kMaxDenseWaves * kRowsPerWave<U, kDenseP<N>>;
         if ((rows + rpb10 - 1) / rpb10 >= QMV_DENSE_BIG_GRID)
             // (seven columns at depth five do not fit 168 registers)
-            return launch_dense_nuw<F, N, U, kMaxDenseWaves, (N == 7 ? 3 : IT), DUMP>(w, xq, out, dump, rows, K, s);
+            return launch_dense_nuw<F, N, U, kMaxDenseWaves, (N == 7 ? 3 : IT), DUMP>(w, xq, out, dump, rows, K, s,
+                                                                                      ncols);
     }
-    return launch_dense_nuw<F, N, U, kDenseWaves, IT, DUMP>(w, xq, out, dump, rows, K, s);
+    return launch_dense_nuw<F, N, U, kDenseWaves, IT, DUMP>(w, xq, out, dump, rows, K, s, ncols);
 }
 
 template <class F, int N, int U, bool DUMP>
 hipError_t launch_dense_nu(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                           hipStream_t s) {
+                           hipStream_t s, int ncols = N) {
     const int units = (int)(K / 32 / F::SBPU);
     if constexpr (F::IT > 3) {
         if (depth_for(units, U, F::IT) == 3)
-            return launch_dense_nui<F, N, U, 3, DUMP>(w, xq, out, dump, rows, K, s);
+            return launch_dense_nui<F, N, U, 3, DUMP>(w, xq, out, dump, rows, K, s, ncols);
     }
-    return launch_dense_nui<F, N, U, F::IT, DUMP>(w, xq, out, dump, rows, K, s);
+    return launch_dense_nui<F, N, U, F::IT, DUMP>(w, xq, out, dump, rows, K, s, ncols);
 }
+
+// Q4_K/Q5_K at six or seven columns with 32 or 64 lanes per row: the
+// compiler puts those instantiations at 256 VGPRs plus accumulation
+// registers (one wave per SIMD) while eight columns fit in 140-187.  The
+// products run on the eight-column kernel with the last real column read
+// again for the missing ones and only the real columns stored; the
+// per-sub-block sums (a test dump) run as four columns, then the rest.
+// Every column's arithmetic is the same at any column count, so the bits
+// do not change.
+template <class F, int U>
+constexpr bool kDenseWide67 = F::SBPU == 2 && U >= 32;
 
 template <class F, int U, bool DUMP>
 hipError_t launch_dense_u(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                           int ncols, hipStream_t s) {
+    if constexpr (kDenseWide67<F, U>) {
+        if (ncols == 6 || ncols == 7) {
+            if constexpr (DUMP) {
+                const hipError_t e = launch_dense_nu<F, 4, U, DUMP>(w, xq, out, dump, rows, K, s);
+                if (e != hipSuccess) return e;
+                const uint8_t *x4 = static_cast<const uint8_t *>(xq) + 4 * (K / 32) * kQ81Bytes;
+                int32_t *d4 = dump + 4 * rows * (K / 32);
+                return ncols == 6 ? launch_dense_nu<F, 2, U, DUMP>(w, x4, out, d4, rows, K, s)
+                                  : launch_dense_nu<F, 3, U, DUMP>(w, x4, out, d4, rows, K, s);
+            } else {
+                return launch_dense_nu<F, 8, U, DUMP>(w, xq, out, dump, rows, K, s, ncols);
+            }
+        }
+    }
     switch (ncols) {
     case 1: return launch_dense_nu<F, 1, U, DUMP>(w, xq, out, dump, rows, K, s);
     case 2: return launch_dense_nu<F, 2, U, DUMP>(w, xq, out, dump, rows, K, s);
     case 3: return launch_dense_nu<F, 3, U, DUMP>(w, xq, out, dump, rows, K, s);
     case 4: return launch_dense_nu<F, 4, U, DUMP>(w, xq, out, dump, rows, K, s);
     case 5: return launch_dense_nu<F, 5, U, DUMP>(w, xq, out, dump, rows, K, s);
-    case 6: return launch_dense_nu<F, 6, U, DUMP>(w, xq, out, dump, rows, K, s);
-    case 7: return launch_dense_nu<F, 7, U, DUMP>(w, xq, out, dump, rows, K, s);
+    case 6:
+        if constexpr (!kDenseWide67<F, U>) return launch_dense_nu<F, 6, U, DUMP>(w, xq, out, dump, rows, K, s);
+        return hipErrorInvalidValue;
+    case 7:
+        if constexpr (!kDenseWide67<F, U>) return launch_dense_nu<F, 7, U, DUMP>(w, xq, out, dump, rows, K, s);
+        return hipErrorInvalidValue;
     case 8: return launch_dense_nu<F, 8, U, DUMP>(w, xq, out, dump, rows, K, s);
     default: return hipErrorInvalidValue;
     }

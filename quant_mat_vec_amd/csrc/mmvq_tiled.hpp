@@ -595,6 +595,7 @@ hipError_t launch_tiled_cfg(const void *w, const void *xq, float *out, int32_t *
     a.colpack = 0x0706050403020100ull;
     a.xstride = K / 32;
     a.its = IT;
+    a.nout = N;
     const int64_t tiles = (rows + 15) / 16;
     int64_t grid = (tiles + RTW - 1) / RTW;
     if constexpr (N > 8) grid = 8 * ((grid + 7) / 8) * nbat;

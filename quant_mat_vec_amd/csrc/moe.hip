@@ -137,6 +137,7 @@ __device__ __forceinline__ void gateup_n(const MoeArgs &m, int e, const int32_t 
     for (int n = 0; n < N; n++) a.colpack |= (uint64_t)(sl[n] / m.topk) << (8 * n);
     a.xstride = m.d_model / 32;
     a.its = its;
+    a.nout = N;
     const int64_t row0 = (int64_t)tile * 2 * kGuRows;
     float acc[1][N];
     // the gate/up weight loads of the first kPreUnits units go out with the
@@ -227,6 +228,7 @@ __device__ __forceinline__ void down_n(const MoeArgs &m, int e, const int32_t (&
     for (int n = 0; n < N; n++) a.colpack |= (uint64_t)sl[n] << (8 * n);
     a.xstride = m.d_ff / 32;
     a.its = its;
+    a.nout = N;
     const int64_t row0 = (int64_t)e * m.d_model + (int64_t)tile * kDnWaves * (kWave / U);
     float acc[1][N];
     mmvq_rows<F, N, U, 1, nthr, false, IT, RAGGED>(f, a, row0, lds, acc);

@@ -9,11 +9,14 @@ max|gpu - oracle| <= 1e-5 * max|oracle|.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 import sys
 
 import numpy as np
 import torch
 
+import oracle as orc
 from quant_mat_vec_amd import qmv
 
 DEV = "cuda:0"
@@ -104,3 +107,50 @@ def assert_close(got: np.ndarray, ref: np.ndarray, absum: np.ndarray, what: str 
                              f"{float((err / np.maximum(absum, 1e-300)).max()):.3e}")
     colmax = np.abs(ref).max(axis=-1)
     assert np.all(err.max(axis=-1) <= TOL * colmax), f"{what}: column max error beyond 1e-5*max|ref|"
+
+
+# ------------------------------------------------ the oracle on every row
+_POOL = None
+
+
+def _pool() -> cf.ThreadPoolExecutor:
+    """Host threads for the oracle (its calls release the GIL)."""
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max(1, min(len(os.sched_getaffinity(0)), 16)))
+    return _POOL
+
+
+def _row_chunks(rows: int):
+    n = _pool()._max_workers
+    step = max(1, -(-rows // (4 * n)))
+    return [(r0, min(step, rows - r0)) for r0 in range(0, rows, step)]
+
+
+def oracle_all_rows(kind: str, w: np.ndarray, xq_np: np.ndarray, rows: int, K: int):
+    """(out, absum) of the oracle for every row, fp64 [ncols][rows], the
+    rows split over host threads."""
+    futs = [_pool().submit(orc.mmvq, kind, w, xq_np, rows, K, r0, n) for r0, n in _row_chunks(rows)]
+    parts = [f.result() for f in futs]
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
+
+
+def oracle_isums_all_rows(kind: str, w: np.ndarray, xq_np: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """The oracle's per-sub-block integer sums for every row, int32
+    [ncols][rows][K/32] (Q6_K isums, Q4_K/Q5_K dots), rows split over host
+    threads."""
+    bpb = {"q6k": 210, "q4k": 144, "q5k": 176}[kind] * (K // 256)
+
+    def part(r0, n):
+        sub = w[r0 * bpb:(r0 + n) * bpb]
+        return orc.q6k_isums(sub, xq_np, n, K) if kind == "q6k" else orc.q45_dots(kind, sub, xq_np, n, K)
+    futs = [_pool().submit(part, r0, n) for r0, n in _row_chunks(rows)]
+    return np.concatenate([f.result() for f in futs], axis=1)
+
+
+def check_all_rows(kind: str, w: np.ndarray, xq_np: np.ndarray, got: np.ndarray, rows: int, K: int,
+                   what: str = "") -> None:
+    """Every output of a full-size product against the oracle (tolerance
+    rule above)."""
+    ref, ab = oracle_all_rows(kind, w, xq_np, rows, K)
+    assert_close(got, ref, ab, what or f"{kind} {rows}x{K} all rows")

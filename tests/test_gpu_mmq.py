@@ -2,7 +2,7 @@
 through the C ABI, against the CPU oracle and against the decode product.
 
 Bars: fp32 outputs within 1e-5 of the oracle relative to the sum of
-absolute terms (all rows on small shapes, sampled rows at full size); every
+absolute terms (every row and column, small and full sizes); every
 column bit-for-bit equal to the decode product (mmvq_q6k, at most eight
 columns) of the same column; column-planar activations bit-for-bit equal to
 Q8_1 blocks.  The shapes take every batch width and launch shape (16
@@ -16,7 +16,8 @@ import torch
 
 import oracle as orc
 from quant_mat_vec_amd import qmv, synth
-from tests.gpu_util import DEV, assert_close, canaries_intact, dev, guarded, host, mmvq, note, quantize, tiled
+from tests.gpu_util import (DEV, assert_close, canaries_intact, check_all_rows, dev, guarded, host, mmvq, note,
+                            quantize, tiled)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,15 +50,6 @@ def decode_columns(w, xq, rows, K, ncols):
     parts = [mmvq("q6k", w, xq[c * nb:(c + min(8, ncols - c)) * nb], rows, K, min(8, ncols - c), TL)
              for c in range(0, ncols, 8)]
     return np.concatenate(parts)
-
-
-def sampled(rows, g, n=40):
-    return sorted(set(g.choice(rows, size=min(n, rows), replace=False).tolist()) | {0, rows - 1})
-
-
-def rows_of(w, rs, K):
-    nb = K // 256 * 210
-    return np.concatenate([w[r * nb:(r + 1) * nb] for r in rs])
 
 
 # (rows, K, ncols): K = 512 one wave along K (two batches + 1), 768 two
@@ -129,7 +121,7 @@ FULL = [(10240, 2560, 512), (10240, 2560, 70), (2560, 10240, 100), (151936, 2560
 
 
 @pytest.mark.parametrize("rows,K,ncols", FULL)
-def test_mmq_full_size_sampled(rows, K, ncols):
+def test_mmq_full_size_all_rows(rows, K, ncols):
     note(f"mmq_q6k full size {rows}x{K} N={ncols}")
     g = synth.rng(synth.seed_for(13, rows % 101, ncols))
     w = synth.q6k_blocks(g, rows, K)
@@ -137,10 +129,7 @@ def test_mmq_full_size_sampled(rows, K, ncols):
     x = synth.activations(g, ncols, K)
     xq, xq_np = quantize(x)
     got = mmq(wt, xq, rows, K, ncols)
-    rs = sampled(rows, g)
-    cs = sorted(set(g.choice(ncols, size=min(12, ncols), replace=False).tolist()) | {0, ncols - 1})
-    ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np[cs], len(rs), K)
-    assert_close(got[cs][:, rs], ref, ab, f"mmq {rows}x{K} N={ncols} sampled")
+    check_all_rows("q6k", w, xq_np, got, rows, K, f"mmq {rows}x{K} N={ncols} all rows and columns")
     assert np.array_equal(got.view(np.uint32), decode_columns(wt, xq, rows, K, ncols).view(np.uint32))
     gp = mmq(wt, quantize_planar(x), rows, K, ncols, XT)
     assert np.array_equal(gp.view(np.uint32), got.view(np.uint32))

@@ -4,7 +4,7 @@ Bars: bit-exact for the Q8_1 quantizer, the per-sub-block int32 sums, the
 planar conversion and every layout/column-count identity; fp32 outputs within
 1e-5 of the oracle relative to the sum of absolute terms (tests/gpu_util.py).
 Sizes: small ragged cases the oracle checks element by element, and the
-workloads' full sizes checked on sampled rows.
+workloads' full sizes checked on every row (the oracle spread over host threads).
 """
 import numpy as np
 import pytest
@@ -12,8 +12,8 @@ import torch
 
 import oracle as orc
 from quant_mat_vec_amd import qmv, synth
-from tests.gpu_util import (DEV, assert_close, dev, guarded, canaries_intact, host, isums, mmvq, note,
-                            planar, quantize)
+from tests.gpu_util import (DEV, assert_close, check_all_rows, dev, guarded, canaries_intact, host, isums, mmvq,
+                            note, planar, quantize)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,26 @@ def test_quantize_q8_1_bitexact(K, ncols):
     x[-1, 32:64] = np.float32(3e-8)            # d falls in the fp16 subnormal range
     _, got = quantize(x)
     assert np.array_equal(got, orc.quantize_q8_1(x))
+
+
+@pytest.mark.parametrize("planar_out", [False, True])
+def test_quantize_q8_1_ties(planar_out):
+    """Blocks whose quotients x/d sit at or next to half-integers, and blocks
+    whose fp32 product d * sum is an fp16 midpoint (the sum field must round
+    the fp32 product, not the exact one): bytes equal to the oracle's."""
+    from tests.q8_fixtures import near_tie_blocks, s_tie_blocks
+    for x in (near_tie_blocks(), s_tie_blocks()):
+        K = x.shape[1]
+        note(f"quantize_q8_1 ties K={K} planar={planar_out}")
+        ref = orc.quantize_q8_1(x)
+        xd = dev(x)
+        xq = torch.empty(K // 32 * 36, dtype=torch.uint8, device=DEV)
+        if planar_out:
+            qmv.quantize_q8_1_planar(xd, xq, K, 1)
+            ref = orc.q8_1_to_planar(ref, K)
+        else:
+            qmv.quantize_q8_1(xd, xq, K, 1)
+        assert np.array_equal(host(xq).reshape(ref.shape), ref)
 
 
 def test_quantize_q8_1_ties_golden():
@@ -152,14 +172,14 @@ def test_every_column_count(kind, ncols):
 def test_ten_wave_launch_two_chunks():
     """Long rows in one-workgroup-per-CU launches: 64 lanes per row, two full
     register chunks and several LDS sub-tiles per row (K = 20480)."""
-    note("Q6_K 2240x20480 N=8 (ten-wave workgroups, two chunks, LDS sub-tiles), sampled")
+    note("Q6_K 2240x20480 N=8 (ten-wave workgroups, two chunks, LDS sub-tiles), all rows")
     rows, K = 2240, 20480
     g = synth.rng(720)
     w = synth.q6k_blocks(g, rows, K)
     xq, xq_np = quantize(synth.activations(g, 8, K))
     wd = dev(w)
     got = mmvq("q6k", planar(wd, rows, K), xq, rows, K, 8, PL)
-    check_sampled("q6k", w, xq_np, got, rows, K, g)
+    check_all_rows("q6k", w, xq_np, got, rows, K)
     got_g = mmvq("q6k", wd, xq, rows, K, 8, GG)
     assert np.array_equal(got_g.view(np.uint32), got.view(np.uint32)), "planar != GGUF bits"
 
@@ -177,23 +197,9 @@ def test_repack_bytes_and_roundtrip(rows, K):
     assert np.array_equal(host(back), w)
 
 
-# ------------------------------------------------- full sizes, sampled
-def sampled_rows(rows, g, n=40):
-    r = set(g.choice(rows, size=min(n, rows), replace=False).tolist()) | {0, rows - 1}
-    return sorted(r)
-
-
-def check_sampled(kind, w, xq_np, got, rows, K, g):
-    """Oracle on ~40 sampled rows (always the first and last); the
-    per-column criterion is taken over the sampled rows."""
-    rs = sampled_rows(rows, g)
-    refs, abss = zip(*(orc.mmvq(kind, w, xq_np, rows, K, row0=r, nrows=1) for r in rs))
-    ref, ab = np.concatenate(refs, axis=1), np.concatenate(abss, axis=1)
-    assert_close(got[:, rs], ref, ab, f"{kind} {rows}x{K} sampled rows")
-
-
+# ----------------------------------------------- full sizes, every row
 @pytest.mark.parametrize("rows,K", [(10240, 2560), (2560, 10240), (2560, 2560)])
-def test_q6k_full_size_sampled(rows, K):
+def test_q6k_full_size_all_rows(rows, K):
     note(f"full-size Q6_K {rows}x{K}")
     g = synth.rng(synth.seed_for(1, 0 if rows == 2560 and K == 10240 else 1, 8))
     w = synth.q6k_blocks(g, rows, K)
@@ -207,7 +213,7 @@ def test_q6k_full_size_sampled(rows, K):
         got = mmvq("q6k", pd, xq[:n * nb], rows, K, n, PL)
         if full is None:
             full = got
-            check_sampled("q6k", w, xq_np, got, rows, K, g)
+            check_all_rows("q6k", w, xq_np, got, rows, K)
             got_g = mmvq("q6k", wd, xq, rows, K, 8, GG)
             assert np.array_equal(got_g.view(np.uint32), got.view(np.uint32))
         else:
@@ -226,19 +232,19 @@ def test_lm_head_planar_equals_interleaved(ncols):
     got_p = mmvq("q6k", pd, xq, rows, K, ncols, PL)
     got_g = mmvq("q6k", wd, xq, rows, K, ncols, GG)
     assert np.array_equal(got_p.view(np.uint32), got_g.view(np.uint32))
-    check_sampled("q6k", w, xq_np, got_p, rows, K, g)
+    check_all_rows("q6k", w, xq_np, got_p, rows, K)
 
 
 @pytest.mark.parametrize("rows,K", [(12288, 2560), (6144, 2560), (2560, 6144), (512, 2560)])
 @pytest.mark.parametrize("kind", ["q4k", "q5k"])
-def test_q45_full_size_sampled(rows, K, kind):
+def test_q45_full_size_all_rows(rows, K, kind):
     note(f"full-size {kind} {rows}x{K}")
     g = synth.rng(synth.seed_for(3, rows % 97, 4))
     w = synth.blocks(kind, g, rows, K)
     wd = dev(w)
     xq, xq_np = quantize(synth.activations(g, 4, K))
     got4 = mmvq(kind, wd, xq, rows, K, 4)
-    check_sampled(kind, w, xq_np, got4, rows, K, g)
+    check_all_rows(kind, w, xq_np, got4, rows, K)
     got1 = mmvq(kind, wd, xq, rows, K, 1)
     assert np.array_equal(got1[0].view(np.uint32), got4[0].view(np.uint32))
 
@@ -295,7 +301,7 @@ def run_moe(m, xq, ids, rw, T, layout=PL, wg=None, wu=None, wdn=None):
     return host(out).reshape(T, DM), host(ws)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("T", range(1, 9))
 def test_moe_staged_parity(moe, T):
     note(f"grouped_expert_mmvq T={T}")
     g = synth.rng(synth.seed_for(4, 1, T))
@@ -422,11 +428,23 @@ def test_moe_out_of_range_id_is_skipped(moe):
     bad[1, 3] = E + 5
     out, ws = run_moe(moe, xq, bad, rw, T)
     assert ws[:8].view(np.int32)[1] == 1
+    # the oracle chained on the GPU's requantized h, the bad slot given
+    # weight 0 and an all-zero hq (so it adds exactly 0): out within the
+    # tolerance rule, like the staged parity
+    L = qmv.moe_workspace_layout(T, TOPK, DM, DFF)
+    S = T * TOPK
+    hq = ws[L["hq"]:L["hq"] + 36 * S * DFF // 32].reshape(S, -1).copy()
+    hq[1 * TOPK + 3] = 0
     rw0 = rw.copy()
     rw0[1, 3] = 0.0
-    res = orc.grouped_expert(moe["gate"], moe["up"], moe["down"], xq_np, ids, rw0, E, T, TOPK, DM, DFF)
-    # the oracle chain requantizes its own h, so compare at the end-to-end level
-    assert np.abs(out - res["out"]).max() <= 1e-2 * np.abs(res["out"]).max()
+    res = orc.grouped_expert(moe["gate"], moe["up"], moe["down"], xq_np, ids, rw0, E, T, TOPK, DM, DFF,
+                             hq_in=hq)
+    assert_close(out, res["out"], res["out_absum"], "out with an out-of-range id")
+    # the other slots' requantized h are still those of the GPU's own h
+    h = ws[L["h"]:L["h"] + 4 * S * DFF].view(np.float32).reshape(S, DFF)
+    for s in range(S):
+        if s != 1 * TOPK + 3:
+            assert np.array_equal(hq[s], orc.quantize_q8_1(h[s][None])[0]), f"hq slot {s}"
 
 
 @pytest.mark.parametrize("T", [2, 3])

@@ -6,7 +6,7 @@ back to GGUF), the per-sub-block int32 sums and the column-count identities;
 fp32 outputs within 1e-5 of the oracle relative to the sum of absolute terms.
 The sizes cover every workgroup shape the kernel picks by row length (1, 2,
 4, 8 and 16 waves along K), partial last tiles and workgroups, ragged and
-multi-chunk rows, each against the oracle on sampled rows at full size.
+multi-chunk rows, each against the oracle on every row at full size.
 """
 import numpy as np
 import pytest
@@ -14,7 +14,8 @@ import torch
 
 import oracle as orc
 from quant_mat_vec_amd import qmv, synth
-from tests.gpu_util import DEV, assert_close, dev, host, isums, mmvq, note, planar, quantize, tiled
+from tests.gpu_util import (DEV, assert_close, check_all_rows, dev, host, isums, mmvq, note, oracle_all_rows,
+                            oracle_isums_all_rows, planar, quantize, tiled)
 
 pytestmark = pytest.mark.gpu
 
@@ -25,15 +26,6 @@ TL, PL, GG = qmv.LAYOUT_TILED, qmv.LAYOUT_PLANAR, qmv.LAYOUT_GGUF
 def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     qmv.lib()                      # fails loudly if the HIP library is missing
-
-
-def sampled(rows, g, n=40):
-    return sorted(set(g.choice(rows, size=min(n, rows), replace=False).tolist()) | {0, rows - 1})
-
-
-def rows_of(w, rs, K):
-    nb = K // 256 * 210
-    return np.concatenate([w[r * nb:(r + 1) * nb] for r in rs])
 
 
 # ------------------------------------------------------------ conversion
@@ -119,20 +111,18 @@ FULL = [(32805, 256, (8, 1)), (16405, 512, (5, 2)), (4100, 1280, (3, 8)), (10240
 
 
 @pytest.mark.parametrize("rows,K,cols", FULL)
-def test_tiled_full_size_sampled(rows, K, cols):
+def test_tiled_full_size_all_rows(rows, K, cols):
     note(f"tiled full size {rows}x{K} N={cols}")
     g = synth.rng(synth.seed_for(4, rows % 101, 8))
     w = synth.q6k_blocks(g, rows, K)
     wt = tiled(dev(w), rows, K)
     xq, xq_np = quantize(synth.activations(g, 8, K))
-    rs = sampled(rows, g)
-    ws = rows_of(w, rs, K)
-    ref, ab = orc.mmvq("q6k", ws, xq_np, len(rs), K)
+    ref, ab = oracle_all_rows("q6k", w, xq_np[:max(cols)].reshape(-1), rows, K)
     nb = K // 32 * 36
     first = None
     for n in cols:
         got = mmvq("q6k", wt, xq[:n * nb], rows, K, n, TL)
-        assert_close(got[:, rs], ref[:n], ab[:n], f"tiled {rows}x{K} N={n} sampled rows")
+        assert_close(got, ref[:n], ab[:n], f"tiled {rows}x{K} N={n} all rows")
         if first is None:
             first = got
         else:
@@ -141,14 +131,13 @@ def test_tiled_full_size_sampled(rows, K, cols):
 
 
 @pytest.mark.parametrize("rows,K,ncols", [(10240, 2560, 8), (2560, 10240, 4), (32805, 256, 3)])
-def test_tiled_isums_full_size_sampled(rows, K, ncols):
+def test_tiled_isums_full_size_all_rows(rows, K, ncols):
     note(f"tiled isums full size {rows}x{K} N={ncols}")
     g = synth.rng(synth.seed_for(5, rows % 101, ncols))
     w = synth.q6k_blocks(g, rows, K)
     xq, xq_np = quantize(synth.activations(g, ncols, K))
     got = isums("q6k", tiled(dev(w), rows, K), xq, rows, K, ncols, TL)
-    rs = sampled(rows, g)
-    assert np.array_equal(got[:, rs], orc.q6k_isums(rows_of(w, rs, K), xq_np, len(rs), K))
+    assert np.array_equal(got, oracle_isums_all_rows("q6k", w, xq_np, rows, K))
 
 
 def test_tiled_agrees_with_planar():
@@ -163,9 +152,7 @@ def test_tiled_agrees_with_planar():
     pt, pp = tiled(wd, rows, K), planar(wd, rows, K)
     assert np.array_equal(isums("q6k", pt, xq, rows, K, ncols, TL), isums("q6k", pp, xq, rows, K, ncols, PL))
     a, b = mmvq("q6k", pt, xq, rows, K, ncols, TL), mmvq("q6k", pp, xq, rows, K, ncols, PL)
-    rs = sampled(rows, g)
-    ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np, len(rs), K)
-    assert_close(a[:, rs], ref, ab, "tiled")
+    check_all_rows("q6k", w, xq_np, a, rows, K, "tiled")
     assert np.all(np.abs(a.astype(np.float64) - b) <= 3e-5 * np.abs(b).max(axis=-1, keepdims=True))
 
 
@@ -254,10 +241,12 @@ def test_argmax_matches_own_outputs_and_oracle(rows, K, ncols):
     out, idx, val = run(wb)
     assert np.array_equal(idx, np.argmax(out, axis=1))
     assert np.array_equal(val.view(np.uint32), out[np.arange(ncols), idx].view(np.uint32))
-    rs = sorted(set(sampled(rows, g, 20)) | set(idx.tolist()))
-    ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np, len(rs), K)
+    # against the oracle on every row: the outputs within tolerance, and the
+    # chosen row's exact value within tolerance of the exact maximum
+    ref, ab = oracle_all_rows("q6k", w, xq_np, rows, K)
+    assert_close(out, ref, ab, f"argmax product {rows}x{K} N={ncols}")
     best = ref.max(axis=1)
-    chosen = ref[np.arange(ncols), [rs.index(i) for i in idx]]
+    chosen = ref[np.arange(ncols), idx]
     assert np.all(chosen >= best - 2e-5 * ab.max(axis=1))
     if rows > 1 and idx[0] > 0:
         w2 = wb.copy()
@@ -313,7 +302,7 @@ def test_planar_activations_match_blocks_bitexact(rows, K, ncols):
                                          (8200, 20480, (2,))])
 def test_planar_activations_full_size(rows, K, cols):
     """Full sizes (every launch shape): bits equal to the Q8_1-block path,
-    sampled rows within the oracle tolerance."""
+    every row within the oracle tolerance."""
     g = synth.rng(980 + rows)
     w = synth.q6k_blocks(g, rows, K)
     wt = tiled(dev(w), rows, K)
@@ -325,9 +314,7 @@ def test_planar_activations_full_size(rows, K, cols):
         a = mmvq("q6k", wt, xq, rows, K, n, TL)
         b = mmvq("q6k", wt, xp, rows, K, n, XT)
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-        rs = sampled(rows, g, 24)
-        ref, ab = orc.mmvq("q6k", rows_of(w, rs, K), xq_np[:n].reshape(-1), len(rs), K)
-        assert_close(b[:, rs], ref, ab, f"act_planar {rows}x{K} N={n}")
+        check_all_rows("q6k", w, xq_np[:n].reshape(-1), b, rows, K, f"act_planar {rows}x{K} N={n}")
 
 
 @pytest.mark.parametrize("rows,K,ncols", [(151936, 2560, 4), (1000, 2560, 1), (37, 768, 8)])

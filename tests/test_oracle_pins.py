@@ -15,6 +15,7 @@ import pytest
 
 import oracle as orc
 from quant_mat_vec_amd import synth
+from tests.q8_fixtures import near_tie_blocks, numpy_q8_1, s_tie_blocks
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -307,78 +308,6 @@ def test_q8_1_scale_and_sign_symmetry():
 
 
 # ------------------------------------------ Q8_1 vs an independent numpy quantizer
-def numpy_q8_1(x, mode="div32"):
-    """Q8_1 written here from the quantizer reading, with numpy's IEEE fp32
-    arithmetic: amax = max|x|, d = amax/127 (fp32 division), q =
-    round-half-away-from-zero(x/d) with x/d an fp32 division, clamped to
-    +-127 (all zero when d == 0), stored d = fp16(d), s = fp16(d * sum q)
-    (fp32 product), both rounded to nearest even by numpy's cast.  `mode`
-    selects a deliberately wrong variant to show that the fixtures below tell
-    them apart: "recip" (x times the fp32 reciprocal of d), "div64" (x/d in
-    fp64) and "even" (ties to even)."""
-    x = np.ascontiguousarray(x, np.float32)
-    ncols, K = x.shape
-    xb = x.reshape(ncols, K // 32, 32)
-    amax = np.abs(xb).max(-1)
-    d = amax / np.float32(127)
-    assert d.dtype == np.float32
-    dz = np.where(d > 0, d, np.float32(1))[..., None]
-    if mode == "recip":
-        v = (xb * (np.float32(1) / dz)).astype(np.float64)
-    elif mode == "div64":
-        v = xb.astype(np.float64) / dz.astype(np.float64)
-    else:
-        v = (xb / dz).astype(np.float64)
-    if mode == "even":
-        q = np.rint(v)
-    else:
-        q = np.sign(v) * np.floor(np.abs(v) + 0.5)       # exact in fp64
-    q = np.clip(q, -127, 127)
-    q[d == 0] = 0
-    q = q.astype(np.int8)
-    s = d * q.astype(np.int32).sum(-1).astype(np.float32)
-    assert s.dtype == np.float32
-    out = np.zeros((ncols, K // 32, 36), np.uint8)
-    out[..., 0:2] = d.astype(np.float16).view(np.uint8).reshape(ncols, K // 32, 2)
-    out[..., 2:4] = s.astype(np.float16).view(np.uint8).reshape(ncols, K // 32, 2)
-    out[..., 4:] = q.view(np.uint8)
-    return out.reshape(ncols, -1)
-
-
-def near_tie_blocks(seed=31, nblocks=512):
-    """fp32 activations whose quotient x/d lies at or within a few ulps of a
-    half-integer k + 1/2, chosen where an fp32 division, a multiply by the
-    fp32 reciprocal and an fp64 division round to different codes, plus exact
-    ties for the tie rule.  Each block holds its amax first (so d is fixed)
-    and 31 such values."""
-    g = synth.rng(seed)
-    picked = []
-    while len(picked) < nblocks:
-        amax = np.float32(np.exp2(g.uniform(-8, 8)) * (1 + g.random()))
-        d = amax / np.float32(127)
-        r = np.float32(1) / d
-        vals = []
-        for k in g.integers(0, 126, 64):
-            x0 = np.float32((k + 0.5) * float(d))
-            for j in range(-3, 4):
-                x = x0
-                for _ in range(abs(j)):
-                    x = np.nextafter(x, np.float32(np.inf if j > 0 else -np.inf))
-                q32 = float(x / d)
-                a = np.floor(abs(q32) + 0.5)
-                b = np.floor(abs(float(x * r)) + 0.5)
-                c = np.floor(abs(float(x) / float(d)) + 0.5)
-                e = np.rint(abs(q32))
-                if a != b or a != c or a != e:
-                    vals.append(x if g.random() < 0.5 else -x)
-        if len(vals) >= 31:
-            blk = np.zeros(32, np.float32)
-            blk[0] = amax if g.random() < 0.5 else -amax
-            blk[1:] = np.asarray(vals[:31], np.float32)
-            picked.append(blk)
-    return np.concatenate(picked).reshape(1, -1)
-
-
 def test_q8_1_vs_independent_numpy_random():
     g = synth.rng(41)
     x = synth.activations(g, 6, 2560)
@@ -402,6 +331,19 @@ def test_q8_1_near_ties_decide_the_division_reading():
         assert not np.array_equal(other, ref), mode
         nq = np.count_nonzero(other.reshape(-1, 36)[:, 4:] != ref.reshape(-1, 36)[:, 4:])
         assert nq >= 50, (mode, nq)
+
+
+def test_q8_1_sum_field_rounds_the_fp32_product():
+    """s = fp16(fp32(d * sum)): on blocks where the fp32 product is an fp16
+    midpoint but the exact product is not, the two roundings differ; the
+    oracle must take the fp32 product (a fused multiply-convert would fail)."""
+    x = s_tie_blocks()
+    ref = numpy_q8_1(x)
+    assert np.array_equal(orc.quantize_q8_1(x), ref)
+    fused = numpy_q8_1(x, "fused_s").reshape(-1, 36)
+    r = ref.reshape(-1, 36)
+    assert np.array_equal(fused[:, 4:], r[:, 4:]) and np.array_equal(fused[:, :2], r[:, :2])
+    assert np.count_nonzero((fused[:, 2:4] != r[:, 2:4]).any(-1)) == len(r)   # every block's s differs
 
 
 # ------------------------------------------ exhaustive decoders vs numpy
