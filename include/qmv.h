@@ -290,6 +290,24 @@ int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down
                         void *stream);
 size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff);
 
+/* grouped_expert_mmvq without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid allocation): the same kernels, arguments, checks and
+ * results, with the workspace taken from a 4 MiB device array that the
+ * library holds on every GPU it runs on until the process ends.  Calls whose
+ * workspace would exceed 4 MiB (grouped_expert_mmvq_workspace() > 4194304)
+ * return QMV_ERR_UNSUPPORTED before any HIP call.  The array of the calling
+ * thread's current device is used (`stream` must belong to that device);
+ * its address is looked up on the first call on each device.  Nothing in it
+ * needs clearing between calls (every call writes what it reads), but every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (on different streams, or from several threads) race and must not be
+ * issued. */
+int grouped_expert_mmvq_noalloc(const void *w_gate, const void *w_up, const void *w_down,
+                                int down_layout, const void *xq, const int32_t *ids,
+                                const float *route_w, float *out, int E, int T, int topk,
+                                int64_t d_model, int64_t d_ff, void *stream);
+
 /* Diagnostics. */
 /* Streaming-read calibration: reads `bytes` (a multiple of 16) from src
  * (16-byte aligned) with 16-byte non-temporal loads, four per thread per

@@ -92,6 +92,50 @@ int check_repack(const void *src, const void *dst, int64_t rows, int64_t K, uint
     return QMV_OK;
 }
 
+// Checks shared by the grouped MoE entry points (all but the workspace).
+int check_moe(const void *w_gate, const void *w_up, const void *w_down, int down_layout, const void *xq,
+              const int32_t *ids, const float *route_w, const float *out, int E, int T, int topk, int64_t d_model,
+              int64_t d_ff) {
+    if (!w_gate || !w_up || !w_down || !xq || !ids || !route_w || !out) return QMV_ERR_INVALID_ARG;
+    if (E < 1 || T < 1 || topk < 1 || d_model <= 0 || d_ff <= 0) return QMV_ERR_INVALID_ARG;
+    if (T > 8 || topk > 8 || d_model % 256 || d_ff % 256 || d_model > kMaxK || d_ff > kMaxK)
+        return QMV_ERR_UNSUPPORTED;
+    if (down_layout != QMV_LAYOUT_GGUF && down_layout != QMV_LAYOUT_PLANAR) return QMV_ERR_UNSUPPORTED;
+    const int64_t gu_bytes = (int64_t)E * d_ff * (d_model / 256) * 144;
+    const int64_t dn_bytes = (int64_t)E * d_model * (d_ff / 256) * 210;
+    if (gu_bytes >= kMaxBytes || dn_bytes >= kMaxBytes || (int64_t)E * d_model > kMaxRows)
+        return QMV_ERR_UNSUPPORTED;
+    if (!qmv::moe_grid_fits(T * topk, d_model, d_ff, kMaxGridY)) return QMV_ERR_UNSUPPORTED;
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, down_layout == QMV_LAYOUT_PLANAR ? 16 : 4) ||
+        !aligned(xq, 4) || !aligned(ids, 4) || !aligned(route_w, 4) || !aligned(out, 4))
+        return QMV_ERR_ALIGNMENT;
+    return QMV_OK;
+}
+
+int run_moe(const void *w_gate, const void *w_up, const void *w_down, int down_layout, const void *xq,
+            const int32_t *ids, const float *route_w, float *out, int E, int T, int topk, int64_t d_model,
+            int64_t d_ff, void *ws, const qmv::MoeLayout &L, void *stream) {
+    qmv::MoeArgs m;
+    m.w_gate = reinterpret_cast<const uint8_t *>(w_gate);
+    m.w_up = reinterpret_cast<const uint8_t *>(w_up);
+    m.w_down = reinterpret_cast<const uint8_t *>(w_down);
+    m.xq = reinterpret_cast<const uint8_t *>(xq);
+    m.ids = ids;
+    m.route_w = route_w;
+    m.out = out;
+    m.ws = reinterpret_cast<uint8_t *>(ws);
+    m.E = E;
+    m.T = T;
+    m.topk = topk;
+    m.S = T * topk;
+    m.d_model = d_model;
+    m.d_ff = d_ff;
+    m.off_h = L.off_h;
+    m.off_hq = L.off_hq;
+    m.off_y = L.off_y;
+    return from_hip(qmv::launch_moe(m, down_layout, as_stream(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -252,41 +296,30 @@ size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, in
 int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down, int down_layout,
                         const void *xq, const int32_t *ids, const float *route_w, float *out, int E, int T,
                         int topk, int64_t d_model, int64_t d_ff, void *ws, size_t ws_bytes, void *stream) {
-    if (!w_gate || !w_up || !w_down || !xq || !ids || !route_w || !out) return QMV_ERR_INVALID_ARG;
-    if (E < 1 || T < 1 || topk < 1 || d_model <= 0 || d_ff <= 0) return QMV_ERR_INVALID_ARG;
-    if (T > 8 || topk > 8 || d_model % 256 || d_ff % 256 || d_model > kMaxK || d_ff > kMaxK)
-        return QMV_ERR_UNSUPPORTED;
-    if (down_layout != QMV_LAYOUT_GGUF && down_layout != QMV_LAYOUT_PLANAR) return QMV_ERR_UNSUPPORTED;
-    const int64_t gu_bytes = (int64_t)E * d_ff * (d_model / 256) * 144;
-    const int64_t dn_bytes = (int64_t)E * d_model * (d_ff / 256) * 210;
-    if (gu_bytes >= kMaxBytes || dn_bytes >= kMaxBytes || (int64_t)E * d_model > kMaxRows)
-        return QMV_ERR_UNSUPPORTED;
-    if (!qmv::moe_grid_fits(T * topk, d_model, d_ff, kMaxGridY)) return QMV_ERR_UNSUPPORTED;
-    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, down_layout == QMV_LAYOUT_PLANAR ? 16 : 4) ||
-        !aligned(xq, 4) || !aligned(ids, 4) || !aligned(route_w, 4) || !aligned(out, 4))
-        return QMV_ERR_ALIGNMENT;
+    int rc = check_moe(w_gate, w_up, w_down, down_layout, xq, ids, route_w, out, E, T, topk, d_model, d_ff);
+    if (rc) return rc;
     const qmv::MoeLayout L = qmv::moe_layout(T, topk, d_model, d_ff);
     if (!ws || ws_bytes < (size_t)L.total) return QMV_ERR_WORKSPACE;
     if (!aligned(ws, 256)) return QMV_ERR_ALIGNMENT;
-    qmv::MoeArgs m;
-    m.w_gate = reinterpret_cast<const uint8_t *>(w_gate);
-    m.w_up = reinterpret_cast<const uint8_t *>(w_up);
-    m.w_down = reinterpret_cast<const uint8_t *>(w_down);
-    m.xq = reinterpret_cast<const uint8_t *>(xq);
-    m.ids = ids;
-    m.route_w = route_w;
-    m.out = out;
-    m.ws = reinterpret_cast<uint8_t *>(ws);
-    m.E = E;
-    m.T = T;
-    m.topk = topk;
-    m.S = T * topk;
-    m.d_model = d_model;
-    m.d_ff = d_ff;
-    m.off_h = L.off_h;
-    m.off_hq = L.off_hq;
-    m.off_y = L.off_y;
-    return from_hip(qmv::launch_moe(m, down_layout, as_stream(stream)));
+    return run_moe(w_gate, w_up, w_down, down_layout, xq, ids, route_w, out, E, T, topk, d_model, d_ff, ws, L,
+                   stream);
+}
+
+int grouped_expert_mmvq_noalloc(const void *w_gate, const void *w_up, const void *w_down, int down_layout,
+                                const void *xq, const int32_t *ids, const float *route_w, float *out, int E,
+                                int T, int topk, int64_t d_model, int64_t d_ff, void *stream) {
+    int rc = check_moe(w_gate, w_up, w_down, down_layout, xq, ids, route_w, out, E, T, topk, d_model, d_ff);
+    if (rc) return rc;
+    const qmv::MoeLayout L = qmv::moe_layout(T, topk, d_model, d_ff);
+    if (L.total > qmv::kMoeScratchBytes) return QMV_ERR_UNSUPPORTED;
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return from_hip(e);
+    void *ws = nullptr;
+    e = qmv::moe_scratch(device, &ws);
+    if (e != hipSuccess) return from_hip(e);
+    return run_moe(w_gate, w_up, w_down, down_layout, xq, ids, route_w, out, E, T, topk, d_model, d_ff, ws, L,
+                   stream);
 }
 
 int qmv_stream_read(const void *src, int64_t bytes, uint32_t *sink, int blocks, void *stream) {

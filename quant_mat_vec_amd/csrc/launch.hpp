@@ -71,6 +71,12 @@ struct MoeLayout {
 MoeLayout moe_layout(int T, int topk, int64_t d_model, int64_t d_ff);
 
 hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s);
+
+// Bytes of the per-device scratch array of grouped_expert_mmvq_noalloc, and
+// its device address on `device` (the calling thread's current device),
+// looked up on the first call for that device.
+constexpr int64_t kMoeScratchBytes = 4LL << 20;
+hipError_t moe_scratch(int device, void **ptr);
 // Whether every launch of launch_moe for S slots stays within max_grid_y
 // workgroups along y (host arithmetic only).
 bool moe_grid_fits(int S, int64_t d_model, int64_t d_ff, int64_t max_grid_y);

@@ -14,10 +14,37 @@
 // The selection is one wave ballot over the slot ids (S <= 64 = one wave),
 // and an expert's slots are taken in ascending slot order.  No workgroup
 // reads the weights of an expert no slot is routed to.
+#include <mutex>
+
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace qmv {
+
+// Device scratch for grouped_expert_mmvq_noalloc: the routed chain's
+// workspace when the caller cannot allocate one.  In host code `scratch`
+// only stands for the symbol; its device address (one copy per GPU) comes
+// from hipGetSymbolAddress, looked up once per device and kept.
+static __device__ __align__(256) uint8_t scratch[kMoeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void *g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t moe_scratch(int device, void **ptr) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[device], [device] {
+        // (the calling thread's current device is `device`)
+        void *p = nullptr;
+        g_scratch_err[device] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[device] = g_scratch_err[device] == hipSuccess ? p : nullptr;
+    });
+    *ptr = g_scratch_ptr[device];
+    return g_scratch_err[device];
+}
 
 namespace {
 __host__ __device__ inline int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }

@@ -58,6 +58,7 @@ def lib() -> ctypes.CDLL:
             "mmvq_q4k_isums": [P, P, P, I64, I64, I, P],
             "mmvq_q5k_isums": [P, P, P, I64, I64, I, P],
             "grouped_expert_mmvq": [P, P, P, I, P, P, P, P, I, I, I, I64, I64, P, SZ, P],
+            "grouped_expert_mmvq_noalloc": [P, P, P, I, P, P, P, P, I, I, I, I64, I64, P],
             "qmv_stream_read": [P, I64, P, I, P],
         }
         for name, args in sig.items():
@@ -201,6 +202,13 @@ def grouped_expert_mmvq(w_gate, w_up, w_down, down_layout: int, xq, ids, route_w
     _check(lib().grouped_expert_mmvq(_ptr(w_gate), _ptr(w_up), _ptr(w_down), down_layout, _ptr(xq), _ptr(ids),
                                      _ptr(route_w), _ptr(out), E, T, topk, d_model, d_ff, _ptr(ws), ws_bytes,
                                      _stream(stream)), "grouped_expert_mmvq")
+
+
+def grouped_expert_mmvq_noalloc(w_gate, w_up, w_down, down_layout: int, xq, ids, route_w, out, E: int, T: int,
+                                topk: int, d_model: int, d_ff: int, stream=None) -> None:
+    _check(lib().grouped_expert_mmvq_noalloc(_ptr(w_gate), _ptr(w_up), _ptr(w_down), down_layout, _ptr(xq),
+                                             _ptr(ids), _ptr(route_w), _ptr(out), E, T, topk, d_model, d_ff,
+                                             _stream(stream)), "grouped_expert_mmvq_noalloc")
 
 
 def qmv_stream_read(src, nbytes: int, sink, blocks: int, stream=None) -> None:

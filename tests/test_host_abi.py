@@ -224,6 +224,24 @@ def test_moe_rejects_and_workspace(L):
     assert call(wd=P + 8, lay=1) == E_ALN
 
 
+def test_moe_noalloc_rejects(L):
+    """The allocation-free MoE entry point: the same argument checks as the
+    workspace form, and windows whose workspace exceeds its 4 MiB array."""
+    f = L.grouped_expert_mmvq_noalloc
+
+    def call(**kw):
+        a = dict(wg=P, wu=P, wd=P, lay=1, xq=P, ids=P, rw=P, out=P, E=128, T=8, topk=8, dm=2560, dff=768)
+        a.update(kw)
+        return f(a["wg"], a["wu"], a["wd"], a["lay"], a["xq"], a["ids"], a["rw"], a["out"], a["E"], a["T"],
+                 a["topk"], a["dm"], a["dff"], None)
+
+    assert call(wg=None) == E_INV and call(out=None) == E_INV and call(E=0) == E_INV
+    assert call(T=9) == E_UNS and call(dff=700) == E_UNS and call(lay=qmv.LAYOUT_TILED) == E_UNS
+    assert call(wd=P + 8, lay=1) == E_ALN
+    assert L.grouped_expert_mmvq_workspace(128, 8, 8, 2560, 16384) > 4 << 20
+    assert call(dff=16384) == E_UNS
+
+
 def test_stream_read_rejects(L):
     f = L.qmv_stream_read
     assert f(None, 4096, P, 8, None) == E_INV
