@@ -172,6 +172,31 @@ int rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *x
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out,
              int64_t rows, int64_t K, int ncols, void *stream);
 
+/* One product of a batch (mmvq_q6k_batch): w, xq, out, rows and ncols as
+ * the arguments of mmvq_q6k of the same names. */
+typedef struct qmv_q6k_job {
+    const void *w;
+    const void *xq;
+    float *out;
+    int64_t rows;
+    int ncols;
+} qmv_q6k_job;
+
+/* Several independent Q6_K products of the same K in one launch -- the
+ * decode products of a layer's matrices (each with its own weights,
+ * activation columns and outputs), issued together so that the launch
+ * ramps up and drains once rather than once per matrix (the pages' decode
+ * step runs many such products back to back, PR #2207 "Issue: #1545, #1606
+ * (Arc A-series decode)", "Summary").  jobs: host array of njobs
+ * (1 <= njobs <= 8) descriptions, read during the call.  Tiled layout only
+ * (layout = QMV_LAYOUT_TILED, optionally | QMV_ACT_PLANAR, for every job);
+ * each job as for mmvq_q6k (w 16-byte aligned, xq 4-byte aligned or 16 for
+ * column-planar activations, out 4-byte aligned, 1 <= ncols <= 8) and the
+ * sum of the jobs' rows within the product limit.  Every job's output is
+ * bit for bit what mmvq_q6k gives for it alone.  Outputs of different jobs
+ * must not overlap each other or any input. */
+int mmvq_q6k_batch(const qmv_q6k_job *jobs, int njobs, int layout, int64_t K, void *stream);
+
 /* The same Q6_K x Q8_1 product for many columns at once (the prompt path,
  * which PR #2340 "What it changes" leaves as it is; the arithmetic is the
  * decode product's).  Tiled weights only: layout = QMV_LAYOUT_TILED,

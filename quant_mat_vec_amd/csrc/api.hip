@@ -192,6 +192,25 @@ int mmq_q6k(const void *w, int layout, const void *xq, float *out, int64_t rows,
     return from_hip(qmv::launch_mmq_q6_tiled(w, xq, out, rows, K, ncols, xp, as_stream(stream)));
 }
 
+int mmvq_q6k_batch(const qmv_q6k_job *jobs, int njobs, int layout, int64_t K, void *stream) {
+    if (!jobs || njobs < 1) return QMV_ERR_INVALID_ARG;
+    if (njobs > 8) return QMV_ERR_UNSUPPORTED;
+    const bool xp = (layout & QMV_ACT_PLANAR) != 0;
+    if ((layout & ~QMV_ACT_PLANAR) != QMV_LAYOUT_TILED) return QMV_ERR_UNSUPPORTED;
+    qmv::TiledJobDesc d[8];
+    int64_t total_rows = 0;
+    for (int j = 0; j < njobs; j++) {
+        const qmv_q6k_job &jb = jobs[j];
+        const int rc = check_mmvq(jb.w, jb.xq, jb.out, jb.rows, K, jb.ncols, 210, 16);
+        if (rc) return rc;
+        if (xp && !aligned(jb.xq, 16)) return QMV_ERR_ALIGNMENT;
+        total_rows += jb.rows;
+        d[j] = {jb.w, jb.xq, jb.out, jb.rows, jb.ncols};
+    }
+    if (total_rows > kMaxProductRows) return QMV_ERR_UNSUPPORTED;
+    return from_hip(qmv::launch_mmvq_q6_tiled_jobs(d, njobs, K, xp, as_stream(stream)));
+}
+
 int mmvq_q4k(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols, void *stream) {
     if (!out) return QMV_ERR_INVALID_ARG;
     return q45_dispatch(false, w, xq, out, nullptr, rows, K, ncols, stream);

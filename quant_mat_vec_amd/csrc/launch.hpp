@@ -33,6 +33,15 @@ hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int3
 // xp: activations in the column-planar Q8_1 layout
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump,
                                 int64_t rows, int64_t K, int ncols, bool xp, hipStream_t s);
+// independent products of the same K in one launch (checked by the caller)
+struct TiledJobDesc {
+    const void *w;
+    const void *xq;
+    float *out;
+    int64_t rows;
+    int ncols;
+};
+hipError_t launch_mmvq_q6_tiled_jobs(const TiledJobDesc *jobs, int njobs, int64_t K, bool xp, hipStream_t s);
 // any number of columns (batches of twelve or sixteen, then at most eight)
 hipError_t launch_mmq_q6_tiled(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols,
                                bool xp, hipStream_t s);

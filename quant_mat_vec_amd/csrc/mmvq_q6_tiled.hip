@@ -28,6 +28,21 @@ hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32
                 : tiled_cols<false, false>(w, xq, out, dump, rows, K, ncols, s);
 }
 
+hipError_t launch_mmvq_q6_tiled_jobs(const TiledJobDesc *jobs, int njobs, int64_t K, bool xp, hipStream_t s) {
+    TiledJobs js;
+    js.njobs = njobs;
+    js.K = K;
+    for (int j = 0; j < njobs; j++) {
+        js.job[j].w = jobs[j].w;
+        js.job[j].xq = reinterpret_cast<const uint8_t *>(jobs[j].xq);
+        js.job[j].out = jobs[j].out;
+        js.job[j].rows = jobs[j].rows;
+        js.job[j].ncols = jobs[j].ncols;
+        js.job[j].wg0 = 0;
+    }
+    return xp ? launch_tiled_jobs<true>(js, s) : launch_tiled_jobs<false>(js, s);
+}
+
 // Batched product of any number of columns: full batches in one launch,
 // the rest (fewer than a batch) as products of at most eight columns.
 hipError_t launch_mmq_q6_tiled(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols,

@@ -140,6 +140,91 @@ struct TiledLane {
     int xb[NCG];
 };
 
+// The arithmetic of one step of four sub-blocks for one wave: the codes of
+// its plane pieces (wa, wb), the four sub-blocks' scale bytes (sct) and the
+// block's d (dt), against the activation tile in LDS (lane entry xb[cg] +
+// 4*it; zt = the step's first tile block) -- two matrix-core products per
+// column group, then per sub-block the scales, d_a and d_w on the vector
+// ALU.  Accumulates into acc (DUMP: writes the per-sub-block sums of step
+// z instead).  Every product path of the tiled layout runs its steps through
+// this function, so a column's sum is the same sequence of operations in
+// each.
+template <int N, int NCG, int TNB, int IT, bool DUMP, bool XP>
+__device__ __forceinline__ void tiled_step(uint4 wa, uint2 wb, uint2 sct, uint32_t dt, const int (&xb)[NCG], int it,
+                                           int zt, uint8_t *lds, int kg, const MmvqArgs &a, int64_t row, bool rok,
+                                           int z, float (&acc)[NCG]) {
+    constexpr int XE = N * TNB + 4 * (IT - 1) + 1;  // entries per quant array (the zero entries included)
+    const uint4 *x0 = reinterpret_cast<const uint4 *>(lds);
+    const uint4 *x1 = x0 + (XP ? 1 : XE);
+    constexpr int XS = XP ? 2 : 1;                     // uint4 per entry in x0/x1 indexing
+    const float *fd = reinterpret_cast<const float *>(x0 + 2 * XE);
+    const uint2 *dh = reinterpret_cast<const uint2 *>(x0 + 2 * XE);
+    Q6Planar::Raw r;
+    r.a = wa;
+    r.b = wb;
+    int v[8];
+    Q6Planar::codes(r, v);
+    const v4i32 W0 = {v[0], v[1], v[2], v[3]}, W1 = {v[4], v[5], v[6], v[7]};
+    int sl[4], sh[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const uint32_t word = i < 2 ? sct.x : sct.y;
+        sl[i] = sext8(word, 2 * (i & 1));
+        sh[i] = sext8(word, 2 * (i & 1) + 1);
+    }
+    // (XP: the 1/4 of the codes 4*(q6-32) is taken on d_w instead of d_a,
+    // a power of two, so every product and sum is the same number)
+    const float dw = XP ? half_to_float(dt) * 0.25f : half_to_float(dt);
+    v4i32 D0[NCG], D1[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) {
+        const int idx = xb[cg] + 4 * it;
+        const uint4 X0 = x0[XS * idx], X1 = x1[XS * idx];
+        const v4i32 A0 = {(int)X0.x, (int)X0.y, (int)X0.z, (int)X0.w};
+        const v4i32 A1 = {(int)X1.x, (int)X1.y, (int)X1.z, (int)X1.w};
+        const v4i32 Z = {0, 0, 0, 0};
+        D0[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, W0, Z, 0, 0, 0);
+        D1[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, W1, Z, 0, 0, 0);
+    }
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) {
+        const int no = 4 * cg + kg;            // this lane's output column
+        float dxa[4];
+        if constexpr (XP) {
+            const uint2 h = dh[(min(no, N - 1) * TNB + zt) / 4];
+            dxa[0] = half_to_float(h.x);
+            dxa[1] = half_to_float(h.x >> 16);
+            dxa[2] = half_to_float(h.y);
+            dxa[3] = half_to_float(h.y >> 16);
+        } else {
+            const float4 dx = *reinterpret_cast<const float4 *>(fd + min(no, N - 1) * TNB + zt);
+            dxa[0] = dx.x;
+            dxa[1] = dx.y;
+            dxa[2] = dx.z;
+            dxa[3] = dx.w;
+        }
+        int I[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) I[i] = __mul24(sl[i], D0[cg][i]) + __mul24(sh[i], D1[cg][i]);   // 4 * isum
+        if constexpr (DUMP) {
+            if (rok && no < N) {
+                const int64_t nsb = a.K / 32;
+                int32_t *dp = a.dump + ((int64_t)no * a.rows + row) * nsb + 4 * (int64_t)z;
+#pragma unroll
+                for (int i = 0; i < 4; i++) dp[i] = I[i] >> 2;
+            }
+        } else {
+            // (an fma with +0 is the product: d_a >= 0, so no -0 arises;
+            // the fp16 d_a of column-planar tiles then feeds the fma
+            // without a conversion)
+            float t = __builtin_fmaf(dxa[0], (float)I[0], 0.0f);
+#pragma unroll
+            for (int i = 1; i < 4; i++) t = __builtin_fmaf(dxa[i], (float)I[i], t);
+            acc[cg] = __builtin_fmaf(dw, t, acc[cg]);
+        }
+    }
+}
+
 // One chunk of CZ steps starting at step zc0: wave ks of the row tile takes
 // steps zc0 + ks*IT + it.  FULL: all steps exist (no clamping).
 template <bool FULL, int N, int KS, int RTW, int IT, bool DUMP, bool XP>
@@ -319,13 +404,6 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
     for (int it = 0; it < IT; it++) {
         const int z = zc0 + ks * IT + it;
         if (!FULL && z >= ZS) break;
-        const int zt = 4 * (z - zc0);
-        Q6Planar::Raw r;
-        r.a = wa[it];
-        r.b = wb[it];
-        int v[8];
-        Q6Planar::codes(r, v);
-        const v4i32 W0 = {v[0], v[1], v[2], v[3]}, W1 = {v[4], v[5], v[6], v[7]};
         uint2 sct;
         uint32_t dt;
         if constexpr (C::SCS) {
@@ -340,63 +418,8 @@ __device__ __forceinline__ void tiled_chunk(const Q6Tiled &f, const TiledLane<Ti
             dt = (uint32_t)__shfl((int)dsh, rr + 16 * ((zs[it] >> 1) - (z0 >> 1)));
         else
             dt = wd[it];
-        int sl[4], sh[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t word = i < 2 ? sct.x : sct.y;
-            sl[i] = sext8(word, 2 * (i & 1));
-            sh[i] = sext8(word, 2 * (i & 1) + 1);
-        }
-        // (XP: the 1/4 of the codes 4*(q6-32) is taken on d_w instead of d_a,
-        // a power of two, so every product and sum is the same number)
-        const float dw = XP ? half_to_float(dt) * 0.25f : half_to_float(dt);
-        v4i32 D0[C::NCG], D1[C::NCG];
-#pragma unroll
-        for (int cg = 0; cg < C::NCG; cg++) {
-            const int idx = tl.xb[cg] + 4 * it;
-            const uint4 X0 = x0[XS * idx], X1 = x1[XS * idx];
-            const v4i32 A0 = {(int)X0.x, (int)X0.y, (int)X0.z, (int)X0.w};
-            const v4i32 A1 = {(int)X1.x, (int)X1.y, (int)X1.z, (int)X1.w};
-            const v4i32 Z = {0, 0, 0, 0};
-            D0[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, W0, Z, 0, 0, 0);
-            D1[cg] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, W1, Z, 0, 0, 0);
-        }
-#pragma unroll
-        for (int cg = 0; cg < C::NCG; cg++) {
-            const int no = 4 * cg + kg;            // this lane's output column
-            float dxa[4];
-            if constexpr (XP) {
-                const uint2 h = dh[(min(no, N - 1) * TNB + zt) / 4];
-                dxa[0] = half_to_float(h.x);
-                dxa[1] = half_to_float(h.x >> 16);
-                dxa[2] = half_to_float(h.y);
-                dxa[3] = half_to_float(h.y >> 16);
-            } else {
-                const float4 dx = *reinterpret_cast<const float4 *>(fd + min(no, N - 1) * TNB + zt);
-                dxa[0] = dx.x;
-                dxa[1] = dx.y;
-                dxa[2] = dx.z;
-                dxa[3] = dx.w;
-            }
-            int I[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) I[i] = __mul24(sl[i], D0[cg][i]) + __mul24(sh[i], D1[cg][i]);   // 4 * isum
-            if constexpr (DUMP) {
-                if (rok && no < N) {
-                    int32_t *dp = a.dump + ((int64_t)no * a.rows + row) * nsb + 4 * (int64_t)z;
-#pragma unroll
-                    for (int i = 0; i < 4; i++) dp[i] = I[i] >> 2;
-                }
-            } else {
-                // (an fma with +0 is the product: d_a >= 0, so no -0 arises;
-                // the fp16 d_a of column-planar tiles then feeds the fma
-                // without a conversion)
-                float t = __builtin_fmaf(dxa[0], (float)I[0], 0.0f);
-#pragma unroll
-                for (int i = 1; i < 4; i++) t = __builtin_fmaf(dxa[i], (float)I[i], t);
-                acc[cg] = __builtin_fmaf(dw, t, acc[cg]);
-            }
-        }
+        tiled_step<N, C::NCG, TNB, IT, DUMP, XP>(wa[it], wb[it], sct, dt, tl.xb, it, 4 * (z - zc0), lds, kg, a, row,
+                                                 rok, z, acc);
     }
 }
 
@@ -421,12 +444,13 @@ __device__ __forceinline__ uint64_t argmax_key(float v, int64_t row) {
 // one row workgroup run on one XCD close together in time and read its
 // weights from that XCD's L2 after the first.  Every column goes through the
 // same arithmetic as in a product of eight or fewer columns.
-template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false, bool XP = false>
-__global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
-                                                                    float *__restrict__ out) {
+// One workgroup of the tiled product: row workgroup wg (RTW tiles of 16
+// rows, KS waves along K each), the N columns at a.xq; outputs to out (or
+// keys, or integer sums to a.dump).
+template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX, bool XP>
+__device__ __forceinline__ void tiled_workgroup(const void *__restrict__ w, const MmvqArgs &a,
+                                                float *__restrict__ out, int64_t wg, uint8_t *lds) {
     using C = TiledCfg<N, KS, RTW, IT, XP>;
-    static_assert(N <= 8 || (!DUMP && !AMAX), "batched products write outputs only");
-    extern __shared__ __align__(16) uint8_t lds[];
     Q6Tiled f;
     f.init(w, a.rows, a.K);
     const int tid = threadIdx.x, l = tid & (kWave - 1);
@@ -435,24 +459,6 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
     // the wave's tile and the lane's row; lanes past the last row load from a
     // row that exists and store nothing
     const int64_t ntiles = (a.rows + 15) / 16;
-    int64_t wg = blockIdx.x;
-    if constexpr (N > 8) {
-        const int64_t nrw = (ntiles + RTW - 1) / RTW, g8 = (nrw + 7) / 8;
-        const int64_t nbat = gridDim.x / (8 * g8), j = blockIdx.x >> 3;
-        const int64_t cb = j % nbat;
-        wg = (j / nbat) * 8 + (blockIdx.x & 7);
-        if (wg >= nrw) return;                              // the whole workgroup
-        a.xq += cb * N * 36 * (a.K / 32);
-        out += cb * N * a.rows;
-    }
-    if constexpr (AMAX) {
-        // clear the reduction's running maxima and counts (k_argmax_reduce)
-        if (blockIdx.x == 0 && tid < N) {
-            uint8_t *tail = reinterpret_cast<uint8_t *>(out) + argmax_tail(ntiles, N);
-            reinterpret_cast<uint64_t *>(tail)[tid] = 0;
-            reinterpret_cast<uint32_t *>(tail + 64)[tid] = 0;
-        }
-    }
     const int64_t tile = wg * RTW + rt, tc = min(tile, ntiles - 1);
     const int R = (int)min((int64_t)16, a.rows - 16 * tc);
     const int r = l & 15, rr = min(r, R - 1), kg = l >> 4;
@@ -530,6 +536,87 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
                 }
             }
         }
+    }
+}
+
+template <int N, int KS, int RTW, int IT, bool DUMP, bool AMAX = false, bool XP = false>
+__global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *__restrict__ w, MmvqArgs a,
+                                                                    float *__restrict__ out) {
+    static_assert(N <= 8 || (!DUMP && !AMAX), "batched products write outputs only");
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int64_t ntiles = (a.rows + 15) / 16;
+    int64_t wg = blockIdx.x;
+    if constexpr (N > 8) {
+        const int64_t nrw = (ntiles + RTW - 1) / RTW, g8 = (nrw + 7) / 8;
+        const int64_t nbat = gridDim.x / (8 * g8), j = blockIdx.x >> 3;
+        const int64_t cb = j % nbat;
+        wg = (j / nbat) * 8 + (blockIdx.x & 7);
+        if (wg >= nrw) return;                              // the whole workgroup
+        a.xq += cb * N * 36 * (a.K / 32);
+        out += cb * N * a.rows;
+    }
+    if constexpr (AMAX) {
+        // clear the reduction's running maxima and counts (k_argmax_reduce)
+        if (blockIdx.x == 0 && threadIdx.x < N) {
+            uint8_t *tail = reinterpret_cast<uint8_t *>(out) + argmax_tail(ntiles, N);
+            reinterpret_cast<uint64_t *>(tail)[threadIdx.x] = 0;
+            reinterpret_cast<uint32_t *>(tail + 64)[threadIdx.x] = 0;
+        }
+    }
+    tiled_workgroup<N, KS, RTW, IT, DUMP, AMAX, XP>(w, a, out, wg, lds);
+}
+
+// Several independent products of the same K in one launch (the matrices of
+// a layer, each with its own activation columns): job j takes workgroups
+// wg0[j] .. wg0[j+1]-1, each one row workgroup of that job's product, with
+// the same waves along K and so the same bits as the job launched alone.
+// One launch ramps up and drains once for all of them.
+constexpr int kMaxTiledJobs = 8;
+struct TiledJob {
+    const void *w;
+    const uint8_t *xq;
+    float *out;
+    int64_t rows;
+    int32_t ncols, wg0;
+};
+struct TiledJobs {
+    TiledJob job[kMaxTiledJobs];
+    int32_t njobs;
+    int64_t K;
+};
+
+template <int KS, int RTW, int IT, bool XP>
+__global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const TiledJobs js) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int b = blockIdx.x;
+    // this workgroup's job, and its fields, by selects over the (scalar)
+    // kernel arguments rather than an indexed access
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxTiledJobs; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
+    TiledJob jb = js.job[0];
+#pragma unroll
+    for (int i = 1; i < kMaxTiledJobs; i++)
+        if (j == i) jb = js.job[i];
+    MmvqArgs a;
+    a.xq = jb.xq;
+    a.dump = nullptr;
+    a.rows = jb.rows;
+    a.K = js.K;
+    a.colpack = 0x0706050403020100ull;
+    a.xstride = js.K / 32;
+    a.its = IT;
+    a.nout = jb.ncols;
+    const int64_t wg = b - jb.wg0;
+    switch (jb.ncols) {
+    case 1: tiled_workgroup<1, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    case 2: tiled_workgroup<2, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    case 3: tiled_workgroup<3, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    case 4: tiled_workgroup<4, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    case 5: tiled_workgroup<5, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    case 6: tiled_workgroup<6, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    case 7: tiled_workgroup<7, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    default: tiled_workgroup<8, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
     }
 }
 
@@ -619,6 +706,47 @@ hipError_t launch_tiled_n(const void *w, const void *xq, float *out, int32_t *du
     if (need <= 4) return launch_tiled_cfg<N, 4, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
     if (need <= 8) return launch_tiled_cfg<N, 8, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
     return launch_tiled_cfg<N, 16, 1, 5, DUMP, AMAX, XP>(w, xq, out, dump, rows, K, s);
+}
+
+// LDS of the jobs kernel: the largest any column count needs.
+template <int KS, int RTW, int IT, bool XP>
+constexpr size_t tiled_jobs_lds() {
+    size_t m = 0;
+    const size_t v[8] = {TiledCfg<1, KS, RTW, IT, XP>::LDS, TiledCfg<2, KS, RTW, IT, XP>::LDS,
+                         TiledCfg<3, KS, RTW, IT, XP>::LDS, TiledCfg<4, KS, RTW, IT, XP>::LDS,
+                         TiledCfg<5, KS, RTW, IT, XP>::LDS, TiledCfg<6, KS, RTW, IT, XP>::LDS,
+                         TiledCfg<7, KS, RTW, IT, XP>::LDS, TiledCfg<8, KS, RTW, IT, XP>::LDS};
+    for (size_t x : v) m = x > m ? x : m;
+    return m;
+}
+
+// Jobs (at most kMaxTiledJobs, same K) in one launch; the caller has checked
+// every job.  Workgroup ranges in the given job order.
+template <int KS, int RTW, int IT, bool XP>
+hipError_t launch_tiled_jobs_cfg(TiledJobs js, hipStream_t s) {
+    constexpr int NTHR = KS * RTW * kWave;
+    int64_t wg = 0;
+    for (int j = 0; j < js.njobs; j++) {
+        js.job[j].wg0 = (int32_t)wg;
+        wg += ((js.job[j].rows + 15) / 16 + RTW - 1) / RTW;
+    }
+    for (int j = js.njobs; j < kMaxTiledJobs; j++) js.job[j] = js.job[0];
+    if (wg * NTHR > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
+    constexpr size_t lds = tiled_jobs_lds<KS, RTW, IT, XP>();
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled_jobs<KS, RTW, IT, XP>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mmvq_q6_tiled_jobs<KS, RTW, IT, XP>), dim3((unsigned)wg), dim3(NTHR), lds, s, js);
+    return hipGetLastError();
+}
+
+template <bool XP>
+hipError_t launch_tiled_jobs(const TiledJobs &js, hipStream_t s) {
+    const int64_t need = (js.K / 128 + 4) / 5;
+    if (need <= 1) return launch_tiled_jobs_cfg<1, 4, 5, XP>(js, s);
+    if (need <= 2) return launch_tiled_jobs_cfg<2, 2, 5, XP>(js, s);
+    if (need <= 4) return launch_tiled_jobs_cfg<4, 1, 5, XP>(js, s);
+    if (need <= 8) return launch_tiled_jobs_cfg<8, 1, 5, XP>(js, s);
+    return launch_tiled_jobs_cfg<16, 1, 5, XP>(js, s);
 }
 
 // Columns per batch of the batched product: sixteen, twelve with sixteen

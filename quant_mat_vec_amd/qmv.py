@@ -24,6 +24,12 @@ ACT_PLANAR = 16   # OR-ed into the layout with LAYOUT_TILED: column-planar activ
 _lib = None
 
 
+class Q6kJob(ctypes.Structure):
+    """qmv_q6k_job of include/qmv.h."""
+    _fields_ = [("w", ctypes.c_void_p), ("xq", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("rows", ctypes.c_int64), ("ncols", ctypes.c_int)]
+
+
 class QmvError(RuntimeError):
     def __init__(self, code: int, what: str):
         self.code = code
@@ -65,6 +71,8 @@ def lib() -> ctypes.CDLL:
             fn = getattr(L, name)
             fn.argtypes = args
             fn.restype = I
+        L.mmvq_q6k_batch.argtypes = [ctypes.POINTER(Q6kJob), I, I, I64, P]
+        L.mmvq_q6k_batch.restype = I
         L.grouped_expert_mmvq_workspace.argtypes = [I, I, I, I64, I64]
         L.mmvq_q6k_argmax_workspace.restype = SZ
         L.mmvq_q6k_argmax_workspace.argtypes = [I64, I]
@@ -191,6 +199,12 @@ def mmvq_q4k_isums(w, xq, isums, rows: int, K: int, ncols: int, stream=None) -> 
 def mmvq_q5k_isums(w, xq, isums, rows: int, K: int, ncols: int, stream=None) -> None:
     _check(lib().mmvq_q5k_isums(_ptr(w), _ptr(xq), _ptr(isums), rows, K, ncols, _stream(stream)),
            "mmvq_q5k_isums")
+
+
+def mmvq_q6k_batch(jobs, layout: int, K: int, stream=None) -> None:
+    """jobs: sequence of (w, xq, out, rows, ncols) -- one launch for all."""
+    arr = (Q6kJob * max(1, len(jobs)))(*[Q6kJob(_ptr(w), _ptr(x), _ptr(o), rows, n) for w, x, o, rows, n in jobs])
+    _check(lib().mmvq_q6k_batch(arr, len(jobs), layout, K, _stream(stream)), "mmvq_q6k_batch")
 
 
 def grouped_expert_mmvq_workspace(E: int, T: int, topk: int, d_model: int, d_ff: int) -> int:

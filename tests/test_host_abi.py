@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(L):
                 "unpack_q6k_planar", "repack_q6k_tiled", "unpack_q6k_tiled", "gather_q6k_rows", "mmvq_q6k_argmax", "mmvq_q6k_argmax_workspace",
                 "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
-                "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "qmv_strerror",
+                "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "grouped_expert_mmvq_noalloc",
+                "mmvq_q6k_batch", "qmv_strerror",
                 "qmv_last_hip_error", "qmv_stream_read"}
     assert expected <= set(names), set(names) ^ expected
     for n in names:
@@ -240,6 +241,27 @@ def test_moe_noalloc_rejects(L):
     assert call(wd=P + 8, lay=1) == E_ALN
     assert L.grouped_expert_mmvq_workspace(128, 8, 8, 2560, 16384) > 4 << 20
     assert call(dff=16384) == E_UNS
+
+
+def test_batch_rejects(L):
+    T, XT = qmv.LAYOUT_TILED, qmv.LAYOUT_TILED | qmv.ACT_PLANAR
+
+    def call(jobs, layout=T, K=512, n=None):
+        arr = (qmv.Q6kJob * max(1, len(jobs)))(*[qmv.Q6kJob(*j) for j in jobs])
+        return L.mmvq_q6k_batch(arr, len(jobs) if n is None else n, layout, K, None)
+
+    ok = (P, P, P, 16, 2)
+    assert L.mmvq_q6k_batch(None, 1, T, 512, None) == E_INV
+    assert call([ok], n=0) == E_INV
+    assert call([ok] * 9) == E_UNS
+    assert call([ok], layout=qmv.LAYOUT_PLANAR) == E_UNS and call([ok], layout=qmv.LAYOUT_GGUF) == E_UNS
+    assert call([ok], K=300) == E_UNS and call([ok], K=1 << 21) == E_UNS
+    assert call([ok, (P, P, P, 16, 9)]) == E_UNS and call([ok, (P, P, P, 16, 0)]) == E_UNS
+    assert call([ok, (P, P, P, 0, 2)]) == E_INV and call([ok, (None, P, P, 16, 2)]) == E_INV
+    assert call([ok, (P + 8, P, P, 16, 2)]) == E_ALN and call([ok, (P, P, P + 2, 16, 2)]) == E_ALN
+    assert call([ok, (P, P + 4, P, 16, 2)], layout=XT) == E_ALN
+    half = (1 << 25)
+    assert call([(P, P, P, half, 1), (P, P, P, half, 1)]) == E_UNS      # rows summed past the product limit
 
 
 def test_stream_read_rejects(L):
