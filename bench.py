@@ -1,50 +1,62 @@
 #!/usr/bin/env python3
 """Benchmark of the Q6_K MMVQ decode path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu] [--no-profile]
 
 Workload (one "step"): quantize 13 fp32 activation columns to Q8_1 (the
-column-planar arrangement of its bytes) in one launch, then run the Q6_K
-MMVQ of a 10240 x 2560 (rows x cols) matrix in the tiled layout (int8
-matrix-core kernel) at N = 1, 4 and 8 columns (each product on its own
-columns: 1 + 4 + 8 = 13)
--- the decode matrix the pages measure as "2560 x 10240" (n_in x n_out).  Weights are resident in HBM before timing and
-each launch reads a different one of 26 copies (559 MB, more than twice the
-256 MB Infinity Cache), so every weight byte comes from HBM.
+column-planar arrangement of its bytes) in one launch, then the Q6_K MMVQ of
+three 10240 x 2560 (rows x cols) matrices in the tiled layout (int8
+matrix-core kernel) at N = 8, 4 and 1 columns -- each product on its own
+weights and its own columns (8 + 4 + 1 = 13) -- issued as one batched launch
+(mmvq_q6k_batch), as the decode products of a layer's matrices are.  This is
+the decode matrix the pages measure as "2560 x 10240" (n_in x n_out) at 1-8
+columns.  Weights are resident in HBM before timing and the step's three
+products read three of 26 copies (559 MB, more than twice the 256 MB
+Infinity Cache), rotating, so every weight byte comes from HBM.
 
-Printed: one JSON line.  `value` is effective weight throughput over the
-whole step (weight bytes of the three products / step wall time, GB/s).
-`roofline` is for the dominant kernel (the MMVQ instantiation with the
-largest share of GPU time): algorithmic bytes per launch over its average
-launch time, from HIP events on its launch stream around graph replays of
-back-to-back launches.  The step itself is timed from HIP graph replays,
-each graph holding 26 consecutive steps (events on the stream, and host wall
-time; the larger is used); `extras` also gives the rate with one graph launch
-per step.  `cpu_baseline` times the CPU oracle on
-the same step.  `extras` holds per-N figures, the other shapes, the grouped
-MoE, a cache-warm figure (not HBM) and a plain device copy for calibration.
+Timing: exactly `steps` steps, replayed from HIP graphs holding
+min(steps, 26) consecutive steps (and one graph for a remainder), with HIP
+events on the launch stream and host wall time around them (the larger is
+used).  `value` = weight bytes of the three products / step time (GB/s).
+
+`roofline` is for the dominant kernel (the batched launch): algorithmic
+bytes per launch over its average launch duration, from HIP events on its
+stream around graph replays of back-to-back launches (3 repeats of at least
+2000 launches).  Before the GPU is touched, bench.py runs two short child
+processes under rocprofv3: one with the FETCH_SIZE and one with the
+WRITE_SIZE counter (HBM traffic per dispatch, scaled by what the same
+counters read for a device copy of known size), and one kernel trace (per
+kernel median, p10 and p90 dispatch durations, in three repeats); their
+results go into the line (`roofline.traffic`, `extras.rocprof`).
+`cpu_baseline` times the CPU oracle on the same step.  `extras` holds the
+single launches per column count, the other shapes, the grouped MoE, a
+cache-warm figure (not HBM) and calibration reads.
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import json
 import math
 import os
+import shutil
+import subprocess
 import sys
+import tempfile
 import time
 
+HERE = os.path.dirname(os.path.abspath(__file__))
 ROWS, K = 10240, 2560
-# HBM traffic of the dominant kernel per launch, from rocprofv3 --pmc
-# FETCH_SIZE / WRITE_SIZE (KiB per dispatch) scaled by the same counters on a
-# plain copy of known size (FETCH_SIZE x 1.9977, WRITE_SIZE x 1.0); to be
-# emptied whenever the kernel changes after the counters were taken.
-TRAFFIC = {1: 21671450, 4: 21866882, 8: 22143231}
+JOBS = (8, 4, 1)            # column counts of the step's three products, in launch order
 NCOLS = (1, 4, 8)
-XCOLS = sum(NCOLS)          # distinct activation columns quantized per step
-COL0 = {1: 0, 4: 1, 8: 5}   # first activation column of each product
+XCOLS = sum(JOBS)           # distinct activation columns quantized per step
+COL0 = {8: 0, 4: 8, 1: 12}  # first activation column of each product
 Q6K_BYTES = 210
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20
+BATCH_KERNEL = "k_mmvq_q6_tiled_jobs<4, 1, 5, true>"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # pages' figures for this matrix (Arc A770, large-GRF launch, 1/4/8 columns):
 # 86.1, 92.9, 370.5 us per call
 PAGES_US = {1: 86.1, 4: 92.9, 8: 370.5}
@@ -55,8 +67,8 @@ def weight_bytes(rows, k, per_block=Q6K_BYTES):
 
 
 def alg_bytes(rows, k, n, per_block=Q6K_BYTES):
-    """Algorithmic bytes of one MMVQ launch: weights once, Q8_1 activations,
-    fp32 outputs."""
+    """Algorithmic bytes of one MMVQ: weights once, Q8_1 activations, fp32
+    outputs."""
     return weight_bytes(rows, k, per_block) + n * (k // 32) * 36 + 4 * n * rows
 
 
@@ -67,28 +79,19 @@ def parse():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-extras", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-profile", action="store_true",
+                   help="skip the rocprofv3 child runs (traffic and kernel-trace statistics)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--pmc-workload", action="store_true",
-                   help="only run 30 launches each of the N=1/4/8 products and of a 21.5 MB device "
-                        "copy (for rocprofv3 --pmc passes), print nothing")
+                   help="only run 30 batched launches, 30 single launches per column count and 30 device copies "
+                        "of the same 21.5 MB (the workload of the rocprofv3 --pmc passes), print nothing")
+    p.add_argument("--trace-workload", action="store_true",
+                   help="only run 3 repeats of at least 2000 batched launches and of single launches per column "
+                        "count (the workload of the kernel trace), print nothing")
     p.add_argument("--pmc-mmq", action="store_true",
                    help="only run 8 launches of the 512-column product mmq_q6k on the same matrix "
                         "(for rocprofv3 --pmc passes), print nothing")
     return p.parse_args()
-
-
-def timed_launches(torch, fn, n_iter, copies):
-    """Per-launch GPU time (us) from events around each launch; fn(buf)."""
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_iter)]
-    for i in range(n_iter):
-        evs[i][0].record()
-        fn(copies[i % len(copies)])
-        evs[i][1].record()
-    torch.cuda.synchronize()
-    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
-    return {"mean_us": sum(t) / len(t), "median_us": t[len(t) // 2], "p10_us": t[len(t) // 10],
-            "p90_us": t[(9 * len(t)) // 10]}
 
 
 def graph_avg_us(torch, calls, reps=6):
@@ -110,6 +113,147 @@ def graph_avg_us(torch, calls, reps=6):
     return a.elapsed_time(b) * 1e3 / (reps * len(calls))
 
 
+def repeated_avg_us(torch, fn, nrot, min_launches=2000, repeats=3):
+    """Per-launch device time (us) of fn(i), i = launch index: a graph of
+    2*nrot back-to-back launches replayed until at least min_launches ran,
+    events on the launch stream; `repeats` such measurements."""
+    stream = torch.cuda.current_stream()
+    per = 2 * nrot
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph, stream=stream):
+        for i in range(per):
+            fn(i)
+    gph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(min_launches / per))
+    res = []
+    for _ in range(repeats):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            gph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        res.append(a.elapsed_time(b) * 1e3 / (reps * per))
+    del gph
+    return {"avg_launch_us": round(sum(res) / len(res), 3), "repeats_us": [round(v, 3) for v in res],
+            "launches_per_repeat": reps * per}
+
+
+# ----------------------------------------------------------- rocprofv3 runs
+def _child(cmd, outdir, seconds):
+    env = dict(os.environ, TMPDIR="/tmp", PYTHONPATH=HERE + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    try:
+        r = subprocess.run(["timeout", "-s", "KILL", str(seconds), *cmd], cwd="/tmp", env=env,
+                           capture_output=True, text=True)
+    except OSError as e:
+        return f"could not run rocprofv3: {e}"
+    found = glob.glob(os.path.join(outdir, "**", "*.csv"), recursive=True)
+    if r.returncode != 0 and not found:
+        return f"rocprofv3 exit {r.returncode}: {(r.stderr or r.stdout)[-300:]}"
+    return None
+
+
+def _rows(outdir, suffix):
+    rows = []
+    for f in glob.glob(os.path.join(outdir, "**", f"*{suffix}"), recursive=True):
+        with open(f, newline="") as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    n = name.split("(")[0].replace("void ", "").replace("qmv::", "")
+    return n.strip()
+
+
+def profile_children(py):
+    """Traffic (two --pmc passes) and kernel-trace statistics of this
+    script's own workloads, run under rocprofv3 as child processes before
+    this process touches the GPU."""
+    if shutil.which("rocprofv3") is None:
+        return {"error": "rocprofv3 not found"}, None
+    out = {}
+    tmp = tempfile.mkdtemp(prefix="qmv_bench_prof_", dir="/tmp")
+    try:
+        # HBM traffic per dispatch, calibrated by a device copy of known size
+        counters = {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = os.path.join(tmp, c)
+            err = _child(["rocprofv3", "--pmc", c, "--output-format", "csv", "-d", d, "-o", "pmc", "--",
+                          py, "-u", os.path.join(HERE, "bench.py"), "--pmc-workload"], d, 120)
+            if err:
+                out["traffic_error"] = err
+                break
+            for r in _rows(d, "counter_collection.csv"):
+                if r.get("Counter_Name") != c:
+                    continue
+                k = _short(r["Kernel_Name"])
+                counters.setdefault(k, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+        if "traffic_error" not in out:
+            copy = counters.get(COPY_KERNEL, {})
+            wb = weight_bytes(ROWS, K)
+            if not copy.get("FETCH_SIZE") or not copy.get("WRITE_SIZE"):
+                out["traffic_error"] = "no copy-kernel counters for calibration"
+            else:
+                fk = sum(copy["FETCH_SIZE"]) / len(copy["FETCH_SIZE"])
+                wk = sum(copy["WRITE_SIZE"]) / len(copy["WRITE_SIZE"])
+                sf, sw = wb / (fk * 1024), wb / (wk * 1024)
+                tr = {}
+                for k, v in counters.items():
+                    if "FETCH_SIZE" in v and "WRITE_SIZE" in v and k != COPY_KERNEL:
+                        f = sum(v["FETCH_SIZE"]) / len(v["FETCH_SIZE"])
+                        w = sum(v["WRITE_SIZE"]) / len(v["WRITE_SIZE"])
+                        tr[k] = {"FETCH_SIZE_KiB": round(f, 1), "WRITE_SIZE_KiB": round(w, 1),
+                                 "bytes": round(f * 1024 * sf + w * 1024 * sw), "dispatches": len(v["FETCH_SIZE"])}
+                out["traffic"] = {"per_kernel": tr,
+                                  "calibration": {"copy_bytes": wb, "FETCH_SIZE_KiB": round(fk, 1),
+                                                  "WRITE_SIZE_KiB": round(wk, 1), "fetch_scale": round(sf, 4),
+                                                  "write_scale": round(sw, 4)}}
+        # kernel trace: per-kernel median / p10 / p90 in three repeats
+        d = os.path.join(tmp, "trace")
+        err = _child(["rocprofv3", "--kernel-trace", "--output-format", "csv", "-d", d, "-o", "tr", "--",
+                      py, "-u", os.path.join(HERE, "bench.py"), "--trace-workload"], d, 180)
+        if err:
+            out["trace_error"] = err
+        else:
+            per = {}
+            for r in _rows(d, "kernel_trace.csv"):
+                per.setdefault(_short(r["Kernel_Name"]), []).append(
+                    (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+            stats = {}
+            for k, v in per.items():
+                if "tiled" not in k or len(v) < 300:
+                    continue
+                v.sort()
+                dur = [x[1] / 1e3 for x in v]
+                third = len(dur) // 3
+                reps = []
+                for i in range(3):
+                    s = sorted(dur[i * third:(i + 1) * third])
+                    reps.append({"median_us": round(s[len(s) // 2], 3), "p10_us": round(s[len(s) // 10], 3),
+                                 "p90_us": round(s[(9 * len(s)) // 10], 3), "dispatches": len(s)})
+                a = sorted(dur)
+                stats[k] = {"median_us": round(a[len(a) // 2], 3), "p10_us": round(a[len(a) // 10], 3),
+                            "p90_us": round(a[(9 * len(a)) // 10], 3), "mean_us": round(sum(a) / len(a), 3),
+                            "dispatches": len(a), "repeats": reps}
+            out["kernel_trace"] = stats
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    return out, out.get("traffic")
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -117,6 +261,11 @@ def main():
         print("bench.py: this benchmark runs on one GPU only (the MMVQ would shard by output rows "
               "across GPUs; no multi-GPU path is built). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    workload_only = args.pmc_workload or args.trace_workload or args.pmc_mmq
+    prof, traffic = ({}, None)
+    if not workload_only and not args.no_profile:
+        prof, traffic = profile_children(sys.executable)
 
     import numpy as np
     import torch
@@ -128,6 +277,7 @@ def main():
     # all work on one non-default stream (graph capture needs one; default
     # priority, like every stream here)
     torch.cuda.set_stream(torch.cuda.Stream())
+    stream = torch.cuda.current_stream()
     # tiled weights (matrix cores), column-planar Q8_1 activations
     XT = qmv.LAYOUT_TILED | qmv.ACT_PLANAR
     g = synth.rng(synth.seed_for(1, 1, 8))
@@ -138,19 +288,25 @@ def main():
     w_gguf = torch.from_numpy(w_np).to(dev)
     base = torch.empty_like(w_gguf)
     qmv.repack_q6k_tiled(w_gguf, base, ROWS, K)
+    del w_gguf
     copies = [base.clone() for _ in range(ncopies)]
     xd = torch.from_numpy(x_np).to(dev)
     xq_all = torch.empty(XCOLS * (K // 32) * 36, dtype=torch.uint8, device=dev)
     qcol = (K // 32) * 36      # bytes of one Q8_1 column
+    outs = {n: torch.empty(n * ROWS, dtype=torch.float32, device=dev) for n in JOBS}
 
     def xq_of(n):
         return xq_all[COL0[n] * qcol:(COL0[n] + n) * qcol]
     qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
-    xq = xq_all[:8 * qcol]
-    out = torch.empty(8 * ROWS, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
+    def batch(i):
+        """The step's three products, on weight copies 3i, 3i+1, 3i+2."""
+        qmv.mmvq_q6k_batch([(copies[(len(JOBS) * i + j) % ncopies], xq_of(n), outs[n], ROWS, n)
+                            for j, n in enumerate(JOBS)], XT, K)
+
+    def single(n):
+        return lambda i: qmv.mmvq_q6k(copies[i % ncopies], XT, xq_of(n), outs[n], ROWS, K, n)
 
     if args.pmc_mmq:
         n = 512
@@ -164,131 +320,115 @@ def main():
         return
 
     if args.pmc_workload:
-        # fixed workload for hardware-counter passes: the three products on
-        # rotated copies, then a plain copy of the same size (its FETCH_SIZE /
-        # WRITE_SIZE calibrate the counters against known bytes)
-        qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
+        # hardware-counter passes: the batched launch and the single products
+        # on rotated copies, then a plain copy of the same size (its
+        # FETCH_SIZE / WRITE_SIZE calibrate the counters against known bytes)
+        for i in range(30):
+            batch(i)
         for n in NCOLS:
             for i in range(30):
-                qmv.mmvq_q6k(copies[i % ncopies], XT, xq_of(n), out, ROWS, K, n)
+                single(n)(i)
         dst = torch.empty_like(base)
         for i in range(30):
             dst.copy_(copies[i % ncopies])
         torch.cuda.synchronize()
         return
 
+    if args.trace_workload:
+        # per kernel three consecutive repeats of at least 2000 launches (the
+        # trace's thirds)
+        repeated_avg_us(torch, batch, ncopies, min_launches=2000, repeats=3)
+        for n in NCOLS:
+            repeated_avg_us(torch, single(n), ncopies, min_launches=2000, repeats=3)
+        return
+
     def step(i):
         qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
-        for j, n in enumerate(NCOLS):
-            c = copies[(len(NCOLS) * i + j) % ncopies]
-            qmv.mmvq_q6k(c, XT, xq_of(n), out, ROWS, K, n)
+        batch(i)
 
-    # Step i uses weight copies at rotation offset i % ncopies.  HIP graphs:
-    # one holding `ncopies` consecutive steps (offsets 0 .. ncopies-1, so the
-    # rotation continues across replays) and one single-step graph per
-    # offset for a remainder; exactly `steps` steps run in the timed region.
-    # A decode loop captures many launches per graph; the single-step figure
-    # (one graph launch per step) is reported beside it.
-    graphs = []
-    for i in range(ncopies):
-        gph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gph, stream=stream):
-            step(i)
-        graphs.append(gph)
-    multi = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(multi, stream=stream):
-        for i in range(ncopies):
-            step(i)
-    torch.cuda.synchronize()
+    # Exactly `steps` steps: graphs of G = min(steps, ncopies) consecutive
+    # steps (step offsets 0 .. G-1; with G = ncopies the rotation continues
+    # across replays) and one graph for the remainder.
+    graphs = {}
 
-    def run_steps(n, batched):
-        done = 0
-        if batched:
-            while n - done >= ncopies:
-                multi.replay()
-                done += ncopies
-        while done < n:
-            graphs[done % ncopies].replay()
-            done += 1
+    def graph_of(n):
+        if n not in graphs:
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph, stream=stream):
+                for i in range(n):
+                    step(i)
+            graphs[n] = gph
+        return graphs[n]
 
-    def timed_steps(n, batched):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def run_steps(n):
+        G = min(n, ncopies)
+        full, rest = divmod(n, G)
+        for _ in range(full):
+            graph_of(G).replay()
+        if rest:
+            graph_of(rest).replay()
+
+    def timed_steps(n):
+        run_steps(n)                       # capture and load every graph this count uses
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(stream)
-        run_steps(n, batched)
+        run_steps(n)
         e1.record(stream)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         return e0.elapsed_time(e1) / n, (t1 - t0) * 1e3 / n
 
-    run_steps(args.warmup, True)
-    torch.cuda.synchronize()
-    ms_per_step, wall_ms_per_step = timed_steps(args.steps, True)
-    step_bytes = wb * len(NCOLS)
+    if args.warmup:
+        run_steps(args.warmup)
+        torch.cuda.synchronize()
+    ms_per_step, wall_ms_per_step = timed_steps(args.steps)
+    step_bytes = wb * len(JOBS)
     value = step_bytes / (max(ms_per_step, wall_ms_per_step) * 1e-3) / 1e9
-    single_ms, single_wall_ms = timed_steps(args.steps, False)
 
-    # Per-kernel average launch time: events on the launch stream around
-    # graph replays of back-to-back launches of one MMVQ instantiation
-    # (rotating copies), so host launch cost is excluded and only the device's
-    # per-launch time (kernel plus the dispatch gap between kernels) remains.
-    per_n = {}
-    reps, per_graph = 8, ncopies * 2
+    # Per-launch averages: the batched launch (the dominant kernel) and the
+    # single products per column count.
     qmv.quantize_q8_1_planar(xd, xq_all, K, XCOLS)
+    bt = repeated_avg_us(torch, batch, ncopies)
+    batch_alg = sum(alg_bytes(ROWS, K, n) for n in JOBS)
+    per_n = {}
     for n in NCOLS:
-        gph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gph, stream=stream):
-            for i in range(per_graph):
-                qmv.mmvq_q6k(copies[i % ncopies], XT, xq_of(n), out, ROWS, K, n)
-        gph.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            gph.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        mean = a.elapsed_time(b) * 1e3 / (reps * per_graph)
-        per_n[n] = {"kernel": f"qmv::k_mmvq_q6_tiled<{n}, 4, 1, 5, false, false, true>",
-                    "avg_launch_us": round(mean, 3),
-                    "weight_GBps": round(wb / (mean * 1e-6) / 1e9, 1),
-                    "weight_frac_of_8TBps": round(wb / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                    "alg_bytes": alg_bytes(ROWS, K, n), "launches_timed": reps * per_graph}
-        del gph
-    dom = max(NCOLS, key=lambda n: per_n[n]["avg_launch_us"])
-    ach = alg_bytes(ROWS, K, dom) / (per_n[dom]["avg_launch_us"] * 1e-6) / 1e9
+        r = repeated_avg_us(torch, single(n), ncopies)
+        per_n[str(n)] = dict(r, kernel=f"k_mmvq_q6_tiled<{n}, 4, 1, 5, false, false, true>",
+                             weight_GBps=round(wb / (r["avg_launch_us"] * 1e-6) / 1e9, 1),
+                             weight_frac_of_8TBps=round(wb / (r["avg_launch_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                             alg_bytes=alg_bytes(ROWS, K, n))
+    ach = batch_alg / (bt["avg_launch_us"] * 1e-6) / 1e9
+    tr_bytes = None
+    if traffic and BATCH_KERNEL in traffic.get("per_kernel", {}):
+        tr_bytes = traffic["per_kernel"][BATCH_KERNEL]["bytes"]
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": TRAFFIC.get(dom),
-                "kernel": per_n[dom]["kernel"], "ncols": dom,
-                "alg_bytes_per_launch": alg_bytes(ROWS, K, dom),
-                "avg_launch_us": per_n[dom]["avg_launch_us"]}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": tr_bytes,
+                "kernel": BATCH_KERNEL, "jobs": "10240x2560 at 8, 4 and 1 columns",
+                "alg_bytes_per_launch": batch_alg, "avg_launch_us": bt["avg_launch_us"],
+                "launch_repeats_us": bt["repeats_us"], "launches_per_repeat": bt["launches_per_repeat"]}
 
-    # eager launches with per-launch events (host launch path included)
-    eager = {}
-    for n in NCOLS:
-        r = timed_launches(torch, lambda c, n=n: qmv.mmvq_q6k(c, XT, xq_of(n), out, ROWS, K, n), 100, copies)
-        eager[str(n)] = round(r["mean_us"], 3)
-
-    # checksum of the last step's N=8 output bits (FNV-1a 32)
+    # checksum of the last N=8 output bits (FNV-1a 32)
     torch.cuda.synchronize()
-    ob = out.cpu().numpy().view(np.uint32)
+    ob = outs[8].cpu().numpy().view(np.uint8)[:4096 * 4]
     h = np.uint32(2166136261)
-    for byte in ob.view(np.uint8)[:4096 * 4]:
+    for byte in ob:
         h = np.uint32((int(h) ^ int(byte)) * 16777619 & 0xFFFFFFFF)
 
-    extras = {"per_ncols": {str(n): per_n[n] for n in NCOLS},
-              "eager_event_us_per_launch": eager,
+    extras = {"single_launch_per_ncols": per_n,
+              "batched_launch": dict(bt, alg_bytes=batch_alg,
+                                     weight_GBps=round(step_bytes / (bt["avg_launch_us"] * 1e-6) / 1e9, 1)),
               "wall_ms_per_step": round(wall_ms_per_step, 4),
-              "one_graph_launch_per_step": {"ms_per_step": round(single_ms, 4),
-                                            "wall_ms_per_step": round(single_wall_ms, 4),
-                                            "weight_GBps": round(step_bytes / (max(single_ms, single_wall_ms) * 1e-3) / 1e9, 1)},
-              "steps_per_graph": ncopies,
+              "steps_per_graph": min(args.steps, ncopies),
               "weight_copies": ncopies, "weight_bytes_per_copy": wb,
               "fnv1a32_out_prefix": int(h),
               "pages_A770_us": PAGES_US}
+    if prof:
+        extras["rocprof"] = prof
     if not args.no_extras:
-        extras.update(run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out))
+        xq8 = xq_all[:8 * qcol]
+        extras.update(run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq8, outs[8]))
 
     cpu = None
     if not args.no_cpu:
@@ -301,10 +441,11 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": round(value / pages_gbs, 2), "dtype": "int8",
         "data": "synthetic",
-        "config": {"workload": "Q6_K MMVQ 10240x2560 (rows x cols), tiled weights (matrix cores), 1/4/8 columns, "
-                               "one Q8_1 quantize (column-planar layout) of the 13 activation columns + the three MMVQs, "
-                               f"weights rotated over {ncopies} HBM copies",
-                   "rows": ROWS, "cols": K, "ncols": list(NCOLS),
+        "config": {"workload": "Q6_K MMVQ 10240x2560 (rows x cols), tiled weights (matrix cores), 8, 4 and 1 "
+                               "columns on three weight copies in one batched launch, after one Q8_1 quantize "
+                               "(column-planar layout) of the 13 activation columns; weights rotated over "
+                               f"{ncopies} HBM copies",
+                   "rows": ROWS, "cols": K, "ncols": list(JOBS),
                    "vs_baseline_basis": f"pages' A770 large-GRF figures for this matrix "
                                         f"(86.1/92.9/370.5 us) = {pages_gbs:.1f} GB/s; other hardware, context"},
         "roofline": roofline,
@@ -576,6 +717,7 @@ def cpu_baseline(np, synth, w_np, x_np, seconds):
         all_s, all_reps = timed(pool, cores, seconds * 0.6)
     step_bytes = weight_bytes(ROWS, K) * len(NCOLS)
     return {"value": round(step_bytes / all_s / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"the full step (10240x2560 Q6_K, quantize 13 columns + products at N=1,4,8): "
                       f"{all_reps} steps at {all_s * 1e3:.1f} ms/step with rows split over {cores} threads; "
                       f"{one_reps} steps at {one_s * 1e3:.1f} ms/step "
