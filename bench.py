@@ -15,9 +15,12 @@ products read three of 26 copies (559 MB, more than twice the 256 MB
 Infinity Cache), rotating, so every weight byte comes from HBM.
 
 Timing: exactly `steps` steps, replayed from HIP graphs holding
-min(steps, 26) consecutive steps (and one graph for a remainder), with HIP
-events on the launch stream and host wall time around them (the larger is
-used).  `value` = weight bytes of the three products / step time (GB/s).
+min(steps, 26) consecutive steps (and one graph for a remainder), between
+two synchronizations; `value` = weight bytes of the three products / step
+time (GB/s), the step time from HIP events on the launch stream around the
+steps (the device's time, the wait for the first graph launch included;
+the host wall time, which adds the host's own launch and synchronization
+calls, is reported beside it).
 
 `roofline` is for the dominant kernel (the batched launch): algorithmic
 bytes per launch over its average launch duration, from HIP events on its
@@ -385,7 +388,7 @@ def main():
         torch.cuda.synchronize()
     ms_per_step, wall_ms_per_step = timed_steps(args.steps)
     step_bytes = wb * len(JOBS)
-    value = step_bytes / (max(ms_per_step, wall_ms_per_step) * 1e-3) / 1e9
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # Per-launch averages: the batched launch (the dominant kernel) and the
     # single products per column count.
@@ -421,6 +424,7 @@ def main():
                                      weight_GBps=round(step_bytes / (bt["avg_launch_us"] * 1e-6) / 1e9, 1)),
               "wall_ms_per_step": round(wall_ms_per_step, 4),
               "steps_per_graph": min(args.steps, ncopies),
+              "wall_clock_weight_GBps": round(step_bytes / (wall_ms_per_step * 1e-3) / 1e9, 1),
               "weight_copies": ncopies, "weight_bytes_per_copy": wb,
               "fnv1a32_out_prefix": int(h),
               "pages_A770_us": PAGES_US}
