@@ -72,7 +72,9 @@ struct Q6Tiled {
 // Weight steps whose code-plane loads are issued before the activation tile
 // is stored (the rest follow it): measured best at two, and at three with
 // eight or more waves along K (of 1, 2, 3 and all five; 2560x10240:
-// 0.05-0.1 us faster than two).
+// 0.05-0.1 us faster than two).  Re-measured in the batched launch of three
+// 10240x2560 products (8, 4, 1 columns): 1, 3 and all five steps, and
+// per-wave staging with four waves along K, all within -0.1..+0.6 us of two.
 constexpr int kTiledPre = 2, kTiledPreLong = 3;
 
 
@@ -590,7 +592,9 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const T
     extern __shared__ __align__(16) uint8_t lds[];
     const int b = blockIdx.x;
     // this workgroup's job, and its fields, by selects over the (scalar)
-    // kernel arguments rather than an indexed access
+    // kernel arguments rather than an indexed access.  (The jobs' workgroups
+    // handed out interleaved, round by round, measured 0.2-0.4 us slower on
+    // three 10240x2560 products than each job's in one consecutive range.)
     int j = 0;
 #pragma unroll
     for (int i = 1; i < kMaxTiledJobs; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
