@@ -259,6 +259,27 @@ int mmvq_q6k_argmax(const void *w, int layout, const void *xq, int64_t rows, int
                     void *stream);
 size_t mmvq_q6k_argmax_workspace(int64_t rows, int ncols);
 
+/* The k largest outputs of each column of the product (the candidates a
+ * verify window keeps when it samples beyond the greedy token; the pages'
+ * verify path runs the LM head at 1-8 columns, PR #2207 "Summary", with the
+ * draft head taken from the converted head, PR #2340 "What it changes"):
+ * for each column n, idx[n][i] and val[n][i] (i = 0..k-1) are the rows and
+ * fp32 values of mmvq_q6k's outputs in descending order of value, among
+ * equal values the lower row first, -0 counted as +0; the values are bit for
+ * bit mmvq_q6k's outputs for the same inputs.  Any layout mmvq_q6k takes.
+ * 1 <= k <= 64, k <= rows, and ceil(rows/4096) * k <= 4096 (k = 64 up to
+ * 262,144 rows; k = 16 up to 1,048,576).  idx int32 [ncols][k], val fp32
+ * [ncols][k] (4-byte aligned); ws: device workspace of at least
+ * mmvq_q6k_topk_workspace(rows, ncols, k) bytes, 256-byte aligned,
+ * overwritten: the product's fp32 outputs [ncols][rows], then (at the next
+ * 256-byte boundary) 8-byte candidate keys.  Three launches: the product,
+ * a radix select of the k largest keys of each 4096-row chunk, a radix
+ * select of each column's candidates ranked into order.  Other arguments and
+ * checks as for mmvq_q6k; outputs must be finite. */
+int mmvq_q6k_topk(const void *w, int layout, const void *xq, int64_t rows, int64_t K, int ncols,
+                  int k, int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream);
+size_t mmvq_q6k_topk_workspace(int64_t rows, int ncols, int k);
+
 /* Per-sub-block integer sums of the same kernels (for verification):
  * isums int32 [ncols][rows][K/32].  Q6_K: sum over the sub-block's two
  * 16-weight groups of scale * sum (q6-32)*q8.  Q4_K/Q5_K: sum q*q8 of the

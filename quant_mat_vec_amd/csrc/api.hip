@@ -46,6 +46,23 @@ int check_mmvq(const void *w, const void *xq, const void *out, int64_t rows, int
     return QMV_OK;
 }
 
+// The checks of a Q6_K product's weights, activations and shape (layout
+// with the activation flag), outputs aside.
+int q6_check(const void *w, int layout_arg, const void *xq, int64_t rows, int64_t K, int ncols) {
+    const bool xp = (layout_arg & QMV_ACT_PLANAR) != 0;
+    const int layout = layout_arg & ~QMV_ACT_PLANAR;
+    if ((layout != QMV_LAYOUT_GGUF && layout != QMV_LAYOUT_PLANAR && layout != QMV_LAYOUT_TILED) ||
+        (xp && layout != QMV_LAYOUT_TILED)) {
+        if (!w || !xq) return QMV_ERR_INVALID_ARG;
+        return QMV_ERR_UNSUPPORTED;
+    }
+    // (a 4-byte aligned stand-in for the output: only its alignment is checked)
+    int rc = check_mmvq(w, xq, xq, rows, K, ncols, 210, layout == QMV_LAYOUT_GGUF ? 4 : 16);
+    if (rc) return rc;
+    if (xp && !aligned(xq, 16)) return QMV_ERR_ALIGNMENT;
+    return QMV_OK;
+}
+
 int q6_dispatch(const void *w, int layout_arg, const void *xq, float *out, int32_t *dump, int64_t rows,
                 int64_t K, int ncols, void *stream) {
     const bool xp = (layout_arg & QMV_ACT_PLANAR) != 0;
@@ -303,6 +320,32 @@ int mmvq_q6k_argmax(const void *w, int layout, const void *xq, int64_t rows, int
     if (ws_bytes < mmvq_q6k_argmax_workspace(rows, ncols)) return QMV_ERR_WORKSPACE;
     return from_hip(qmv::launch_mmvq_q6_tiled_argmax(w, xq, reinterpret_cast<uint64_t *>(ws), rows, K, ncols, idx,
                                                      val, xp, as_stream(stream)));
+}
+
+size_t mmvq_q6k_topk_workspace(int64_t rows, int ncols, int k) {
+    if (rows <= 0 || rows > kMaxProductRows || ncols < 1 || ncols > 8 || k < 1 || k > qmv::kTopkMax || k > rows)
+        return 0;
+    const int64_t nchunks = (rows + qmv::kTopkChunk - 1) / qmv::kTopkChunk;
+    if (nchunks * k > qmv::kTopkChunk) return 0;
+    const int64_t outs = (4 * rows * ncols + 255) & ~(int64_t)255;
+    return (size_t)(outs + 8 * nchunks * k * ncols);
+}
+
+int mmvq_q6k_topk(const void *w, int layout, const void *xq, int64_t rows, int64_t K, int ncols, int k,
+                  int32_t *idx, float *val, void *ws, size_t ws_bytes, void *stream) {
+    if (!idx || !val || !ws || !w || !xq || k < 1) return QMV_ERR_INVALID_ARG;
+    const int rc = q6_check(w, layout, xq, rows, K, ncols);
+    if (rc) return rc;
+    if (k > qmv::kTopkMax || k > rows || ((rows + qmv::kTopkChunk - 1) / qmv::kTopkChunk) * k > qmv::kTopkChunk)
+        return QMV_ERR_UNSUPPORTED;
+    if (!aligned(idx, 4) || !aligned(val, 4) || !aligned(ws, 256)) return QMV_ERR_ALIGNMENT;
+    if (ws_bytes < mmvq_q6k_topk_workspace(rows, ncols, k)) return QMV_ERR_WORKSPACE;
+    float *out = reinterpret_cast<float *>(ws);
+    const int64_t outs = (4 * rows * ncols + 255) & ~(int64_t)255;
+    uint64_t *cand = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(ws) + outs);
+    const int e = q6_dispatch(w, layout, xq, out, nullptr, rows, K, ncols, stream);
+    if (e) return e;
+    return from_hip(qmv::launch_topk(out, rows, ncols, k, cand, idx, val, as_stream(stream)));
 }
 
 size_t grouped_expert_mmvq_workspace(int E, int T, int topk, int64_t d_model, int64_t d_ff) {

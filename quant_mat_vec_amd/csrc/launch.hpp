@@ -54,6 +54,12 @@ __host__ __device__ inline int64_t argmax_tail(int64_t ntiles, int ncols) {
 }
 hipError_t launch_mmvq_q6_tiled_argmax(const void *w, const void *xq, uint64_t *keys, int64_t rows, int64_t K,
                                        int ncols, int32_t *idx, float *val, bool xp, hipStream_t s);
+// Top-k rows per column of fp32 outputs [ncols][rows] (k <= kTopkMax,
+// ceil(rows / kTopkChunk) * k <= kTopkChunk); cand: ncols * ceil(rows /
+// kTopkChunk) * k keys of scratch; idx/val [ncols][k], descending.
+constexpr int kTopkChunk = 4096, kTopkMax = 64;
+hipError_t launch_topk(const float *out, int64_t rows, int ncols, int k, uint64_t *cand, int32_t *idx, float *val,
+                       hipStream_t s);
 hipError_t launch_mmvq_q6_gguf(const void *w, const void *xq, float *out, int32_t *dump,
                                int64_t rows, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_mmvq_q4(const void *w, const void *xq, float *out, int32_t *dump,

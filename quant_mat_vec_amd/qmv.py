@@ -60,6 +60,7 @@ def lib() -> ctypes.CDLL:
             "unpack_q6k_tiled": [P, P, I64, I64, P],
             "gather_q6k_rows": [P, I, I64, I64, P, I64, P, P],
             "mmvq_q6k_argmax": [P, I, P, I64, I64, I, P, P, P, SZ, P],
+            "mmvq_q6k_topk": [P, I, P, I64, I64, I, I, P, P, P, SZ, P],
             "mmvq_q6k_isums": [P, I, P, P, I64, I64, I, P],
             "mmvq_q4k_isums": [P, P, P, I64, I64, I, P],
             "mmvq_q5k_isums": [P, P, P, I64, I64, I, P],
@@ -74,6 +75,8 @@ def lib() -> ctypes.CDLL:
         L.mmvq_q6k_batch.argtypes = [ctypes.POINTER(Q6kJob), I, I, I64, P]
         L.mmvq_q6k_batch.restype = I
         L.grouped_expert_mmvq_workspace.argtypes = [I, I, I, I64, I64]
+        L.mmvq_q6k_topk_workspace.restype = SZ
+        L.mmvq_q6k_topk_workspace.argtypes = [I64, I, I]
         L.mmvq_q6k_argmax_workspace.restype = SZ
         L.mmvq_q6k_argmax_workspace.argtypes = [I64, I]
         L.grouped_expert_mmvq_workspace.restype = SZ
@@ -184,6 +187,16 @@ def mmvq_q6k_argmax(w, layout: int, xq, rows: int, K: int, ncols: int, idx, val,
                     stream=None) -> None:
     _check(lib().mmvq_q6k_argmax(_ptr(w), layout, _ptr(xq), rows, K, ncols, _ptr(idx), _ptr(val), _ptr(ws),
                                  ws_bytes, _stream(stream)), "mmvq_q6k_argmax")
+
+
+def mmvq_q6k_topk_workspace(rows: int, ncols: int, k: int) -> int:
+    return int(lib().mmvq_q6k_topk_workspace(rows, ncols, k))
+
+
+def mmvq_q6k_topk(w, layout: int, xq, rows: int, K: int, ncols: int, k: int, idx, val, ws, ws_bytes: int,
+                  stream=None) -> None:
+    _check(lib().mmvq_q6k_topk(_ptr(w), layout, _ptr(xq), rows, K, ncols, k, _ptr(idx), _ptr(val), _ptr(ws),
+                               ws_bytes, _stream(stream)), "mmvq_q6k_topk")
 
 
 def mmvq_q6k_isums(w, layout: int, xq, isums, rows: int, K: int, ncols: int, stream=None) -> None:

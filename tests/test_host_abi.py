@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
                 "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
                 "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "grouped_expert_mmvq_noalloc",
-                "mmvq_q6k_batch", "qmv_strerror",
+                "mmvq_q6k_batch", "mmvq_q6k_topk", "mmvq_q6k_topk_workspace", "qmv_strerror",
                 "qmv_last_hip_error", "qmv_stream_read"}
     assert expected <= set(names), set(names) ^ expected
     for n in names:
@@ -189,6 +189,27 @@ def test_argmax_rejects(L):
     assert call(lay=qmv.LAYOUT_PLANAR | qmv.ACT_PLANAR) == E_UNS
     assert call(lay=XT, xq=P + 4) == E_ALN
     assert call(lay=XT, wsb=nws - 1) == E_WS
+
+
+def test_topk_rejects_and_workspace(L):
+    f = L.mmvq_q6k_topk
+    TL = qmv.LAYOUT_TILED
+    nws = L.mmvq_q6k_topk_workspace(100, 4, 8)
+    assert nws == (4 * 100 * 4 + 255) // 256 * 256 + 8 * 1 * 8 * 4
+    assert L.mmvq_q6k_topk_workspace(100, 4, 0) == 0 and L.mmvq_q6k_topk_workspace(100, 4, 65) == 0
+    assert L.mmvq_q6k_topk_workspace(5, 4, 6) == 0 and L.mmvq_q6k_topk_workspace(100, 9, 4) == 0
+    assert L.mmvq_q6k_topk_workspace(4096 * 65, 1, 64) == 0          # 65 chunks x 64 candidates > 4096
+
+    def call(w=P, lay=TL, xq=P, rows=100, K=512, n=4, k=8, idx=P, val=P, ws=P, wsb=nws):
+        return f(w, lay, xq, rows, K, n, k, idx, val, ws, wsb, None)
+
+    assert call(idx=None) == E_INV and call(val=None) == E_INV and call(ws=None) == E_INV
+    assert call(w=None) == E_INV and call(k=0) == E_INV and call(rows=0) == E_INV
+    assert call(k=65) == E_UNS and call(k=101) == E_UNS and call(n=9) == E_UNS and call(K=300) == E_UNS
+    assert call(lay=7) == E_UNS and call(lay=qmv.LAYOUT_PLANAR | qmv.ACT_PLANAR) == E_UNS
+    assert call(rows=4096 * 65, k=64) == E_UNS
+    assert call(w=P + 8) == E_ALN and call(idx=P + 2) == E_ALN and call(ws=P + 64) == E_ALN
+    assert call(wsb=nws - 1) == E_WS
 
 
 def test_moe_rejects_and_workspace(L):
