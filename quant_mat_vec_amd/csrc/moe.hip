@@ -9,8 +9,8 @@
 //   down    : the same selection, with a row tile of d_model: Q6_K MMVQ over
 //             the expert's requantized slots, y written per slot;
 //   combine : out[t] = sum over k, ascending, of route_w[t][k] * y[t][k].
-// Windows of at most eight slots with planar down weights run down and
-// combine as one launch (k_moe_down_combine, below).
+// With planar down weights (and d_ff <= 1024) down and combine are one
+// launch by (row block, token) instead (k_moe_down_tok, below).
 // The selection is one wave ballot over the slot ids (S <= 64 = one wave),
 // and an expert's slots are taken in ascending slot order.  No workgroup
 // reads the weights of an expert no slot is routed to.
@@ -322,115 +322,82 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs m) {
     m.out[(int64_t)t * m.d_model + i] = acc;
 }
 
-// ------------------------------------------------ down + combine, short window
-// For windows of at most kDcMaxS slots (one token at top-8) and planar down
-// weights: a workgroup
-// owns kDcRows rows of d_model and holds one wave per slot position; wave w
-// takes the w-th distinct expert (in order of first slot) and, for the
-// workgroup's rows, forms y for that expert's slots (in passes of two, in
-// ascending slot order) with its activation blocks held in registers -- the
-// Q6_K planar dot product and fp32 scaling of the dense kernel.  After one
-// barrier the workgroup sums out[t] for its rows: the same ascending-k fp32
-// sum as k_moe_combine, without the third launch.  y is also written to the
-// workspace.  Measured per call (E = 128, d_model 2560, d_ff 768): one token
-// 14.0 -> 12.9 us; at two tokens (16 slots) the three-launch chain was
-// faster (19.9 against 21.7 us), hence the limit.
-constexpr int kDcRows = 8;      // rows per workgroup: eight lanes per row, one wave
-constexpr int kDcMaxS = 8;      // slots (and waves) at most
-constexpr int kDcUnits = 3;     // sub-blocks per lane per pass over a row
+// ------------------------------------------------- down + routed sum, by token
+// Planar down weights, d_ff / 256 <= kDtMaxUnits: workgroup (x, t) owns
+// kDtRows rows of d_model for token t and holds one wave per routed slot of
+// the token.  Wave k forms y of slot t*topk + k for the workgroup's rows (its
+// expert's rows times the slot's requantized h, eight lanes per row, lane u
+// taking sub-blocks u, u + 8, ...; the h blocks go out before the slot id is
+// back), then after one barrier the token's routed sum of those rows is
+// formed in ascending k, as k_moe_combine does.  No workgroup waits on
+// another and there is no combine launch.  An expert routed from several
+// tokens is read once per token; the repeats are served by the caches
+// (measured HBM fetch in the design notes).  y is also written to the
+// workspace.
+constexpr int kDtRows = 8;       // rows per workgroup: eight lanes per row, one wave
+constexpr int kDtMaxUnits = 4;   // d_ff / 256 at most
 
-__global__ __launch_bounds__(kDcMaxS *kWave) void k_moe_down_combine(MoeArgs m) {
-    __shared__ float ylds[kDcMaxS][kDcRows];
+template <int UN>
+__global__ __launch_bounds__(8 * kWave) void k_moe_down_tok(MoeArgs m) {
+    __shared__ float ylds[8][kDtRows];
+    const int nsb = 8 * UN;                                  // d_ff / 32
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x & (kWave - 1);
-    int id = -1;
-    if (lane < m.S) {
-        id = m.ids[lane];
-        if (id < 0 || id >= m.E) id = -1;
-    }
-    const uint64_t valid = __ballot(id >= 0);
-    int pos = 0;                                  // earlier slots of the same expert
-    for (int t = 0; t < m.S; t++) {
-        const int et = __builtin_amdgcn_readlane(id, t);
-        if (et >= 0 && et == id && t < lane) pos++;
-    }
-    const uint64_t fo = __ballot(id >= 0 && pos == 0);   // first slot of each expert
-    const int64_t row0 = (int64_t)blockIdx.x * kDcRows;
     const int r = lane >> 3, u = lane & 7;
-    const int nsb = (int)(m.d_ff / 32);
-    float *yws = reinterpret_cast<float *>(m.ws + m.off_y);
+    const int tk = blockIdx.y, slot = tk * m.topk + wave;    // wave < topk (one wave per slot)
+    const int64_t row0 = (int64_t)blockIdx.x * kDtRows;
     const uint8_t *hq = m.ws + m.off_hq;
-    if (wave < __popcll(fo)) {
-        uint64_t f = fo;
-        for (int k = 0; k < wave; k++) f &= f - 1;
-        const int e = __builtin_amdgcn_readlane(id, (int)__ffsll((long long)f) - 1);
-        uint64_t mm = __ballot(id == e);
+    ActRaw x[UN];
+#pragma unroll
+    for (int k = 0; k < UN; k++) act_load(x[k], hq, (int64_t)slot * nsb + u + 8 * k);
+    const int e = m.ids[slot];
+    if (e >= 0 && e < m.E) {
+        // sub-blocks u + 8k of the row: with 8 * UN sub-blocks a row,
+        // sub-block u + 8k lies in the row's superblock k
         Q6Planar fmt;
         fmt.init(m.w_down, (int64_t)m.E * m.d_model, m.d_ff);
         const int64_t wrow = (int64_t)e * m.d_model + row0 + r;
-        while (mm) {
-            const int s0 = (int)__ffsll((long long)mm) - 1;
-            mm &= mm - 1;
-            const int s1 = mm ? (int)__ffsll((long long)mm) - 1 : -1;
-            if (s1 >= 0) mm &= mm - 1;
-            float a0 = 0.0f, a1 = 0.0f;
-            for (int c = 0; c < nsb; c += 8 * kDcUnits) {
-                Q6Planar::Raw w[kDcUnits];
-                ActRaw x0[kDcUnits], x1[kDcUnits];
+        const int64_t i0 = wrow * nsb + u;
+        Q6Planar::Raw w[UN];
 #pragma unroll
-                for (int k = 0; k < kDcUnits; k++) {
-                    const int sb = min(c + u + 8 * k, nsb - 1);
-                    fmt.load(w[k], wrow, sb);
-                    act_load(x0[k], hq, (int64_t)s0 * nsb + sb);
-                    if (s1 >= 0) act_load(x1[k], hq, (int64_t)s1 * nsb + sb);   // wave-uniform
-                }
+        for (int k = 0; k < UN; k++) {
+            w[k].a = fmt.A[i0 + 8 * k];
+            w[k].b = fmt.B[i0 + 8 * k];
+            w[k].sc = fmt.SC[i0 + 8 * k];
+            w[k].d = fmt.D[wrow * UN + k];
+        }
+        float a = 0.0f;
 #pragma unroll
-                for (int k = 0; k < kDcUnits; k++) {
-                    if (c + u + 8 * k >= nsb) continue;
-                    int v[8];
-                    Q6Planar::codes(w[k], v);
-                    const int sc0 = sext8(w[k].sc, 0), sc1 = sext8(w[k].sc, 1);
-                    const float dw = half_to_float(w[k].d);
-#pragma unroll
-                    for (int n = 0; n < 2; n++) {
-                        if (n == 1 && s1 < 0) break;
-                        const ActRaw &x = n == 0 ? x0[k] : x1[k];
-                        int d0 = sdot4(v[0], (int)x.w[1], 0);
-                        d0 = sdot4(v[1], (int)x.w[2], d0);
-                        d0 = sdot4(v[2], (int)x.w[3], d0);
-                        d0 = sdot4(v[3], (int)x.w[4], d0);
-                        int d1 = sdot4(v[4], (int)x.w[5], 0);
-                        d1 = sdot4(v[5], (int)x.w[6], d1);
-                        d1 = sdot4(v[6], (int)x.w[7], d1);
-                        d1 = sdot4(v[7], (int)x.w[8], d1);
-                        const int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact
-                        const float da = half_to_float(x.w[0]) * 0.25f;
-                        if (n == 0) a0 = __builtin_fmaf(dw * da, (float)isum4, a0);
-                        else a1 = __builtin_fmaf(dw * da, (float)isum4, a1);
-                    }
-                }
-            }
-            a0 = group_sum<8>(a0);
-            a1 = group_sum<8>(a1);
-            if (u == 0) {
-                ylds[s0][r] = a0;
-                yws[(int64_t)s0 * m.d_model + row0 + r] = a0;
-                if (s1 >= 0) {
-                    ylds[s1][r] = a1;
-                    yws[(int64_t)s1 * m.d_model + row0 + r] = a1;
-                }
-            }
+        for (int k = 0; k < UN; k++) {
+            int v[8];
+            Q6Planar::codes(w[k], v);
+            const int sc0 = sext8(w[k].sc, 0), sc1 = sext8(w[k].sc, 1);
+            int d0 = sdot4(v[0], (int)x[k].w[1], 0);
+            d0 = sdot4(v[1], (int)x[k].w[2], d0);
+            d0 = sdot4(v[2], (int)x[k].w[3], d0);
+            d0 = sdot4(v[3], (int)x[k].w[4], d0);
+            int d1 = sdot4(v[4], (int)x[k].w[5], 0);
+            d1 = sdot4(v[5], (int)x[k].w[6], d1);
+            d1 = sdot4(v[6], (int)x[k].w[7], d1);
+            d1 = sdot4(v[7], (int)x[k].w[8], d1);
+            const int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact
+            const float da = half_to_float(x[k].w[0]) * 0.25f;
+            a = __builtin_fmaf(half_to_float(w[k].d) * da, (float)isum4, a);
+        }
+        a = group_sum<8>(a);
+        if (u == 0) {
+            ylds[wave][r] = a;
+            reinterpret_cast<float *>(m.ws + m.off_y)[(int64_t)slot * m.d_model + row0 + r] = a;
         }
     }
-    __syncthreads();
-    const int j = threadIdx.x;
-    if (j < m.T * kDcRows) {
-        const int t = j / kDcRows, rr = j % kDcRows;
+    lds_barrier();
+    if (threadIdx.x < kDtRows) {
+        const int rr = threadIdx.x;
         float acc = 0.0f;
         for (int k = 0; k < m.topk; k++) {
-            const int sl = t * m.topk + k;
-            if ((valid >> sl) & 1) acc = __builtin_fmaf(m.route_w[sl], ylds[sl][rr], acc);
+            const int sl = tk * m.topk + k, ek = m.ids[sl];
+            if (ek >= 0 && ek < m.E) acc = __builtin_fmaf(m.route_w[sl], ylds[k][rr], acc);
         }
-        m.out[(int64_t)t * m.d_model + row0 + rr] = acc;
+        m.out[(int64_t)tk * m.d_model + row0 + rr] = acc;
     }
 }
 
@@ -518,9 +485,16 @@ hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s) {
     // keep the register budget of two waves per SIMD)
     hipError_t err = launch_gateup<8>(m, smax, s);
     if (err != hipSuccess) return err;
-    if (down_layout == 1 && m.S <= kDcMaxS && m.T * kDcRows <= m.S * kWave && m.d_model % kDcRows == 0) {
-        // short window: down and the weighted sum in one launch
-        hipLaunchKernelGGL(k_moe_down_combine, dim3((unsigned)(m.d_model / kDcRows)), dim3(m.S * kWave), 0, s, m);
+    const int un = (int)(m.d_ff / 256);
+    if (down_layout == 1 && un <= kDtMaxUnits && m.d_model % kDtRows == 0) {
+        // down and the routed sum in one launch, by (row block, token)
+        const dim3 grid((unsigned)(m.d_model / kDtRows), (unsigned)m.T), block(m.topk * kWave);
+        switch (un) {
+        case 1: hipLaunchKernelGGL(k_moe_down_tok<1>, grid, block, 0, s, m); break;
+        case 2: hipLaunchKernelGGL(k_moe_down_tok<2>, grid, block, 0, s, m); break;
+        case 3: hipLaunchKernelGGL(k_moe_down_tok<3>, grid, block, 0, s, m); break;
+        default: hipLaunchKernelGGL(k_moe_down_tok<4>, grid, block, 0, s, m); break;
+        }
         return hipGetLastError();
     }
     err = down_layout == 1 ? launch_down<Q6Planar>(m, smax, s) : launch_down<Q6Gguf>(m, smax, s);
