@@ -324,7 +324,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs m) {
 
 // ------------------------------------------------- down + routed sum, by token
 // Planar down weights, d_ff / 256 <= kDtMaxUnits: workgroup (x, t) owns
-// kDtRows rows of d_model for token t and holds one wave per routed slot of
+// 8 or 16 rows of d_model for token t and holds one wave per routed slot of
 // the token.  Wave k forms y of slot t*topk + k for the workgroup's rows (its
 // expert's rows times the slot's requantized h, eight lanes per row, lane u
 // taking sub-blocks u, u + 8, ...; the h blocks go out before the slot id is
@@ -334,63 +334,77 @@ __global__ __launch_bounds__(256) void k_moe_combine(MoeArgs m) {
 // tokens is read once per token; the repeats are served by the caches
 // (measured HBM fetch in the design notes).  y is also written to the
 // workspace.
-constexpr int kDtRows = 8;       // rows per workgroup: eight lanes per row, one wave
 constexpr int kDtMaxUnits = 4;   // d_ff / 256 at most
+constexpr int64_t kDtWideGrid = 1024;
 
-template <int UN>
+// RPL rows per lane (rows r and r + 8 when RPL = 2): 8 * RPL rows per
+// workgroup.
+template <int UN, int RPL>
 __global__ __launch_bounds__(8 * kWave) void k_moe_down_tok(MoeArgs m) {
-    __shared__ float ylds[8][kDtRows];
+    constexpr int ROWS = 8 * RPL;
+    __shared__ float ylds[8][ROWS];
     const int nsb = 8 * UN;                                  // d_ff / 32
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x & (kWave - 1);
     const int r = lane >> 3, u = lane & 7;
     const int tk = blockIdx.y, slot = tk * m.topk + wave;    // wave < topk (one wave per slot)
-    const int64_t row0 = (int64_t)blockIdx.x * kDtRows;
+    const int64_t row0 = (int64_t)blockIdx.x * ROWS;
     const uint8_t *hq = m.ws + m.off_hq;
     ActRaw x[UN];
 #pragma unroll
     for (int k = 0; k < UN; k++) act_load(x[k], hq, (int64_t)slot * nsb + u + 8 * k);
     const int e = m.ids[slot];
     if (e >= 0 && e < m.E) {
-        // sub-blocks u + 8k of the row: with 8 * UN sub-blocks a row,
+        // sub-blocks u + 8k of a row: with 8 * UN sub-blocks a row,
         // sub-block u + 8k lies in the row's superblock k
         Q6Planar fmt;
         fmt.init(m.w_down, (int64_t)m.E * m.d_model, m.d_ff);
-        const int64_t wrow = (int64_t)e * m.d_model + row0 + r;
-        const int64_t i0 = wrow * nsb + u;
-        Q6Planar::Raw w[UN];
+        Q6Planar::Raw w[RPL][UN];
 #pragma unroll
-        for (int k = 0; k < UN; k++) {
-            w[k].a = fmt.A[i0 + 8 * k];
-            w[k].b = fmt.B[i0 + 8 * k];
-            w[k].sc = fmt.SC[i0 + 8 * k];
-            w[k].d = fmt.D[wrow * UN + k];
-        }
-        float a = 0.0f;
+        for (int p = 0; p < RPL; p++) {
+            const int64_t wrow = (int64_t)e * m.d_model + row0 + r + 8 * p;
+            const int64_t i0 = wrow * nsb + u;
 #pragma unroll
-        for (int k = 0; k < UN; k++) {
-            int v[8];
-            Q6Planar::codes(w[k], v);
-            const int sc0 = sext8(w[k].sc, 0), sc1 = sext8(w[k].sc, 1);
-            int d0 = sdot4(v[0], (int)x[k].w[1], 0);
-            d0 = sdot4(v[1], (int)x[k].w[2], d0);
-            d0 = sdot4(v[2], (int)x[k].w[3], d0);
-            d0 = sdot4(v[3], (int)x[k].w[4], d0);
-            int d1 = sdot4(v[4], (int)x[k].w[5], 0);
-            d1 = sdot4(v[5], (int)x[k].w[6], d1);
-            d1 = sdot4(v[6], (int)x[k].w[7], d1);
-            d1 = sdot4(v[7], (int)x[k].w[8], d1);
-            const int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact
-            const float da = half_to_float(x[k].w[0]) * 0.25f;
-            a = __builtin_fmaf(half_to_float(w[k].d) * da, (float)isum4, a);
+            for (int k = 0; k < UN; k++) {
+                w[p][k].a = fmt.A[i0 + 8 * k];
+                w[p][k].b = fmt.B[i0 + 8 * k];
+                w[p][k].sc = fmt.SC[i0 + 8 * k];
+                w[p][k].d = fmt.D[wrow * UN + k];
+            }
         }
-        a = group_sum<8>(a);
+        float a[RPL];
+#pragma unroll
+        for (int p = 0; p < RPL; p++) {
+            a[p] = 0.0f;
+#pragma unroll
+            for (int k = 0; k < UN; k++) {
+                int v[8];
+                Q6Planar::codes(w[p][k], v);
+                const int sc0 = sext8(w[p][k].sc, 0), sc1 = sext8(w[p][k].sc, 1);
+                int d0 = sdot4(v[0], (int)x[k].w[1], 0);
+                d0 = sdot4(v[1], (int)x[k].w[2], d0);
+                d0 = sdot4(v[2], (int)x[k].w[3], d0);
+                d0 = sdot4(v[3], (int)x[k].w[4], d0);
+                int d1 = sdot4(v[4], (int)x[k].w[5], 0);
+                d1 = sdot4(v[5], (int)x[k].w[6], d1);
+                d1 = sdot4(v[6], (int)x[k].w[7], d1);
+                d1 = sdot4(v[7], (int)x[k].w[8], d1);
+                const int isum4 = __mul24(sc0, d0) + __mul24(sc1, d1);   // 4 * isum, exact
+                const float da = half_to_float(x[k].w[0]) * 0.25f;
+                a[p] = __builtin_fmaf(half_to_float(w[p][k].d) * da, (float)isum4, a[p]);
+            }
+            a[p] = group_sum<8>(a[p]);
+        }
         if (u == 0) {
-            ylds[wave][r] = a;
-            reinterpret_cast<float *>(m.ws + m.off_y)[(int64_t)slot * m.d_model + row0 + r] = a;
+            float *yws = reinterpret_cast<float *>(m.ws + m.off_y) + (int64_t)slot * m.d_model + row0;
+#pragma unroll
+            for (int p = 0; p < RPL; p++) {
+                ylds[wave][r + 8 * p] = a[p];
+                yws[r + 8 * p] = a[p];
+            }
         }
     }
     lds_barrier();
-    if (threadIdx.x < kDtRows) {
+    if (threadIdx.x < ROWS) {
         const int rr = threadIdx.x;
         float acc = 0.0f;
         for (int k = 0; k < m.topk; k++) {
@@ -486,16 +500,26 @@ hipError_t launch_moe(const MoeArgs &m, int down_layout, hipStream_t s) {
     hipError_t err = launch_gateup<8>(m, smax, s);
     if (err != hipSuccess) return err;
     const int un = (int)(m.d_ff / 256);
-    if (down_layout == 1 && un <= kDtMaxUnits && m.d_model % kDtRows == 0) {
-        // down and the routed sum in one launch, by (row block, token)
-        const dim3 grid((unsigned)(m.d_model / kDtRows), (unsigned)m.T), block(m.topk * kWave);
-        switch (un) {
-        case 1: hipLaunchKernelGGL(k_moe_down_tok<1>, grid, block, 0, s, m); break;
-        case 2: hipLaunchKernelGGL(k_moe_down_tok<2>, grid, block, 0, s, m); break;
-        case 3: hipLaunchKernelGGL(k_moe_down_tok<3>, grid, block, 0, s, m); break;
-        default: hipLaunchKernelGGL(k_moe_down_tok<4>, grid, block, 0, s, m); break;
+    if (down_layout == 1 && un <= kDtMaxUnits && m.d_model % 16 == 0) {
+        // down and the routed sum in one launch, by (row block, token); two
+        // rows per lane once that still gives kDtWideGrid workgroups (one
+        // token at d_model 2560: 12.7 -> 12.5 us per call; two: 18.1 ->
+        // 18.8 us, so one row there; eight: 46.6 -> 44.5-45.2 us)
+        const bool two = (m.d_model / 16) * m.T >= kDtWideGrid;
+        const dim3 grid((unsigned)(m.d_model / (two ? 16 : 8)), (unsigned)m.T), block(m.topk * kWave);
+        const void *k = nullptr;
+        switch (un * 2 + (two ? 1 : 0)) {
+        case 2: k = reinterpret_cast<const void *>(&k_moe_down_tok<1, 1>); break;
+        case 3: k = reinterpret_cast<const void *>(&k_moe_down_tok<1, 2>); break;
+        case 4: k = reinterpret_cast<const void *>(&k_moe_down_tok<2, 1>); break;
+        case 5: k = reinterpret_cast<const void *>(&k_moe_down_tok<2, 2>); break;
+        case 6: k = reinterpret_cast<const void *>(&k_moe_down_tok<3, 1>); break;
+        case 7: k = reinterpret_cast<const void *>(&k_moe_down_tok<3, 2>); break;
+        case 8: k = reinterpret_cast<const void *>(&k_moe_down_tok<4, 1>); break;
+        default: k = reinterpret_cast<const void *>(&k_moe_down_tok<4, 2>); break;
         }
-        return hipGetLastError();
+        void *args[] = {const_cast<MoeArgs *>(&m)};
+        return hipLaunchKernel(k, grid, block, args, 0, s);
     }
     err = down_layout == 1 ? launch_down<Q6Planar>(m, smax, s) : launch_down<Q6Gguf>(m, smax, s);
     if (err != hipSuccess) return err;
