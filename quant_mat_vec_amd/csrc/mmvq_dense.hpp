@@ -151,6 +151,8 @@ hipError_t launch_dense_u(const void *w, const void *xq, float *out, int32_t *du
     }
 }
 
+constexpr int64_t kDenseFillWaves = 256;
+
 template <class F, bool DUMP>
 hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
                         int ncols, hipStream_t s) {
@@ -159,8 +161,17 @@ hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump
     // row that leave each lane at least two units, the last chunk ragged if
     // need be -- at K = 2560, 16 lanes and 2.5 units measured 7-15 % faster
     // than 8 lanes and 5 units (twice the waves; 6144 and 12288 rows, N = 1
-    // and 4).  Q6_K keeps choose_u.  Either way a function of K only.
-    const int u = F::SBPU == 2 ? choose_u_min2(units) : choose_u(units);
+    // and 4).  Q6_K keeps choose_u (a function of K only, so planar and GGUF
+    // outputs are the same bits).
+    int u = F::SBPU == 2 ? choose_u_min2(units) : choose_u(units);
+    // Q4_K/Q5_K matrices too short to give every CU a wave take more lanes
+    // per row while each lane keeps a unit: 512 x 2560 (128 waves at 16
+    // lanes) at 32 lanes, N = 1 / 4: Q4_K 2.49 / 3.47 -> 2.39 / 3.30 us, Q5_K
+    // 2.84 / 3.90 -> 2.67 / 3.61 us.  At 2560 x 2560 (640 waves) 32 lanes
+    // were slower (Q4_K 2.99 -> 3.27 us).  Not a function of the column
+    // count, so every column's sum is the same at any N.
+    if (F::SBPU == 2)
+        while (u < 64 && rows * u / kWave < kDenseFillWaves && units >= 2 * u) u *= 2;
     switch (u) {
     case 8: return launch_dense_u<F, 8, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     case 16: return launch_dense_u<F, 16, DUMP>(w, xq, out, dump, rows, K, ncols, s);
