@@ -113,7 +113,39 @@ def resource_table() -> str:
     return "\n".join(rows)
 
 
+def resource_summary() -> str:
+    """Markdown: per kernel template (by source file) the instantiation count
+    and the range of each resource, then one row per instantiation (template
+    arguments kept, parameter lists dropped)."""
+    import collections
+    import re
+    with open(RESOURCES) as f:
+        ks = json.load(f)
+    names = [n.replace("qmv::", "").replace("(anonymous namespace)::", "").replace("void ", "")
+             for n in demangled([k["kernel"] for k in ks])]
+    short = [re.sub(r"\((?:[^()]|\([^()]*\))*\)$", "", n).strip() for n in names]
+    fam = collections.defaultdict(list)
+    for k, n in zip(ks, short):
+        fam[(k["source"], re.split(r"[<(]", n)[0])].append(k)
+    rows = ["| source | kernel template | instantiations | VGPRs | AGPRs max | spills max | scratch B/lane max | "
+            "waves/SIMD min |", "|---|---|---|---|---|---|---|---|"]
+    for (src, f), v in sorted(fam.items()):
+        g = lambda key: [x.get(key) or 0 for x in v]  # noqa: E731
+        rows.append(f"| {src} | `{f}` | {len(v)} | {min(g('vgprs'))}-{max(g('vgprs'))} | {max(g('agprs'))} | "
+                    f"{max(g('vgpr_spill')) + max(g('sgpr_spill'))} | {max(g('scratch_bytes_per_lane'))} | "
+                    f"{min(g('occupancy_waves_per_simd'))} |")
+    rows += ["", "| source | kernel | VGPRs | AGPRs | SGPRs | spills V/S | scratch B/lane | waves/SIMD | LDS B |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k, n in sorted(zip(ks, short), key=lambda kn: (kn[0]["source"], kn[1])):
+        rows.append(f"| {k['source']} | `{n}` | {k.get('vgprs')} | {k.get('agprs')} | {k.get('sgprs')} | "
+                    f"{k.get('vgpr_spill')}/{k.get('sgpr_spill')} | {k.get('scratch_bytes_per_lane')} | "
+                    f"{k.get('occupancy_waves_per_simd')} | {k.get('static_lds_bytes')} |")
+    return "\n".join(rows)
+
+
 if __name__ == "__main__":
     build()
     if "--table" in sys.argv[1:]:
         print(resource_table())
+    if "--summary" in sys.argv[1:]:
+        print(resource_summary())
