@@ -91,6 +91,10 @@ def parse():
     p.add_argument("--trace-workload", action="store_true",
                    help="only run 3 repeats of at least 2000 batched launches and of single launches per column "
                         "count (the workload of the kernel trace), print nothing")
+    p.add_argument("--pmc-dense", metavar="KIND:ROWSxK",
+                   help="only run 30 launches each at 1 and 4 columns of the Q4_K or Q5_K product (e.g. "
+                        "q4k:12288x2560) on rotated copies, 30 plain streaming reads of the same bytes and 30 "
+                        "device copies of them (for rocprofv3 --pmc passes), print nothing")
     p.add_argument("--pmc-mmq", action="store_true",
                    help="only run 8 launches of the 512-column product mmq_q6k on the same matrix "
                         "(for rocprofv3 --pmc passes), print nothing")
@@ -265,7 +269,7 @@ def main():
               "across GPUs; no multi-GPU path is built). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
-    workload_only = args.pmc_workload or args.trace_workload or args.pmc_mmq
+    workload_only = args.pmc_workload or args.trace_workload or args.pmc_mmq or args.pmc_dense
     prof, traffic = ({}, None)
     if not workload_only and not args.no_profile:
         prof, traffic = profile_children(sys.executable)
@@ -281,6 +285,9 @@ def main():
     # priority, like every stream here)
     torch.cuda.set_stream(torch.cuda.Stream())
     stream = torch.cuda.current_stream()
+    if args.pmc_dense:
+        dense_pmc_workload(torch, qmv, synth, dev, args.pmc_dense)
+        return
     # tiled weights (matrix cores), column-planar Q8_1 activations
     XT = qmv.LAYOUT_TILED | qmv.ACT_PLANAR
     g = synth.rng(synth.seed_for(1, 1, 8))
@@ -645,6 +652,32 @@ def lm_head_case(torch, np, qmv, synth, dev):
     del cs, dcs
     torch.cuda.empty_cache()
     return res
+
+
+def dense_pmc_workload(torch, qmv, synth, dev, spec):
+    """Counter workload of one Q4_K/Q5_K product: 30 launches at N = 1, then
+    at N = 4, on weight copies rotated past the Infinity Cache; 30 plain
+    streaming reads and 30 device copies of the same bytes."""
+    kind, shape = spec.split(":")
+    rows, k = (int(v) for v in shape.split("x"))
+    g = synth.rng(synth.seed_for(3, 0, 0))
+    blk = synth.q4k_blocks(g, rows, k) if kind == "q4k" else synth.q5k_blocks(g, rows, k)
+    base = torch.from_numpy(blk).to(dev)
+    copies = [base.clone() for _ in range(max(2, math.ceil(2 * MALL_BYTES / blk.size) + 1))]
+    fn = qmv.mmvq_q4k if kind == "q4k" else qmv.mmvq_q5k
+    for n in (1, 4):
+        xq = torch.empty(n * (k // 32) * 36, dtype=torch.uint8, device=dev)
+        qmv.quantize_q8_1(torch.from_numpy(synth.activations(g, n, k)).to(dev), xq, k, n)
+        out = torch.empty(n * rows, dtype=torch.float32, device=dev)
+        for i in range(30):
+            fn(copies[i % len(copies)], xq, out, rows, k, n)
+    sink = torch.empty(1 << 18, dtype=torch.int32, device=dev)
+    for i in range(30):
+        qmv.qmv_stream_read(copies[i % len(copies)], blk.size // 16 * 16, sink, 0)
+    dst = torch.empty_like(base)
+    for i in range(30):
+        dst.copy_(copies[i % len(copies)])
+    torch.cuda.synchronize()
 
 
 def moe_case(torch, np, qmv, synth, dev):
