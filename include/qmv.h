@@ -165,8 +165,15 @@ int rmsnorm_quantize_q8_1(const float *x, const float *gamma, float eps, void *x
  * 4-byte aligned; QMV_LAYOUT_PLANAR, QMV_LAYOUT_TILED: the layouts above,
  * 16-byte aligned).  xq: Q8_1 [ncols][K/32], 4-byte aligned.  out: fp32
  * [ncols][rows], 4-byte aligned.  K % 256 == 0, 1 <= ncols <= 8.
- * GGUF and planar inputs run on the vector ALU (dot4); tiled inputs on the
- * int8 matrix cores.  layout = QMV_LAYOUT_TILED | QMV_ACT_PLANAR takes
+ * GGUF and planar inputs run on the vector ALU (v_dot4_i32_i8); tiled
+ * inputs on the int8 matrix cores (v_mfma_i32_16x16x64_i8, each 16-weight
+ * scale group kept apart by masking the activation operand).  The matrix
+ * cores are used although 1-8 columns are a bandwidth-bound GEMV because the
+ * dot4 form is issue-bound on this GPU: at 8 columns of a 10240 x 2560
+ * matrix a dot4 wave issues ~830 VALU instructions (~5 us of issue per SIMD,
+ * longer than the ~4.5 us weight stream; 8.5 us per call), the matrix-core
+ * wave ~450 (6.9 us per call), with HBM traffic 1.01x the weight bytes in
+ * both.  layout = QMV_LAYOUT_TILED | QMV_ACT_PLANAR takes
  * column-planar activations (xq 16-byte aligned); any other layout with
  * QMV_ACT_PLANAR is QMV_ERR_UNSUPPORTED. */
 int mmvq_q6k(const void *w, int layout, const void *xq, float *out,
