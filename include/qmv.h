@@ -308,8 +308,12 @@ int mmvq_q5k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows,
  *   hq = quantize_q8_1(h)                         (d_ff/32 blocks)
  *   y = down_e . hq                               (Q6_K MMVQ, d_model rows)
  *   out[t] = sum over k = 0..topk-1, in that order, of route_w[t][k] * y.
- * Each expert's weights are read once for all tokens routed to it; experts
- * with no token are not read.
+ * Each expert's gate and up rows are read once for all tokens routed to it;
+ * its down rows once per routed token with planar down weights (two
+ * launches: gate/up, then down and the routed sum by (row block, token);
+ * the repeats mostly come from the caches) and once with GGUF down weights
+ * (three launches: gate/up, down, the routed sum).  Experts with no token
+ * are not read.
  *   w_gate, w_up: Q4_K [E][d_ff][d_model/256] blocks, 16-byte aligned.
  *   w_down: Q6_K [E][d_model][d_ff/256] in down_layout (GGUF: 4-byte
  *     aligned; planar: 16-byte aligned, the repack_q6k_planar of the whole
@@ -335,7 +339,7 @@ int mmvq_q5k_isums(const void *w, const void *xq, int32_t *isums, int64_t rows,
  *     fp32 y[S][d_model] @Y = align256(HQ + 36*S*d_ff/32).
  *   The workspace is overwritten; ids that repeat within a token are handled
  *   (their slots are processed like any other) but break the "read once"
- *   property. */
+ *   property of gate and up. */
 int grouped_expert_mmvq(const void *w_gate, const void *w_up, const void *w_down,
                         int down_layout, const void *xq, const int32_t *ids,
                         const float *route_w, float *out, int E, int T, int topk,
