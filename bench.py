@@ -533,11 +533,52 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
     for kind in ("q4k", "q5k"):
         for (r_, k_) in ((12288, 2560), (6144, 2560), (2560, 6144), (512, 2560)):
             ex[f"{kind}_{r_}x{k_}"] = shape_case(kind, r_, k_, (1, 4), seed=15 + r_)
+        ex[f"{kind}_batch_12288_6144_512x2560"] = q45_batch_case(torch, qmv, synth, dev, kind)
     ex["moe_e128_2560_768"] = moe_case(torch, np, qmv, synth, dev)
     ex["rmsnorm_quantize_13x2560"] = norm_case(torch, np, qmv, synth, dev)
     ex["q6k_many_columns_mmq"] = {f"{r_}x{k_}": prefill_case(torch, qmv, synth, dev, r_, k_)
                                   for (r_, k_) in ((10240, 2560), (2560, 10240))}
     return ex
+
+
+def q45_batch_case(torch, qmv, synth, dev, kind, k=2560, shapes=(12288, 6144, 512), ncols_list=(1, 4)):
+    """The dense matrices of one K (12288, 6144 and 512 rows x 2560), each on
+    its own weights, issued as one batch call (mmvq_q4k_batch /
+    mmvq_q5k_batch: one launch per lanes-per-row class, here two) and as
+    three single calls; sets of weights rotated over HBM copies.  Per step:
+    device time, weight GB/s, and the plain streaming read of the same
+    bytes in one launch."""
+    per = {"q4k": 144, "q5k": 176}[kind]
+    g = synth.rng(31 + per)
+    ws = [torch.from_numpy(synth.blocks(kind, g, r, k)).to(dev) for r in shapes]
+    sbytes = sum(weight_bytes(r, k, per) for r in shapes)
+    nc = max(2, math.ceil(2 * MALL_BYTES / sbytes) + 1)
+    sets = [ws] + [[w.clone() for w in ws] for _ in range(nc - 1)]
+    x = torch.from_numpy(synth.activations(g, max(ncols_list), k)).to(dev)
+    q = torch.empty(max(ncols_list) * (k // 32) * 36, dtype=torch.uint8, device=dev)
+    outs = [torch.empty(max(ncols_list) * r, dtype=torch.float32, device=dev) for r in shapes]
+    bfn = qmv.mmvq_q4k_batch if kind == "q4k" else qmv.mmvq_q5k_batch
+    sfn = qmv.mmvq_q4k if kind == "q4k" else qmv.mmvq_q5k
+    res = {"weight_bytes_per_step": sbytes}
+    for n in ncols_list:
+        qmv.quantize_q8_1(x, q, k, n)
+        jobs = [[(w, q, o, r, n) for w, o, r in zip(st, outs, shapes)] for st in sets]
+        calls = [lambda jb=jb: bfn(jb, k) for jb in jobs] * max(1, 40 // len(jobs))
+        bus = graph_avg_us(torch, calls, reps=4)
+        calls = [lambda jb=jb: [sfn(w, q_, o, r, k, n_) for w, q_, o, r, n_ in jb] for jb in jobs]
+        calls = calls * max(1, 40 // len(jobs))
+        sus = graph_avg_us(torch, calls, reps=4)
+        res[str(n)] = {"batch_us": round(bus, 3), "batch_weight_GBps": round(sbytes / (bus * 1e-6) / 1e9, 1),
+                       "three_singles_us": round(sus, 3),
+                       "three_singles_weight_GBps": round(sbytes / (sus * 1e-6) / 1e9, 1)}
+    big = [torch.cat([w.view(-1) for w in st]) for st in sets[:nc]]
+    sink = torch.empty(4096, dtype=torch.int32, device=dev)
+    rb = sbytes // 4096 * 4096
+    us = graph_avg_us(torch, [lambda c=c: qmv.qmv_stream_read(c, rb, sink, 0) for c in big] * 2)
+    res["stream_read_same_bytes"] = {"avg_launch_us": round(us, 3), "read_GBps": round(rb / (us * 1e-6) / 1e9, 1)}
+    del sets, big
+    torch.cuda.empty_cache()
+    return res
 
 
 def prefill_case(torch, qmv, synth, dev, rows, k, ncols_list=(16, 64, 128, 512)):

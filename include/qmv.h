@@ -224,6 +224,19 @@ int mmvq_q4k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
 int mmvq_q5k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
              int ncols, void *stream);
 
+/* Several independent Q4_K (Q5_K) products of the same K issued together,
+ * as mmvq_q6k_batch does for Q6_K (a decode step's products of one layer,
+ * PR #2207 "Summary"): jobs is a host array of njobs (1 <= njobs <= 8)
+ * descriptions, read during the call, each checked as mmvq_q4k (mmvq_q5k)
+ * checks its arguments, and the sum of the jobs' rows within the product
+ * limit.  Jobs whose matrices take the same number of lanes per row (a
+ * function of rows and K) share one launch, so a batch costs one launch per
+ * such class.  Every job's output is bit for bit what mmvq_q4k (mmvq_q5k)
+ * gives for it alone.  Outputs of different jobs must not overlap each
+ * other or any input. */
+int mmvq_q4k_batch(const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream);
+int mmvq_q5k_batch(const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream);
+
 /* Load-time conversion of a GGUF Q6_K matrix into the planar layout above
  * (PR #2340 "What it changes").  Out of place; src (2-byte aligned) and dst
  * (16-byte aligned) are rows*K/256*210 bytes and must not overlap.  The

@@ -153,6 +153,23 @@ int run_moe(const void *w_gate, const void *w_up, const void *w_down, int down_l
     return from_hip(qmv::launch_moe(m, down_layout, as_stream(stream)));
 }
 
+int q45_batch(bool five, const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream) {
+    if (!jobs || njobs < 1) return QMV_ERR_INVALID_ARG;
+    if (njobs > 8) return QMV_ERR_UNSUPPORTED;
+    qmv::TiledJobDesc d[8];
+    int64_t total_rows = 0;
+    for (int j = 0; j < njobs; j++) {
+        const qmv_q6k_job &jb = jobs[j];
+        const int rc = check_mmvq(jb.w, jb.xq, jb.out, jb.rows, K, jb.ncols, five ? 176 : 144, 16);
+        if (rc) return rc;
+        total_rows += jb.rows;
+        d[j] = {jb.w, jb.xq, jb.out, jb.rows, jb.ncols};
+    }
+    if (total_rows > kMaxProductRows) return QMV_ERR_UNSUPPORTED;
+    hipError_t e = five ? qmv::launch_mmvq_q5_jobs(d, njobs, K, as_stream(stream))
+                        : qmv::launch_mmvq_q4_jobs(d, njobs, K, as_stream(stream));
+    return from_hip(e);
+}
 }  // namespace
 
 extern "C" {
@@ -236,6 +253,14 @@ int mmvq_q4k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
 int mmvq_q5k(const void *w, const void *xq, float *out, int64_t rows, int64_t K, int ncols, void *stream) {
     if (!out) return QMV_ERR_INVALID_ARG;
     return q45_dispatch(true, w, xq, out, nullptr, rows, K, ncols, stream);
+}
+
+int mmvq_q4k_batch(const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream) {
+    return q45_batch(false, jobs, njobs, K, stream);
+}
+
+int mmvq_q5k_batch(const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream) {
+    return q45_batch(true, jobs, njobs, K, stream);
 }
 
 int mmvq_q6k_isums(const void *w, int layout, const void *xq, int32_t *isums, int64_t rows, int64_t K,

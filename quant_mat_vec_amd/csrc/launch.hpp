@@ -33,7 +33,8 @@ hipError_t launch_mmvq_q6_planar(const void *w, const void *xq, float *out, int3
 // xp: activations in the column-planar Q8_1 layout
 hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32_t *dump,
                                 int64_t rows, int64_t K, int ncols, bool xp, hipStream_t s);
-// independent products of the same K in one launch (checked by the caller)
+// independent products of the same K in one launch (checked by the caller);
+// also the Q4_K/Q5_K batches (GGUF weights, at most kMaxDenseJobs jobs)
 struct TiledJobDesc {
     const void *w;
     const void *xq;
@@ -66,6 +67,8 @@ hipError_t launch_mmvq_q4(const void *w, const void *xq, float *out, int32_t *du
                           int64_t rows, int64_t K, int ncols, hipStream_t s);
 hipError_t launch_mmvq_q5(const void *w, const void *xq, float *out, int32_t *dump,
                           int64_t rows, int64_t K, int ncols, hipStream_t s);
+hipError_t launch_mmvq_q4_jobs(const TiledJobDesc *jobs, int njobs, int64_t K, hipStream_t s);
+hipError_t launch_mmvq_q5_jobs(const TiledJobDesc *jobs, int njobs, int64_t K, hipStream_t s);
 
 struct MoeArgs {
     const uint8_t *w_gate, *w_up, *w_down;

@@ -153,9 +153,9 @@ hipError_t launch_dense_u(const void *w, const void *xq, float *out, int32_t *du
 
 constexpr int64_t kDenseFillWaves = 256;
 
-template <class F, bool DUMP>
-hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
-                        int ncols, hipStream_t s) {
+// Lanes per row of the dense kernel for a rows x K matrix.
+template <class F>
+int dense_lanes(int64_t rows, int64_t K) {
     const int units = (int)(K / 32 / F::SBPU);
     // Q4_K/Q5_K (a unit is a 32-byte pair of sub-blocks): the most lanes per
     // row that leave each lane at least two units, the last chunk ragged if
@@ -172,13 +172,168 @@ hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump
     // count, so every column's sum is the same at any N.
     if (F::SBPU == 2)
         while (u < 64 && rows * u / kWave < kDenseFillWaves && units >= 2 * u) u *= 2;
-    switch (u) {
+    return u;
+}
+
+template <class F, bool DUMP>
+hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump, int64_t rows, int64_t K,
+                        int ncols, hipStream_t s) {
+    switch (dense_lanes<F>(rows, K)) {
     case 8: return launch_dense_u<F, 8, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     case 16: return launch_dense_u<F, 16, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     case 32: return launch_dense_u<F, 32, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     case 64: return launch_dense_u<F, 64, DUMP>(w, xq, out, dump, rows, K, ncols, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+// ------------------------------------------------- several products, one launch
+// Jobs of one K (at most kMaxDenseJobs), each with its own weights,
+// activation columns, outputs and 1-8 columns.  The jobs' lanes per row and
+// register depth are those of their single launches (the launcher groups the
+// jobs by them), and a row's sum depends on nothing else -- not on the waves
+// per workgroup nor on the column count -- so every job's outputs are the
+// bits of its own product.  Workgroups of kDenseWaves waves; workgroup b
+// belongs to the last job whose first workgroup is at or before b.
+constexpr int kMaxDenseJobs = 8;
+struct DenseJob {
+    const void *w;
+    const uint8_t *xq;
+    float *out;
+    int64_t rows;
+    int32_t ncols, wg0;
+};
+struct DenseJobs {
+    int64_t K;
+    int32_t njobs;
+    DenseJob job[kMaxDenseJobs];
+};
+
+template <class F, int N, int U, int IT>
+__device__ __forceinline__ void dense_job_rows(const F &fmt, const MmvqArgs &a, int64_t row0, void *lds,
+                                               float *out) {
+    float acc[1][N];
+    mmvq_rows<F, N, U, 1, kDenseWaves * kWave, false, IT>(fmt, a, row0, lds, acc);
+    const int u = (threadIdx.x & (kWave - 1)) % U;
+    const int64_t row = lane_row<U, 1>(row0, 0);
+    float v = acc[0][0];
+#pragma unroll
+    for (int n = 1; n < N; n++) v = u == n ? acc[0][n] : v;
+    if (row < a.rows && u < N && u < a.nout) out[(int64_t)u * a.rows + row] = v;
+}
+
+template <class F, int U, int IT, int NMAX>
+__global__ __launch_bounds__(kDenseWaves *kWave) void k_mmvq_dense_jobs(const DenseJobs js) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int b = blockIdx.x;
+    // the job and its fields by selects over the (scalar) kernel arguments
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxDenseJobs; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
+    DenseJob jb = js.job[0];
+#pragma unroll
+    for (int i = 1; i < kMaxDenseJobs; i++)
+        if (j == i) jb = js.job[i];
+    F fmt;
+    fmt.init(jb.w, jb.rows, js.K);
+    MmvqArgs a;
+    a.xq = jb.xq;
+    a.dump = nullptr;
+    a.rows = jb.rows;
+    a.K = js.K;
+    a.colpack = 0;
+#pragma unroll
+    for (int n = 0; n < 8; n++) a.colpack |= (uint64_t)(n < jb.ncols ? n : jb.ncols - 1) << (8 * n);
+    a.nout = jb.ncols;
+    a.xstride = js.K / 32;
+    a.its = IT;
+    const int64_t row0 = (int64_t)(b - jb.wg0) * kDenseWaves * kRowsPerWave<U, 1>;
+    // six and seven columns run as eight (the missing columns read the last
+    // real one again and are not stored), as their single launches do
+    switch (jb.ncols) {
+    case 1: dense_job_rows<F, 1, U, IT>(fmt, a, row0, lds, jb.out); break;
+    case 2: if constexpr (NMAX >= 2) dense_job_rows<F, 2, U, IT>(fmt, a, row0, lds, jb.out); break;
+    case 3: if constexpr (NMAX >= 4) dense_job_rows<F, 3, U, IT>(fmt, a, row0, lds, jb.out); break;
+    case 4: if constexpr (NMAX >= 4) dense_job_rows<F, 4, U, IT>(fmt, a, row0, lds, jb.out); break;
+    case 5: if constexpr (NMAX >= 8) dense_job_rows<F, 5, U, IT>(fmt, a, row0, lds, jb.out); break;
+    default: if constexpr (NMAX >= 8) dense_job_rows<F, 8, U, IT>(fmt, a, row0, lds, jb.out); break;
+    }
+}
+
+template <class F, int U, int IT, int NMAX>
+constexpr size_t dense_jobs_lds() {
+    size_t m = 0;
+    for (int n = 1; n <= NMAX; n++) {
+        const size_t b = (size_t)n * its_for(IT, n, U, F::SBPU, kDenseWaves * kWave) * U * F::SBPU *
+                         kActBytesPerBlock;
+        m = b > m ? b : m;
+    }
+    return m;
+}
+
+template <class F, int U, int IT, int NMAX>
+hipError_t launch_dense_jobs_cfg(DenseJobs js, hipStream_t s) {
+    int64_t wg = 0;
+    for (int j = 0; j < js.njobs; j++) {
+        js.job[j].wg0 = (int32_t)wg;
+        wg += (js.job[j].rows + kDenseWaves * kRowsPerWave<U, 1> - 1) / (kDenseWaves * kRowsPerWave<U, 1>);
+    }
+    for (int j = js.njobs; j < kMaxDenseJobs; j++) js.job[j] = js.job[0];
+    if (wg * kDenseWaves * kWave > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
+    constexpr size_t lds = dense_jobs_lds<F, U, IT, NMAX>();
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_dense_jobs<F, U, IT, NMAX>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mmvq_dense_jobs<F, U, IT, NMAX>), dim3((unsigned)wg), dim3(kDenseWaves * kWave), lds, s,
+                       js);
+    return hipGetLastError();
+}
+
+template <class F, int U, int IT>
+hipError_t launch_dense_jobs_it(const DenseJobs &js, int maxcols, hipStream_t s) {
+    if (maxcols <= 1) return launch_dense_jobs_cfg<F, U, IT, 1>(js, s);
+    if (maxcols <= 2) return launch_dense_jobs_cfg<F, U, IT, 2>(js, s);
+    if (maxcols <= 4) return launch_dense_jobs_cfg<F, U, IT, 4>(js, s);
+    return launch_dense_jobs_cfg<F, U, IT, 8>(js, s);
+}
+
+template <class F, int U>
+hipError_t launch_dense_jobs_u(const DenseJobs &js, int it, int maxcols, hipStream_t s) {
+    if constexpr (F::IT > 3) {
+        if (it == 3) return launch_dense_jobs_it<F, U, 3>(js, maxcols, s);
+    }
+    return launch_dense_jobs_it<F, U, F::IT>(js, maxcols, s);
+}
+
+// The jobs (the caller has checked each), grouped by lanes per row and
+// register depth in their given order, one launch per group.
+template <class F>
+hipError_t launch_dense_jobs(const DenseJob *jobs, int njobs, int64_t K, hipStream_t s) {
+    bool done[kMaxDenseJobs] = {};
+    for (int j0 = 0; j0 < njobs; j0++) {
+        if (done[j0]) continue;
+        const int u = dense_lanes<F>(jobs[j0].rows, K);
+        const int units = (int)(K / 32 / F::SBPU);
+        const int it = F::IT > 3 && depth_for(units, u, F::IT) == 3 ? 3 : F::IT;
+        DenseJobs js;
+        js.njobs = 0;
+        js.K = K;
+        int maxcols = 1;
+        for (int j = j0; j < njobs; j++) {
+            if (done[j] || dense_lanes<F>(jobs[j].rows, K) != u) continue;
+            done[j] = true;
+            js.job[js.njobs++] = jobs[j];
+            maxcols = jobs[j].ncols > maxcols ? jobs[j].ncols : maxcols;
+        }
+        hipError_t e;
+        switch (u) {
+        case 8: e = launch_dense_jobs_u<F, 8>(js, it, maxcols, s); break;
+        case 16: e = launch_dense_jobs_u<F, 16>(js, it, maxcols, s); break;
+        case 32: e = launch_dense_jobs_u<F, 32>(js, it, maxcols, s); break;
+        default: e = launch_dense_jobs_u<F, 64>(js, it, maxcols, s); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <class F>

@@ -6,4 +6,10 @@ hipError_t launch_mmvq_q4(const void *w, const void *xq, float *out, int32_t *du
                             int64_t K, int ncols, hipStream_t s) {
     return launch_dense_any<Q45<false>>(w, xq, out, dump, rows, K, ncols, s);
 }
+hipError_t launch_mmvq_q4_jobs(const TiledJobDesc *jobs, int njobs, int64_t K, hipStream_t s) {
+    DenseJob d[kMaxDenseJobs];
+    for (int j = 0; j < njobs; j++)
+        d[j] = {jobs[j].w, reinterpret_cast<const uint8_t *>(jobs[j].xq), jobs[j].out, jobs[j].rows, jobs[j].ncols, 0};
+    return launch_dense_jobs<Q45<false>>(d, njobs, K, s);
+}
 }  // namespace qmv

@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
             fn.restype = I
         L.mmvq_q6k_batch.argtypes = [ctypes.POINTER(Q6kJob), I, I, I64, P]
         L.mmvq_q6k_batch.restype = I
+        for name in ("mmvq_q4k_batch", "mmvq_q5k_batch"):
+            getattr(L, name).argtypes = [ctypes.POINTER(Q6kJob), I, I64, P]
+            getattr(L, name).restype = I
         L.grouped_expert_mmvq_workspace.argtypes = [I, I, I, I64, I64]
         L.mmvq_q6k_topk_workspace.restype = SZ
         L.mmvq_q6k_topk_workspace.argtypes = [I64, I, I]
@@ -216,8 +219,21 @@ def mmvq_q5k_isums(w, xq, isums, rows: int, K: int, ncols: int, stream=None) -> 
 
 def mmvq_q6k_batch(jobs, layout: int, K: int, stream=None) -> None:
     """jobs: sequence of (w, xq, out, rows, ncols) -- one launch for all."""
-    arr = (Q6kJob * max(1, len(jobs)))(*[Q6kJob(_ptr(w), _ptr(x), _ptr(o), rows, n) for w, x, o, rows, n in jobs])
-    _check(lib().mmvq_q6k_batch(arr, len(jobs), layout, K, _stream(stream)), "mmvq_q6k_batch")
+    _check(lib().mmvq_q6k_batch(_jobs(jobs), len(jobs), layout, K, _stream(stream)), "mmvq_q6k_batch")
+
+
+def _jobs(jobs):
+    return (Q6kJob * max(1, len(jobs)))(*[Q6kJob(_ptr(w), _ptr(x), _ptr(o), rows, n) for w, x, o, rows, n in jobs])
+
+
+def mmvq_q4k_batch(jobs, K: int, stream=None) -> None:
+    """jobs: sequence of (w, xq, out, rows, ncols) of Q4_K products."""
+    _check(lib().mmvq_q4k_batch(_jobs(jobs), len(jobs), K, _stream(stream)), "mmvq_q4k_batch")
+
+
+def mmvq_q5k_batch(jobs, K: int, stream=None) -> None:
+    """jobs: sequence of (w, xq, out, rows, ncols) of Q5_K products."""
+    _check(lib().mmvq_q5k_batch(_jobs(jobs), len(jobs), K, _stream(stream)), "mmvq_q5k_batch")
 
 
 def grouped_expert_mmvq_workspace(E: int, T: int, topk: int, d_model: int, d_ff: int) -> int:

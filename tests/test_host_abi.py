@@ -28,7 +28,7 @@ def test_exports_every_declared_symbol(L):
                 "mmvq_q6k_isums",
                 "mmvq_q4k_isums", "mmvq_q5k_isums",
                 "grouped_expert_mmvq", "grouped_expert_mmvq_workspace", "grouped_expert_mmvq_noalloc",
-                "mmvq_q6k_batch", "mmvq_q6k_topk", "mmvq_q6k_topk_workspace", "qmv_strerror",
+                "mmvq_q6k_batch", "mmvq_q4k_batch", "mmvq_q5k_batch", "mmvq_q6k_topk", "mmvq_q6k_topk_workspace", "qmv_strerror",
                 "qmv_last_hip_error", "qmv_stream_read"}
     assert expected <= set(names), set(names) ^ expected
     for n in names:
@@ -281,6 +281,28 @@ def test_batch_rejects(L):
     assert call([ok, (P, P, P, 0, 2)]) == E_INV and call([ok, (None, P, P, 16, 2)]) == E_INV
     assert call([ok, (P + 8, P, P, 16, 2)]) == E_ALN and call([ok, (P, P, P + 2, 16, 2)]) == E_ALN
     assert call([ok, (P, P + 4, P, 16, 2)], layout=XT) == E_ALN
+    half = (1 << 25)
+    assert call([(P, P, P, half, 1), (P, P, P, half, 1)]) == E_UNS      # rows summed past the product limit
+
+
+@pytest.mark.parametrize("name", ["mmvq_q4k_batch", "mmvq_q5k_batch"])
+def test_q45_batch_rejects(L, name):
+    f = getattr(L, name)
+
+    def call(jobs, K=512, n=None):
+        arr = (qmv.Q6kJob * max(1, len(jobs)))(*[qmv.Q6kJob(*j) for j in jobs])
+        return f(arr, len(jobs) if n is None else n, K, None)
+
+    ok = (P, P, P, 16, 2)
+    assert f(None, 1, 512, None) == E_INV
+    assert call([ok], n=0) == E_INV and call([ok], n=-1) == E_INV
+    assert call([ok] * 9) == E_UNS
+    assert call([ok], K=300) == E_UNS and call([ok], K=1 << 21) == E_UNS and call([ok], K=0) == E_INV
+    assert call([ok, (P, P, P, 16, 9)]) == E_UNS and call([ok, (P, P, P, 16, 0)]) == E_UNS
+    assert call([ok, (P, P, P, 0, 2)]) == E_INV and call([ok, (None, P, P, 16, 2)]) == E_INV
+    assert call([ok, (P, None, P, 16, 2)]) == E_INV and call([ok, (P, P, None, 16, 2)]) == E_INV
+    assert call([ok, (P + 8, P, P, 16, 2)]) == E_ALN            # weights 16-byte aligned
+    assert call([ok, (P, P + 2, P, 16, 2)]) == E_ALN and call([ok, (P, P, P + 2, 16, 2)]) == E_ALN
     half = (1 << 25)
     assert call([(P, P, P, half, 1), (P, P, P, half, 1)]) == E_UNS      # rows summed past the product limit
 
