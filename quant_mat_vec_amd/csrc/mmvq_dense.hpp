@@ -203,10 +203,13 @@ struct DenseJob {
     int64_t rows;
     int32_t ncols, wg0;
 };
+// (MJ entries, the count and K first: the table's size, which every wave
+// reads, is kept small, as for the tiled Q6_K batches)
+template <int MJ>
 struct DenseJobs {
     int64_t K;
     int32_t njobs;
-    DenseJob job[kMaxDenseJobs];
+    DenseJob job[MJ];
 };
 
 template <class F, int N, int U, int IT>
@@ -222,17 +225,17 @@ __device__ __forceinline__ void dense_job_rows(const F &fmt, const MmvqArgs &a, 
     if (row < a.rows && u < N && u < a.nout) out[(int64_t)u * a.rows + row] = v;
 }
 
-template <class F, int U, int IT, int NMAX>
-__global__ __launch_bounds__(kDenseWaves *kWave) void k_mmvq_dense_jobs(const DenseJobs js) {
+template <class F, int U, int IT, int NMAX, int MJ>
+__global__ __launch_bounds__(kDenseWaves *kWave) void k_mmvq_dense_jobs(const DenseJobs<MJ> js) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int b = blockIdx.x;
     // the job and its fields by selects over the (scalar) kernel arguments
     int j = 0;
 #pragma unroll
-    for (int i = 1; i < kMaxDenseJobs; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
+    for (int i = 1; i < MJ; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
     DenseJob jb = js.job[0];
 #pragma unroll
-    for (int i = 1; i < kMaxDenseJobs; i++)
+    for (int i = 1; i < MJ; i++)
         if (j == i) jb = js.job[i];
     F fmt;
     fmt.init(jb.w, jb.rows, js.K);
@@ -271,25 +274,35 @@ constexpr size_t dense_jobs_lds() {
     return m;
 }
 
-template <class F, int U, int IT, int NMAX>
-hipError_t launch_dense_jobs_cfg(DenseJobs js, hipStream_t s) {
+template <class F, int U, int IT, int NMAX, int MJ>
+hipError_t launch_dense_jobs_mj(const DenseJobs<kMaxDenseJobs> &all, hipStream_t s) {
+    DenseJobs<MJ> js;
+    js.K = all.K;
+    js.njobs = all.njobs;
     int64_t wg = 0;
     for (int j = 0; j < js.njobs; j++) {
+        js.job[j] = all.job[j];
         js.job[j].wg0 = (int32_t)wg;
         wg += (js.job[j].rows + kDenseWaves * kRowsPerWave<U, 1> - 1) / (kDenseWaves * kRowsPerWave<U, 1>);
     }
-    for (int j = js.njobs; j < kMaxDenseJobs; j++) js.job[j] = js.job[0];
+    for (int j = js.njobs; j < MJ; j++) js.job[j] = js.job[0];
     if (wg * kDenseWaves * kWave > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     constexpr size_t lds = dense_jobs_lds<F, U, IT, NMAX>();
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_dense_jobs<F, U, IT, NMAX>), lds);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_dense_jobs<F, U, IT, NMAX, MJ>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mmvq_dense_jobs<F, U, IT, NMAX>), dim3((unsigned)wg), dim3(kDenseWaves * kWave), lds, s,
-                       js);
+    hipLaunchKernelGGL((k_mmvq_dense_jobs<F, U, IT, NMAX, MJ>), dim3((unsigned)wg), dim3(kDenseWaves * kWave), lds,
+                       s, js);
     return hipGetLastError();
 }
 
+template <class F, int U, int IT, int NMAX>
+hipError_t launch_dense_jobs_cfg(const DenseJobs<kMaxDenseJobs> &js, hipStream_t s) {
+    if (js.njobs <= 4) return launch_dense_jobs_mj<F, U, IT, NMAX, 4>(js, s);
+    return launch_dense_jobs_mj<F, U, IT, NMAX, kMaxDenseJobs>(js, s);
+}
+
 template <class F, int U, int IT>
-hipError_t launch_dense_jobs_it(const DenseJobs &js, int maxcols, hipStream_t s) {
+hipError_t launch_dense_jobs_it(const DenseJobs<kMaxDenseJobs> &js, int maxcols, hipStream_t s) {
     if (maxcols <= 1) return launch_dense_jobs_cfg<F, U, IT, 1>(js, s);
     if (maxcols <= 2) return launch_dense_jobs_cfg<F, U, IT, 2>(js, s);
     if (maxcols <= 4) return launch_dense_jobs_cfg<F, U, IT, 4>(js, s);
@@ -297,7 +310,7 @@ hipError_t launch_dense_jobs_it(const DenseJobs &js, int maxcols, hipStream_t s)
 }
 
 template <class F, int U>
-hipError_t launch_dense_jobs_u(const DenseJobs &js, int it, int maxcols, hipStream_t s) {
+hipError_t launch_dense_jobs_u(const DenseJobs<kMaxDenseJobs> &js, int it, int maxcols, hipStream_t s) {
     if constexpr (F::IT > 3) {
         if (it == 3) return launch_dense_jobs_it<F, U, 3>(js, maxcols, s);
     }
@@ -308,13 +321,14 @@ hipError_t launch_dense_jobs_u(const DenseJobs &js, int it, int maxcols, hipStre
 // register depth in their given order, one launch per group.
 template <class F>
 hipError_t launch_dense_jobs(const DenseJob *jobs, int njobs, int64_t K, hipStream_t s) {
+    if (njobs < 1 || njobs > kMaxDenseJobs) return hipErrorInvalidValue;
     bool done[kMaxDenseJobs] = {};
     for (int j0 = 0; j0 < njobs; j0++) {
         if (done[j0]) continue;
         const int u = dense_lanes<F>(jobs[j0].rows, K);
         const int units = (int)(K / 32 / F::SBPU);
         const int it = F::IT > 3 && depth_for(units, u, F::IT) == 3 ? 3 : F::IT;
-        DenseJobs js;
+        DenseJobs<kMaxDenseJobs> js;
         js.njobs = 0;
         js.K = K;
         int maxcols = 1;

@@ -29,7 +29,8 @@ hipError_t launch_mmvq_q6_tiled(const void *w, const void *xq, float *out, int32
 }
 
 hipError_t launch_mmvq_q6_tiled_jobs(const TiledJobDesc *jobs, int njobs, int64_t K, bool xp, hipStream_t s) {
-    TiledJobs js;
+    if (njobs < 1 || njobs > kMaxTiledJobs) return hipErrorInvalidValue;
+    TiledJobs<kMaxTiledJobs> js;
     js.njobs = njobs;
     js.K = K;
     for (int j = 0; j < njobs; j++) {

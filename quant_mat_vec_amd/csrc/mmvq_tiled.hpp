@@ -573,6 +573,13 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
 // wg0[j] .. wg0[j+1]-1, each one row workgroup of that job's product, with
 // the same waves along K and so the same bits as the job launched alone.
 // One launch ramps up and drains once for all of them.
+// Every wave reads the job table from the kernel arguments before its first
+// weight load, so the table is kept small: MJ (4 or 8) entries, the count
+// and K first.  Three 10240x2560 products (8, 4, 1 columns) measured 13.09
+// us per launch with eight entries followed by the count and K, 12.89 with
+// the count and K first, 12.75 with four entries.  (Loading every entry at
+// once and selecting by value, one round of argument loads instead of two,
+// measured 12.87.)
 constexpr int kMaxTiledJobs = 8;
 struct TiledJob {
     const void *w;
@@ -581,14 +588,15 @@ struct TiledJob {
     int64_t rows;
     int32_t ncols, wg0;
 };
+template <int MJ>
 struct TiledJobs {
-    TiledJob job[kMaxTiledJobs];
-    int32_t njobs;
     int64_t K;
+    int32_t njobs;
+    TiledJob job[MJ];
 };
 
-template <int KS, int RTW, int IT, bool XP>
-__global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const TiledJobs js) {
+template <int KS, int RTW, int IT, bool XP, int MJ>
+__global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const TiledJobs<MJ> js) {
     extern __shared__ __align__(16) uint8_t lds[];
     const int b = blockIdx.x;
     // this workgroup's job, and its fields, by selects over the (scalar)
@@ -597,10 +605,10 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const T
     // three 10240x2560 products than each job's in one consecutive range.)
     int j = 0;
 #pragma unroll
-    for (int i = 1; i < kMaxTiledJobs; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
+    for (int i = 1; i < MJ; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
     TiledJob jb = js.job[0];
 #pragma unroll
-    for (int i = 1; i < kMaxTiledJobs; i++)
+    for (int i = 1; i < MJ; i++)
         if (j == i) jb = js.job[i];
     MmvqArgs a;
     a.xq = jb.xq;
@@ -724,27 +732,37 @@ constexpr size_t tiled_jobs_lds() {
     return m;
 }
 
-// Jobs (at most kMaxTiledJobs, same K) in one launch; the caller has checked
-// every job.  Workgroup ranges in the given job order.
-template <int KS, int RTW, int IT, bool XP>
-hipError_t launch_tiled_jobs_cfg(TiledJobs js, hipStream_t s) {
+// Jobs (at most MJ, same K) in one launch; the caller has checked every job.
+// Workgroup ranges in the given job order.
+template <int KS, int RTW, int IT, bool XP, int MJ>
+hipError_t launch_tiled_jobs_mj(const TiledJobs<kMaxTiledJobs> &all, hipStream_t s) {
     constexpr int NTHR = KS * RTW * kWave;
+    TiledJobs<MJ> js;
+    js.K = all.K;
+    js.njobs = all.njobs;
     int64_t wg = 0;
     for (int j = 0; j < js.njobs; j++) {
+        js.job[j] = all.job[j];
         js.job[j].wg0 = (int32_t)wg;
         wg += ((js.job[j].rows + 15) / 16 + RTW - 1) / RTW;
     }
-    for (int j = js.njobs; j < kMaxTiledJobs; j++) js.job[j] = js.job[0];
+    for (int j = js.njobs; j < MJ; j++) js.job[j] = js.job[0];
     if (wg * NTHR > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
     constexpr size_t lds = tiled_jobs_lds<KS, RTW, IT, XP>();
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled_jobs<KS, RTW, IT, XP>), lds);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled_jobs<KS, RTW, IT, XP, MJ>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mmvq_q6_tiled_jobs<KS, RTW, IT, XP>), dim3((unsigned)wg), dim3(NTHR), lds, s, js);
+    hipLaunchKernelGGL((k_mmvq_q6_tiled_jobs<KS, RTW, IT, XP, MJ>), dim3((unsigned)wg), dim3(NTHR), lds, s, js);
     return hipGetLastError();
 }
 
+template <int KS, int RTW, int IT, bool XP>
+hipError_t launch_tiled_jobs_cfg(const TiledJobs<kMaxTiledJobs> &js, hipStream_t s) {
+    if (js.njobs <= 4) return launch_tiled_jobs_mj<KS, RTW, IT, XP, 4>(js, s);
+    return launch_tiled_jobs_mj<KS, RTW, IT, XP, kMaxTiledJobs>(js, s);
+}
+
 template <bool XP>
-hipError_t launch_tiled_jobs(const TiledJobs &js, hipStream_t s) {
+hipError_t launch_tiled_jobs(const TiledJobs<kMaxTiledJobs> &js, hipStream_t s) {
     const int64_t need = (js.K / 128 + 4) / 5;
     if (need <= 1) return launch_tiled_jobs_cfg<1, 4, 5, XP>(js, s);
     if (need <= 2) return launch_tiled_jobs_cfg<2, 2, 5, XP>(js, s);
