@@ -229,10 +229,10 @@ int mmvq_q5k(const void *w, const void *xq, float *out, int64_t rows, int64_t K,
  * PR #2207 "Summary"): jobs is a host array of njobs (1 <= njobs <= 8)
  * descriptions, read during the call, each checked as mmvq_q4k (mmvq_q5k)
  * checks its arguments, and the sum of the jobs' rows within the product
- * limit.  Jobs whose matrices take the same number of lanes per row (a
- * function of rows and K) share one launch, so a batch costs one launch per
- * such class.  Every job's output is bit for bit what mmvq_q4k (mmvq_q5k)
- * gives for it alone.  Outputs of different jobs must not overlap each
+ * limit.  Up to four jobs run in one launch; more run in one launch per
+ * lanes-per-row class (a function of rows and K; one K gives at most two).
+ * Every job's output is bit for bit what mmvq_q4k (mmvq_q5k) gives for it
+ * alone.  Outputs of different jobs must not overlap each
  * other or any input. */
 int mmvq_q4k_batch(const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream);
 int mmvq_q5k_batch(const qmv_q6k_job *jobs, int njobs, int64_t K, void *stream);

@@ -189,19 +189,26 @@ hipError_t launch_dense(const void *w, const void *xq, float *out, int32_t *dump
 
 // ------------------------------------------------- several products, one launch
 // Jobs of one K (at most kMaxDenseJobs), each with its own weights,
-// activation columns, outputs and 1-8 columns.  The jobs' lanes per row and
-// register depth are those of their single launches (the launcher groups the
-// jobs by them), and a row's sum depends on nothing else -- not on the waves
-// per workgroup nor on the column count -- so every job's outputs are the
-// bits of its own product.  Workgroups of kDenseWaves waves; workgroup b
-// belongs to the last job whose first workgroup is at or before b.
+// activation columns, outputs and 1-8 columns.  Every job runs with the
+// lanes per row and register depth of its single launch, and a row's sum
+// depends on nothing else -- not on the waves per workgroup nor on the
+// column count -- so every job's outputs are the bits of its own product.
+// Within one K the lanes per row take at most two values, the base width and
+// twice it for matrices too short to fill the chip (dense_lanes: doubling
+// needs at least twice as many units as lanes, which the base width already
+// rules out for a second doubling); a launch serves one width (U2 = 0) or
+// both (U2 = 2U, the "wide" jobs), so a batch of up to four jobs is one
+// launch whatever its matrices' heights.  A second launch for a short matrix
+// cost about as much as that matrix alone (12288, 6144 and 512 x 2560 Q4_K at
+// one column: 7.4 us for the first two in one launch, 10.3 with the third in
+// a launch of its own).  Workgroups of kDenseWaves waves; workgroup b belongs
+// to the last job whose first workgroup is at or before b.
 constexpr int kMaxDenseJobs = 8;
 struct DenseJob {
     const void *w;
     const uint8_t *xq;
     float *out;
-    int64_t rows;
-    int32_t ncols, wg0;
+    int32_t rows, ncols, wg0, wide;
 };
 // (MJ entries, the count and K first: the table's size, which every wave
 // reads, is kept small, as for the tiled Q6_K batches)
@@ -225,30 +232,21 @@ __device__ __forceinline__ void dense_job_rows(const F &fmt, const MmvqArgs &a, 
     if (row < a.rows && u < N && u < a.nout) out[(int64_t)u * a.rows + row] = v;
 }
 
-template <class F, int U, int IT, int NMAX, int MJ>
-__global__ __launch_bounds__(kDenseWaves *kWave) void k_mmvq_dense_jobs(const DenseJobs<MJ> js) {
-    extern __shared__ __align__(16) uint8_t lds[];
-    const int b = blockIdx.x;
-    // the job and its fields by selects over the (scalar) kernel arguments
-    int j = 0;
-#pragma unroll
-    for (int i = 1; i < MJ; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
-    DenseJob jb = js.job[0];
-#pragma unroll
-    for (int i = 1; i < MJ; i++)
-        if (j == i) jb = js.job[i];
+// Workgroup b's rows of job jb at U lanes per row and depth IT.
+template <class F, int U, int IT, int NMAX>
+__device__ __forceinline__ void dense_job(const DenseJob &jb, int64_t K, int b, void *lds) {
     F fmt;
-    fmt.init(jb.w, jb.rows, js.K);
+    fmt.init(jb.w, jb.rows, K);
     MmvqArgs a;
     a.xq = jb.xq;
     a.dump = nullptr;
     a.rows = jb.rows;
-    a.K = js.K;
+    a.K = K;
     a.colpack = 0;
 #pragma unroll
     for (int n = 0; n < 8; n++) a.colpack |= (uint64_t)(n < jb.ncols ? n : jb.ncols - 1) << (8 * n);
     a.nout = jb.ncols;
-    a.xstride = js.K / 32;
+    a.xstride = K / 32;
     a.its = IT;
     const int64_t row0 = (int64_t)(b - jb.wg0) * kDenseWaves * kRowsPerWave<U, 1>;
     // six and seven columns run as eight (the missing columns read the last
@@ -263,6 +261,27 @@ __global__ __launch_bounds__(kDenseWaves *kWave) void k_mmvq_dense_jobs(const De
     }
 }
 
+template <class F, int U, int IT, int U2, int IT2, int NMAX, int MJ>
+__global__ __launch_bounds__(kDenseWaves *kWave) void k_mmvq_dense_jobs(const DenseJobs<MJ> js) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int b = blockIdx.x;
+    // the job and its fields by selects over the (scalar) kernel arguments
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < MJ; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
+    DenseJob jb = js.job[0];
+#pragma unroll
+    for (int i = 1; i < MJ; i++)
+        if (j == i) jb = js.job[i];
+    if constexpr (U2 > 0) {
+        if (jb.wide) {
+            dense_job<F, U2, IT2, NMAX>(jb, js.K, b, lds);
+            return;
+        }
+    }
+    dense_job<F, U, IT, NMAX>(jb, js.K, b, lds);
+}
+
 template <class F, int U, int IT, int NMAX>
 constexpr size_t dense_jobs_lds() {
     size_t m = 0;
@@ -274,7 +293,7 @@ constexpr size_t dense_jobs_lds() {
     return m;
 }
 
-template <class F, int U, int IT, int NMAX, int MJ>
+template <class F, int U, int IT, int U2, int IT2, int NMAX, int MJ>
 hipError_t launch_dense_jobs_mj(const DenseJobs<kMaxDenseJobs> &all, hipStream_t s) {
     DenseJobs<MJ> js;
     js.K = all.K;
@@ -283,68 +302,106 @@ hipError_t launch_dense_jobs_mj(const DenseJobs<kMaxDenseJobs> &all, hipStream_t
     for (int j = 0; j < js.njobs; j++) {
         js.job[j] = all.job[j];
         js.job[j].wg0 = (int32_t)wg;
-        wg += (js.job[j].rows + kDenseWaves * kRowsPerWave<U, 1> - 1) / (kDenseWaves * kRowsPerWave<U, 1>);
+        const int64_t rpw = kDenseWaves * (js.job[j].wide ? kWave / U2 : kWave / U);
+        wg += (js.job[j].rows + rpw - 1) / rpw;
     }
     for (int j = js.njobs; j < MJ; j++) js.job[j] = js.job[0];
     if (wg * kDenseWaves * kWave > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
-    constexpr size_t lds = dense_jobs_lds<F, U, IT, NMAX>();
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_dense_jobs<F, U, IT, NMAX, MJ>), lds);
+    constexpr size_t l1 = dense_jobs_lds<F, U, IT, NMAX>();
+    constexpr size_t l2 = U2 > 0 ? dense_jobs_lds<F, (U2 > 0 ? U2 : U), IT2, NMAX>() : 0;
+    constexpr size_t lds = l1 > l2 ? l1 : l2;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_dense_jobs<F, U, IT, U2, IT2, NMAX, MJ>), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_mmvq_dense_jobs<F, U, IT, NMAX, MJ>), dim3((unsigned)wg), dim3(kDenseWaves * kWave), lds,
-                       s, js);
+    hipLaunchKernelGGL((k_mmvq_dense_jobs<F, U, IT, U2, IT2, NMAX, MJ>), dim3((unsigned)wg),
+                       dim3(kDenseWaves * kWave), lds, s, js);
     return hipGetLastError();
 }
 
-template <class F, int U, int IT, int NMAX>
+// Table size: four entries for up to four jobs, else eight (one width only).
+template <class F, int U, int IT, int U2, int IT2, int NMAX>
 hipError_t launch_dense_jobs_cfg(const DenseJobs<kMaxDenseJobs> &js, hipStream_t s) {
-    if (js.njobs <= 4) return launch_dense_jobs_mj<F, U, IT, NMAX, 4>(js, s);
-    return launch_dense_jobs_mj<F, U, IT, NMAX, kMaxDenseJobs>(js, s);
+    if (js.njobs <= 4) return launch_dense_jobs_mj<F, U, IT, U2, IT2, NMAX, 4>(js, s);
+    if constexpr (U2 == 0) return launch_dense_jobs_mj<F, U, IT, 0, 3, NMAX, kMaxDenseJobs>(js, s);
+    return hipErrorInvalidValue;
 }
 
-template <class F, int U, int IT>
+template <class F, int U, int IT, int U2, int IT2>
 hipError_t launch_dense_jobs_it(const DenseJobs<kMaxDenseJobs> &js, int maxcols, hipStream_t s) {
-    if (maxcols <= 1) return launch_dense_jobs_cfg<F, U, IT, 1>(js, s);
-    if (maxcols <= 2) return launch_dense_jobs_cfg<F, U, IT, 2>(js, s);
-    if (maxcols <= 4) return launch_dense_jobs_cfg<F, U, IT, 4>(js, s);
-    return launch_dense_jobs_cfg<F, U, IT, 8>(js, s);
+    if (maxcols <= 1) return launch_dense_jobs_cfg<F, U, IT, U2, IT2, 1>(js, s);
+    if (maxcols <= 2) return launch_dense_jobs_cfg<F, U, IT, U2, IT2, 2>(js, s);
+    if (maxcols <= 4) return launch_dense_jobs_cfg<F, U, IT, U2, IT2, 4>(js, s);
+    return launch_dense_jobs_cfg<F, U, IT, U2, IT2, 8>(js, s);
 }
 
+// One width (wide = false): it = the depth of the U-lane jobs.  Two widths
+// (wide = true): the U-lane jobs at depth it and the 2U-lane jobs at depth
+// three (they have at most two units per lane).
 template <class F, int U>
-hipError_t launch_dense_jobs_u(const DenseJobs<kMaxDenseJobs> &js, int it, int maxcols, hipStream_t s) {
-    if constexpr (F::IT > 3) {
-        if (it == 3) return launch_dense_jobs_it<F, U, 3>(js, maxcols, s);
+hipError_t launch_dense_jobs_u(const DenseJobs<kMaxDenseJobs> &js, int it, bool wide, int maxcols, hipStream_t s) {
+    if (wide) {
+        if constexpr (2 * U <= 64) {
+            if constexpr (F::IT > 3) {
+                if (it == 3) return launch_dense_jobs_it<F, U, 3, 2 * U, 3>(js, maxcols, s);
+            }
+            return launch_dense_jobs_it<F, U, F::IT, 2 * U, 3>(js, maxcols, s);
+        }
+        return hipErrorInvalidValue;
     }
-    return launch_dense_jobs_it<F, U, F::IT>(js, maxcols, s);
+    if constexpr (F::IT > 3) {
+        if (it == 3) return launch_dense_jobs_it<F, U, 3, 0, 3>(js, maxcols, s);
+    }
+    return launch_dense_jobs_it<F, U, F::IT, 0, 3>(js, maxcols, s);
 }
 
-// The jobs (the caller has checked each), grouped by lanes per row and
-// register depth in their given order, one launch per group.
+// The jobs (the caller has checked each).  Up to four jobs of one or two
+// widths: one launch.  Otherwise one launch per width, the jobs of each in
+// their given order.
 template <class F>
 hipError_t launch_dense_jobs(const DenseJob *jobs, int njobs, int64_t K, hipStream_t s) {
     if (njobs < 1 || njobs > kMaxDenseJobs) return hipErrorInvalidValue;
+    const int units = (int)(K / 32 / F::SBPU);
+    auto depth = [&](int u) { return F::IT > 3 && depth_for(units, u, F::IT) == 3 ? 3 : F::IT; };
+    int lanes[kMaxDenseJobs], umin = 64, umax = 0;
+    for (int j = 0; j < njobs; j++) {
+        lanes[j] = dense_lanes<F>(jobs[j].rows, K);
+        umin = lanes[j] < umin ? lanes[j] : umin;
+        umax = lanes[j] > umax ? lanes[j] : umax;
+    }
+    auto launch = [&](const DenseJobs<kMaxDenseJobs> &js, int u, bool wide, int maxcols) {
+        switch (u) {
+        case 8: return launch_dense_jobs_u<F, 8>(js, depth(u), wide, maxcols, s);
+        case 16: return launch_dense_jobs_u<F, 16>(js, depth(u), wide, maxcols, s);
+        case 32: return launch_dense_jobs_u<F, 32>(js, depth(u), wide, maxcols, s);
+        default: return launch_dense_jobs_u<F, 64>(js, depth(u), wide, maxcols, s);
+        }
+    };
+    if (umax == 2 * umin && njobs <= 4 && depth(umax) == 3) {
+        DenseJobs<kMaxDenseJobs> js;
+        js.njobs = njobs;
+        js.K = K;
+        int maxcols = 1;
+        for (int j = 0; j < njobs; j++) {
+            js.job[j] = jobs[j];
+            js.job[j].wide = lanes[j] == umax;
+            maxcols = jobs[j].ncols > maxcols ? jobs[j].ncols : maxcols;
+        }
+        return launch(js, umin, true, maxcols);
+    }
     bool done[kMaxDenseJobs] = {};
     for (int j0 = 0; j0 < njobs; j0++) {
         if (done[j0]) continue;
-        const int u = dense_lanes<F>(jobs[j0].rows, K);
-        const int units = (int)(K / 32 / F::SBPU);
-        const int it = F::IT > 3 && depth_for(units, u, F::IT) == 3 ? 3 : F::IT;
         DenseJobs<kMaxDenseJobs> js;
         js.njobs = 0;
         js.K = K;
         int maxcols = 1;
         for (int j = j0; j < njobs; j++) {
-            if (done[j] || dense_lanes<F>(jobs[j].rows, K) != u) continue;
+            if (done[j] || lanes[j] != lanes[j0]) continue;
             done[j] = true;
-            js.job[js.njobs++] = jobs[j];
+            js.job[js.njobs] = jobs[j];
+            js.job[js.njobs++].wide = 0;
             maxcols = jobs[j].ncols > maxcols ? jobs[j].ncols : maxcols;
         }
-        hipError_t e;
-        switch (u) {
-        case 8: e = launch_dense_jobs_u<F, 8>(js, it, maxcols, s); break;
-        case 16: e = launch_dense_jobs_u<F, 16>(js, it, maxcols, s); break;
-        case 32: e = launch_dense_jobs_u<F, 32>(js, it, maxcols, s); break;
-        default: e = launch_dense_jobs_u<F, 64>(js, it, maxcols, s); break;
-        }
+        const hipError_t e = launch(js, lanes[j0], false, maxcols);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -4,7 +4,8 @@ for bit what mmvq_q4k / mmvq_q5k gives for it alone, and within the
 oracle's tolerance on every row.  The shapes take every lanes-per-row class
 (8, 16, 32, 64) and both register depths (three units, and five with a
 ragged and a whole last chunk), batches that mix classes in one call (one
-launch per class), every column count 1-8 in one batch, the long-row
+launch for up to four jobs of the two widths one K can take, one launch
+per width beyond), every column count 1-8 in one batch, the long-row
 matrices whose single products take ten-wave workgroups, the dense
 benchmark's 12288 / 6144 / 512 x 2560 decode step at full size, exact
 arithmetic, and graph replay."""
@@ -61,10 +62,15 @@ def same_bits_as_alone(kind, jobs, got, K):
 
 # (K, [(rows, ncols), ...]) -> lanes per row (depth): K = 256 and 512 8 (3);
 # 1024: 16 below 2048 rows, 8 from there (3); 2560: 32 below 1024 rows, 16
-# from there (3); 5120: 64 below 512 rows, 32 from there (3); 14336: 64 (5,
-# ragged last chunk); 20480: 64 (5, one whole chunk); ragged row counts
+# from there (3); 3584: 32 (3) below 1024 rows, 16 (5) from there; 5120: 64
+# below 512 rows, 32 from there (3); 14336: 64 (5, ragged last chunk);
+# 20480: 64 (5, one whole chunk); ragged row counts.  Up to four jobs of
+# two widths run in one launch; the five-job batch of two widths runs one
+# launch per width.
 SHAPES = [(256, [(37, 3), (100, 8), (1, 1)]), (512, [(19, 5), (64, 2), (33, 7)]),
           (1024, [(300, 4), (2100, 1), (50, 6)]), (2560, [(130, 8), (1100, 4), (16, 1), (1030, 7)]),
+          (2560, [(300, 1), (2000, 2), (310, 3), (1500, 4), (320, 5)]),
+          (3584, [(1200, 2), (200, 5), (1100, 8)]),
           (5120, [(40, 8), (600, 3), (23, 6)]), (14336, [(9, 8), (40, 2), (17, 5)]),
           (20480, [(17, 6), (8, 1)])]
 
@@ -73,7 +79,7 @@ SHAPES = [(256, [(37, 3), (100, 8), (1, 1)]), (512, [(19, 5), (64, 2), (33, 7)])
 @pytest.mark.parametrize("K,shapes", SHAPES)
 def test_q45_batch_equals_single_products_and_oracle(kind, K, shapes):
     note(f"mmvq_{kind}_batch K={K} jobs={shapes}")
-    jobs = make_jobs(kind, 2050 + K, K, shapes)
+    jobs = make_jobs(kind, 2050 + K + len(shapes), K, shapes)
     got = run_batch(kind, jobs, K)
     same_bits_as_alone(kind, jobs, got, K)
     for j, o in zip(jobs, got):
