@@ -58,7 +58,7 @@ COL0 = {8: 0, 4: 8, 1: 12}  # first activation column of each product
 Q6K_BYTES = 210
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20
-BATCH_KERNEL = "k_mmvq_q6_tiled_jobs<4, 1, 5, true>"
+BATCH_KERNEL = "k_mmvq_q6_tiled_jobs<4, 1, 5, true, 4>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 # pages' figures for this matrix (Arc A770, large-GRF launch, 1/4/8 columns):
 # 86.1, 92.9, 370.5 us per call
@@ -544,8 +544,9 @@ def run_extras(torch, np, qmv, synth, dev, copies, base, xd, xq, out):
 def q45_batch_case(torch, qmv, synth, dev, kind, k=2560, shapes=(12288, 6144, 512), ncols_list=(1, 4)):
     """The dense matrices of one K (12288, 6144 and 512 rows x 2560), each on
     its own weights, issued as one batch call (mmvq_q4k_batch /
-    mmvq_q5k_batch: one launch per lanes-per-row class, here two) and as
-    three single calls; sets of weights rotated over HBM copies.  Per step:
+    mmvq_q5k_batch: one launch, the 512-row matrix at twice the lanes per
+    row of the others, as alone) and as three single calls; sets of weights
+    rotated over HBM copies.  Per step:
     device time, weight GB/s, and the plain streaming read of the same
     bytes in one launch."""
     per = {"q4k": 144, "q5k": 176}[kind]
