@@ -100,6 +100,27 @@ def test_batch_decode_step_full_size():
         check_all_rows("q6k", j["w"], j["xq_np"], o, rows, K, f"batch job N={j['n']}")
 
 
+@pytest.mark.parametrize("case", range(6))
+def test_batch_random_batches(case):
+    """Seeded random batches: K a multiple of 256 up to 20480 (every number
+    of waves along K), 1-8 jobs of 1-3000 rows and 1-8 columns each, Q8_1
+    blocks or column-planar activations; every job bit for bit its single
+    launch and within tolerance of the oracle on every row."""
+    g = synth.rng(1995 + case)
+    K = 256 * int(g.integers(1, 81))
+    shapes = [(int(g.integers(1, 3001)), int(g.integers(1, 9))) for _ in range(int(g.integers(1, 9)))]
+    planar_act = bool(case % 2)
+    note(f"mmvq_q6k_batch random K={K} jobs={shapes} column-planar={planar_act}")
+    jobs = make_jobs(2000 + case, K, shapes, planar_act)
+    lay = XT if planar_act else TL
+    got = run_batch(jobs, K, lay)
+    for j, o in zip(jobs, got):
+        alone = mmvq("q6k", j["wt"], j["x"], j["rows"], K, j["n"], lay)
+        assert np.array_equal(o.view(np.uint32), alone.view(np.uint32)), f"job {j['rows']}x{K} N={j['n']}"
+        ref, ab = oracle_all_rows("q6k", j["w"], j["xq_np"], j["rows"], K)
+        assert_close(o, ref, ab, f"job {j['rows']}x{K} N={j['n']}")
+
+
 def test_batch_single_job_and_shared_weights():
     """One job alone; and two jobs on the same weights with different
     columns (a matrix applied to two windows)."""

@@ -127,6 +127,25 @@ def test_q45_batch_decode_step_full_size(kind, n):
 
 
 @pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("case", range(6))
+def test_q45_batch_random_batches(kind, case):
+    """Seeded random batches: K a multiple of 256 up to 8192, 1-8 jobs of
+    1-3000 rows and 1-8 columns each (one or two widths, four or more
+    jobs); every job bit for bit its single launch and within tolerance of
+    the oracle on every row."""
+    g = synth.rng(2120 + case)
+    K = 256 * int(g.integers(1, 33))
+    shapes = [(int(g.integers(1, 3001)), int(g.integers(1, 9))) for _ in range(int(g.integers(1, 9)))]
+    note(f"mmvq_{kind}_batch random K={K} jobs={shapes}")
+    jobs = make_jobs(kind, 2130 + case, K, shapes)
+    got = run_batch(kind, jobs, K)
+    same_bits_as_alone(kind, jobs, got, K)
+    for j, o in zip(jobs, got):
+        ref, ab = oracle_all_rows(kind, j["w"], j["xq_np"], j["rows"], K)
+        assert_close(o, ref, ab, f"job {j['rows']}x{K} N={j['n']}")
+
+
+@pytest.mark.parametrize("kind", KINDS)
 def test_q45_batch_exact_arithmetic_bitexact(kind):
     """Inputs whose every fp32 product and partial sum is exact: each job
     returns the oracle's value exactly."""
