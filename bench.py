@@ -60,6 +60,7 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20
 BATCH_KERNEL = "k_mmvq_q6_tiled_jobs<4, 1, 5, true, 4>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
+SPIN_CYCLES = 1_000_000     # the untimed spin before the timed steps (shader clock: ~0.4 ms)
 # pages' figures for this matrix (Arc A770, large-GRF launch, 1/4/8 columns):
 # 86.1, 92.9, 370.5 us per call
 PAGES_US = {1: 86.1, 4: 92.9, 8: 370.5}
@@ -381,11 +382,19 @@ def main():
     def timed_steps(n):
         run_steps(n)                       # capture and load every graph this count uses
         torch.cuda.synchronize()
+        # device time of the n steps: a bounded spin kernel queued first keeps
+        # the stream busy while the host enqueues the start event and the
+        # graphs, so the events bracket the steps and not the host's
+        # submission latency (one graph launch, ~5 % of 20 steps)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
+        torch.cuda._sleep(SPIN_CYCLES)
         e0.record(stream)
         run_steps(n)
         e1.record(stream)
+        torch.cuda.synchronize()
+        # host wall time of the same n steps from an idle stream
+        t0 = time.perf_counter()
+        run_steps(n)
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         return e0.elapsed_time(e1) / n, (t1 - t0) * 1e3 / n
