@@ -58,7 +58,7 @@ COL0 = {8: 0, 4: 8, 1: 12}  # first activation column of each product
 Q6K_BYTES = 210
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 * 2**20
-BATCH_KERNEL = "k_mmvq_q6_tiled_jobs<4, 1, 5, true, 4>"
+BATCH_KERNEL = "k_mmvq_q6_tiled_jobs_stream<4, 4, 5, 4>"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 SPIN_CYCLES = 1_000_000     # the untimed spin before the timed steps (shader clock: ~0.4 ms)
 # pages' figures for this matrix (Arc A770, large-GRF launch, 1/4/8 columns):

@@ -568,6 +568,148 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
     tiled_workgroup<N, KS, RTW, IT, DUMP, AMAX, XP>(w, a, out, wg, lds);
 }
 
+// Streamed form of a workgroup of column-planar products whose K is one
+// chunk of VKS waves of IT steps (K = 128 * VKS * IT): one wave per 16-row
+// tile takes all VKS * IT steps, with RM * IT steps' weight loads in flight
+// (a ring: step s + RM*IT's loads go out once step s is computed), against
+// one activation tile of the whole K staged once for the workgroup's RTW
+// tiles.  The VKS partial sums -- one per IT consecutive steps, what the VKS
+// waves of the chunked form each add up -- are kept apart and added in wave
+// order, so every output is the chunked form's bits.  No cross-wave sum, a
+// quarter of the activation reads per weight byte at RTW = 4, and a batch's
+// waves (one per row tile) all resident at once rather than in two rounds.
+template <int N, int RTW, int VKS, int IT, int RM = 1>
+__device__ __forceinline__ void tiled_stream_workgroup(const void *__restrict__ w, const MmvqArgs &a,
+                                                       float *__restrict__ out, int64_t wg, uint8_t *lds) {
+    constexpr int ST = VKS * IT;                       // steps of K
+    constexpr int RG = RM * IT;                        // steps in flight (the ring)
+    static_assert(VKS % RM == 0, "whole quarters per ring");
+    using C = TiledCfg<N, 1, RTW, ST, true>;           // staging geometry: one tile of the whole K
+    constexpr int TNB = C::TNB, NCG = C::NCG;
+    static_assert(!C::WT && !C::SCS && TNB == 4 * ST, "one shared tile of the whole K");
+    Q6Tiled f;
+    f.init(w, a.rows, a.K);
+    const int tid = threadIdx.x, l = tid & (kWave - 1);
+    const int rt = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int64_t ntiles = (a.rows + 15) / 16;
+    const int64_t tile = wg * RTW + rt, tc = min(tile, ntiles - 1);
+    const int R = (int)min((int64_t)16, a.rows - 16 * tc);
+    const int r = l & 15, rr = min(r, R - 1), kg = l >> 4;
+    const int64_t row = 16 * tile + r;
+    const bool rok = tile < ntiles && r < R;
+    TiledLane<NCG> tl;
+    tl.R = R;
+    tl.a = plane_rsrc(f.A + 16 * tc * f.nsb, 16 * R * f.nsb);
+    tl.b = plane_rsrc(f.B + 16 * tc * f.nsb, 8 * R * f.nsb);
+    tl.sc = plane_rsrc(f.SC + 16 * tc * (f.nsb / 4), 8 * R * (f.nsb / 4));
+    tl.d = plane_rsrc(f.D + 16 * tc * f.nb, 2 * R * f.nb);
+    tl.oa = 16u * (uint32_t)(kg * R + rr);
+    tl.ob = 8u * (uint32_t)(kg * R + rr);
+    tl.osc = 8u * (uint32_t)rr;
+    tl.od = 2u * (uint32_t)rr;
+    {
+        const bool am = (l & 3) == kg;
+#pragma unroll
+        for (int cg = 0; cg < NCG; cg++) {
+            const int na = min(4 * cg + ((l & 15) >> 2), N - 1);
+            tl.xb[cg] = am ? na * TNB + kg : N * TNB;
+        }
+    }
+
+    // activation loads first: the whole K of the N columns (consecutive),
+    // shared by the workgroup's threads
+    const uint32_t cstride = (uint32_t)(36 * (a.K / 32));
+    const __amdgpu_buffer_rsrc_t xr = plane_rsrc(a.xq, (int64_t)N * cstride);
+    v4u32 xv[C::QSL];
+    v2u32 dv[C::DSL];
+#pragma unroll
+    for (int s = 0; s < C::QSL; s++) {
+        const int i = tid + s * C::SLOTW, ic = min(i, N * C::QU - 1), n = ic / C::QU, j = ic - n * C::QU;
+        xv[s] = __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)n * cstride + 16u * (uint32_t)j, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < C::DSL; s++) {
+        const int i = tid + s * C::SLOTW, ic = min(i, N * C::DU - 1), n = ic / C::DU, k = ic - n * C::DU;
+        dv[s] = __builtin_amdgcn_raw_buffer_load_b64(xr, (uint32_t)n * cstride + (uint32_t)a.K + 8u * (uint32_t)k,
+                                                     0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // the first RG steps' weights (the ring)
+    uint4 wa[RG];
+    uint2 wb[RG], wsc[RG];
+    uint32_t wd[RG];
+    auto load_step = [&](int z, int slot) {
+        const int zr = z * tl.R;                                   // wave-uniform
+        const v2u32 sc = __builtin_amdgcn_raw_buffer_load_b64(tl.sc, tl.osc, 8 * zr, 0);
+        wd[slot] = __builtin_amdgcn_raw_buffer_load_b16(tl.d, tl.od, 2 * ((z >> 1) * tl.R), 0);
+        const v4u32 va = __builtin_amdgcn_raw_buffer_load_b128(tl.a, tl.oa, 64 * zr, kNonTemporal);
+        const v2u32 vb = __builtin_amdgcn_raw_buffer_load_b64(tl.b, tl.ob, 32 * zr, kNonTemporal);
+        wsc[slot] = make_uint2(sc.x, sc.y);
+        wa[slot] = make_uint4(va.x, va.y, va.z, va.w);
+        wb[slot] = make_uint2(vb.x, vb.y);
+    };
+#pragma unroll
+    for (int z = 0; z < RG; z++) {
+        load_step(z, z);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // stage the tile: quant entries (32 B), the zero entries, then d
+    uint4 *x0 = reinterpret_cast<uint4 *>(lds);
+    uint2 *dh = reinterpret_cast<uint2 *>(x0 + 2 * C::XE);
+    if (tid < C::ZW) {
+        x0[2 * (N * TNB + tid)] = make_uint4(0, 0, 0, 0);
+        x0[2 * (N * TNB + tid) + 1] = make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int s = 0; s < C::QSL; s++) {
+        const int i = tid + s * C::SLOTW, n = i / C::QU, j = i - n * C::QU;
+        if (i < N * C::QU) reinterpret_cast<v4u32 *>(x0)[2 * n * TNB + j] = xv[s];
+    }
+#pragma unroll
+    for (int s = 0; s < C::DSL; s++) {
+        const int i = tid + s * C::SLOTW, n = i / C::DU, k = i - n * C::DU;
+        if (i < N * C::DU) reinterpret_cast<v2u32 *>(dh)[n * (TNB / 4) + k] = dv[s];
+    }
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // quarter q (the IT steps one wave of the chunked form takes): its sum
+    // formed alone, then added to those before it in order.  The loop over
+    // quarters stays rolled so that no step's operands are fetched ahead of
+    // its quarter; the last quarter's ring loads (steps past K) fall outside
+    // the tile's buffer ranges and read nothing.
+    float acc[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) acc[cg] = 0.0f;
+#pragma unroll 1
+    for (int q0 = 0; q0 < VKS; q0 += RM) {
+#pragma unroll
+        for (int m = 0; m < RM; m++) {
+            float accq[NCG];
+#pragma unroll
+            for (int cg = 0; cg < NCG; cg++) accq[cg] = 0.0f;
+#pragma unroll
+            for (int it = 0; it < IT; it++) {
+                const int slot = m * IT + it, z = q0 * IT + slot;
+                tiled_step<N, NCG, TNB, ST, false, true>(wa[slot], wb[slot], wsc[slot], wd[slot], tl.xb, z, 4 * z, lds,
+                                                         kg, a, row, rok, z, accq);
+                __builtin_amdgcn_sched_barrier(0);
+                load_step(z + RG, slot);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int cg = 0; cg < NCG; cg++) acc[cg] = q0 + m == 0 ? accq[cg] : acc[cg] + accq[cg];
+        }
+    }
+#pragma unroll
+    for (int cg = 0; cg < NCG; cg++) {
+        const int no = 4 * cg + (l >> 4);
+        if (rok && no < N) out[(int64_t)no * a.rows + row] = acc[cg];
+    }
+}
+
 // Several independent products of the same K in one launch (the matrices of
 // a layer, each with its own activation columns): job j takes workgroups
 // wg0[j] .. wg0[j+1]-1, each one row workgroup of that job's product, with
@@ -629,6 +771,42 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const T
     case 6: tiled_workgroup<6, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
     case 7: tiled_workgroup<7, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
     default: tiled_workgroup<8, KS, RTW, IT, false, false, XP>(jb.w, a, jb.out, wg, lds); break;
+    }
+}
+
+// The jobs kernel in the streamed form (column-planar activations, K one
+// chunk of VKS waves of IT steps): workgroup b takes RTW row tiles of its
+// job, one wave each.
+template <int RTW, int VKS, int IT, int MJ>
+__global__ __launch_bounds__(RTW * kWave) void k_mmvq_q6_tiled_jobs_stream(const TiledJobs<MJ> js) {
+    extern __shared__ __align__(16) uint8_t lds[];
+    const int b = blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < MJ; i++) j = (i < js.njobs && b >= js.job[i].wg0) ? i : j;
+    TiledJob jb = js.job[0];
+#pragma unroll
+    for (int i = 1; i < MJ; i++)
+        if (j == i) jb = js.job[i];
+    MmvqArgs a;
+    a.xq = jb.xq;
+    a.dump = nullptr;
+    a.rows = jb.rows;
+    a.K = js.K;
+    a.colpack = 0x0706050403020100ull;
+    a.xstride = js.K / 32;
+    a.its = IT;
+    a.nout = jb.ncols;
+    const int64_t wg = b - jb.wg0;
+    switch (jb.ncols) {
+    case 1: tiled_stream_workgroup<1, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 2: tiled_stream_workgroup<2, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 3: tiled_stream_workgroup<3, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 4: tiled_stream_workgroup<4, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 5: tiled_stream_workgroup<5, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 6: tiled_stream_workgroup<6, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 7: tiled_stream_workgroup<7, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    default: tiled_stream_workgroup<8, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
     }
 }
 
@@ -761,9 +939,48 @@ hipError_t launch_tiled_jobs_cfg(const TiledJobs<kMaxTiledJobs> &js, hipStream_t
     return launch_tiled_jobs_mj<KS, RTW, IT, XP, kMaxTiledJobs>(js, s);
 }
 
+// Row tiles (waves) per workgroup of the streamed form.  Three 10240x2560
+// products (8, 4, 1 columns), per launch: 12.30 us at four tiles, 13.43 at
+// two, 12.52 at eight; a ring of ten steps (RM = 2) 13.50.
+constexpr int kStreamRtw = 4;
+
+template <int VKS, int IT, int MJ>
+hipError_t launch_tiled_jobs_stream_mj(const TiledJobs<kMaxTiledJobs> &all, hipStream_t s) {
+    constexpr int NTHR = kStreamRtw * kWave;
+    TiledJobs<MJ> js;
+    js.K = all.K;
+    js.njobs = all.njobs;
+    int64_t wg = 0;
+    for (int j = 0; j < js.njobs; j++) {
+        js.job[j] = all.job[j];
+        js.job[j].wg0 = (int32_t)wg;
+        wg += ((js.job[j].rows + 15) / 16 + kStreamRtw - 1) / kStreamRtw;
+    }
+    for (int j = js.njobs; j < MJ; j++) js.job[j] = js.job[0];
+    if (wg * NTHR > 0xFFFFFFFFLL) return hipErrorInvalidConfiguration;
+    size_t lds = 0;
+    const size_t v[8] = {TiledCfg<1, 1, kStreamRtw, VKS * IT, true>::LDS, TiledCfg<2, 1, kStreamRtw, VKS * IT, true>::LDS,
+                         TiledCfg<3, 1, kStreamRtw, VKS * IT, true>::LDS, TiledCfg<4, 1, kStreamRtw, VKS * IT, true>::LDS,
+                         TiledCfg<5, 1, kStreamRtw, VKS * IT, true>::LDS, TiledCfg<6, 1, kStreamRtw, VKS * IT, true>::LDS,
+                         TiledCfg<7, 1, kStreamRtw, VKS * IT, true>::LDS, TiledCfg<8, 1, kStreamRtw, VKS * IT, true>::LDS};
+    for (size_t x : v) lds = x > lds ? x : lds;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(&k_mmvq_q6_tiled_jobs_stream<kStreamRtw, VKS, IT, MJ>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_mmvq_q6_tiled_jobs_stream<kStreamRtw, VKS, IT, MJ>), dim3((unsigned)wg), dim3(NTHR), lds, s,
+                       js);
+    return hipGetLastError();
+}
+
 template <bool XP>
 hipError_t launch_tiled_jobs(const TiledJobs<kMaxTiledJobs> &js, hipStream_t s) {
     const int64_t need = (js.K / 128 + 4) / 5;
+    // column-planar jobs whose K is exactly one chunk of four waves of five
+    // steps (K = 2560): the streamed form, the same bits
+    if constexpr (XP) {
+        if (js.K == 4 * 5 * 128)
+            return js.njobs <= 4 ? launch_tiled_jobs_stream_mj<4, 5, 4>(js, s)
+                                 : launch_tiled_jobs_stream_mj<4, 5, kMaxTiledJobs>(js, s);
+    }
     if (need <= 1) return launch_tiled_jobs_cfg<1, 4, 5, XP>(js, s);
     if (need <= 2) return launch_tiled_jobs_cfg<2, 2, 5, XP>(js, s);
     if (need <= 4) return launch_tiled_jobs_cfg<4, 1, 5, XP>(js, s);
