@@ -974,12 +974,18 @@ hipError_t launch_tiled_jobs_stream_mj(const TiledJobs<kMaxTiledJobs> &all, hipS
 template <bool XP>
 hipError_t launch_tiled_jobs(const TiledJobs<kMaxTiledJobs> &js, hipStream_t s) {
     const int64_t need = (js.K / 128 + 4) / 5;
-    // column-planar jobs whose K is exactly one chunk of four waves of five
-    // steps (K = 2560): the streamed form, the same bits
+    // column-planar jobs whose K is exactly one chunk of four or eight waves
+    // of five steps (K = 2560, 5120): the streamed form, the same bits.
+    // Three products of 8, 4 and 1 columns, per launch: 10240x2560 12.75 ->
+    // 12.30 us, 5120x5120 13.34 -> 12.95 us; at K = 1280 (two waves) the
+    // streamed form was slower (10240 rows: 7.65 -> 7.90 us), so not there.
     if constexpr (XP) {
         if (js.K == 4 * 5 * 128)
             return js.njobs <= 4 ? launch_tiled_jobs_stream_mj<4, 5, 4>(js, s)
                                  : launch_tiled_jobs_stream_mj<4, 5, kMaxTiledJobs>(js, s);
+        if (js.K == 8 * 5 * 128)
+            return js.njobs <= 4 ? launch_tiled_jobs_stream_mj<8, 5, 4>(js, s)
+                                 : launch_tiled_jobs_stream_mj<8, 5, kMaxTiledJobs>(js, s);
     }
     if (need <= 1) return launch_tiled_jobs_cfg<1, 4, 5, XP>(js, s);
     if (need <= 2) return launch_tiled_jobs_cfg<2, 2, 5, XP>(js, s);

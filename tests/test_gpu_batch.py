@@ -100,6 +100,24 @@ def test_batch_decode_step_full_size():
         check_all_rows("q6k", j["w"], j["xq_np"], o, rows, K, f"batch job N={j['n']}")
 
 
+@pytest.mark.parametrize("K,shapes", [(2560, [(100, 8), (17, 1), (300, 4), (64, 7), (5, 2), (1000, 3)]),
+                                      (5120, [(3000, 8), (3000, 4), (3000, 1)]),
+                                      (5120, [(90, 8), (17, 1), (300, 4), (64, 7), (5, 2), (777, 3)])])
+def test_batch_streamed_form(K, shapes):
+    """Column-planar jobs at K = 2560 and 5120 take the streamed form (one
+    wave per row tile over all of K; four-entry job table up to four jobs,
+    eight beyond): every job bit for bit its single product and within s6 of
+    the oracle on every row."""
+    note(f"mmvq_q6k_batch streamed K={K} jobs={shapes}")
+    jobs = make_jobs(2010 + K // 256 + len(shapes), K, shapes, True)
+    got = run_batch(jobs, K, XT)
+    for j, o in zip(jobs, got):
+        alone = mmvq("q6k", j["wt"], j["x"], j["rows"], K, j["n"], XT)
+        assert np.array_equal(o.view(np.uint32), alone.view(np.uint32)), f"job {j['rows']}x{K} N={j['n']}"
+        ref, ab = oracle_all_rows("q6k", j["w"], j["xq_np"], j["rows"], K)
+        assert_close(o, ref, ab, f"job {j['rows']}x{K} N={j['n']}")
+
+
 @pytest.mark.parametrize("case", range(6))
 def test_batch_random_batches(case):
     """Seeded random batches: K a multiple of 256 up to 20480 (every number
