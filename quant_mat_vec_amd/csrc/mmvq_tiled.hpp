@@ -570,20 +570,19 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled(const void *
 
 // Streamed form of a workgroup of column-planar products whose K is one
 // chunk of VKS waves of IT steps (K = 128 * VKS * IT): one wave per 16-row
-// tile takes all VKS * IT steps, with RM * IT steps' weight loads in flight
-// (a ring: step s + RM*IT's loads go out once step s is computed), against
-// one activation tile of the whole K staged once for the workgroup's RTW
-// tiles.  The VKS partial sums -- one per IT consecutive steps, what the VKS
-// waves of the chunked form each add up -- are kept apart and added in wave
+// tile takes all VKS * IT steps, with RG steps' weight loads in flight (a
+// ring: step s + RG's loads go out once step s is computed), against one
+// activation tile of the whole K staged once for the workgroup's RTW tiles.
+// The VKS partial sums -- one per IT consecutive steps, what the VKS waves
+// of the chunked form each add up -- are kept apart and added in wave
 // order, so every output is the chunked form's bits.  No cross-wave sum, a
 // quarter of the activation reads per weight byte at RTW = 4, and a batch's
 // waves (one per row tile) all resident at once rather than in two rounds.
-template <int N, int RTW, int VKS, int IT, int RM = 1>
+template <int N, int RTW, int VKS, int IT, int RG>
 __device__ __forceinline__ void tiled_stream_workgroup(const void *__restrict__ w, const MmvqArgs &a,
                                                        float *__restrict__ out, int64_t wg, uint8_t *lds) {
     constexpr int ST = VKS * IT;                       // steps of K
-    constexpr int RG = RM * IT;                        // steps in flight (the ring)
-    static_assert(VKS % RM == 0, "whole quarters per ring");
+    static_assert(RG >= 1 && RG <= ST, "ring of at most the steps of K");
     using C = TiledCfg<N, 1, RTW, ST, true>;           // staging geometry: one tile of the whole K
     constexpr int TNB = C::TNB, NCG = C::NCG;
     static_assert(!C::WT && !C::SCS && TNB == 4 * ST, "one shared tile of the whole K");
@@ -675,32 +674,38 @@ __device__ __forceinline__ void tiled_stream_workgroup(const void *__restrict__ 
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
 
-    // quarter q (the IT steps one wave of the chunked form takes): its sum
-    // formed alone, then added to those before it in order.  The loop over
-    // quarters stays rolled so that no step's operands are fetched ahead of
-    // its quarter; the last quarter's ring loads (steps past K) fall outside
-    // the tile's buffer ranges and read nothing.
-    float acc[NCG];
+    // The steps in order, unrolled (ring slot z % RG).  Quarter q (the IT
+    // steps one wave of the chunked form takes) has its sum formed alone,
+    // then added to those before it in order.  Two empty asm statements
+    // per step keep the code in step order: the step index reaches the LDS
+    // addresses through one (so no later step's activation operands are
+    // fetched ahead), and the quarter's sum passes through the other once
+    // the step is added (so its scale arithmetic is not deferred, holding
+    // every step's matrix-core results).  Unrolled without them the kernel
+    // took 256 VGPRs.  (A rolled loop over quarters with a ring of one
+    // quarter, five steps, measured 0.6-0.8 us slower per batched launch.)
+    float acc[NCG], accq[NCG];
 #pragma unroll
     for (int cg = 0; cg < NCG; cg++) acc[cg] = 0.0f;
-#pragma unroll 1
-    for (int q0 = 0; q0 < VKS; q0 += RM) {
 #pragma unroll
-        for (int m = 0; m < RM; m++) {
-            float accq[NCG];
+    for (int z = 0; z < ST; z++) {
+        if (z % IT == 0) {
 #pragma unroll
             for (int cg = 0; cg < NCG; cg++) accq[cg] = 0.0f;
+        }
+        const int slot = z % RG;
+        int zs = z;
+        asm volatile("" : "+s"(zs));
+        tiled_step<N, NCG, TNB, ST, false, true>(wa[slot], wb[slot], wsc[slot], wd[slot], tl.xb, zs, 4 * zs, lds, kg,
+                                                 a, row, rok, z, accq);
 #pragma unroll
-            for (int it = 0; it < IT; it++) {
-                const int slot = m * IT + it, z = q0 * IT + slot;
-                tiled_step<N, NCG, TNB, ST, false, true>(wa[slot], wb[slot], wsc[slot], wd[slot], tl.xb, z, 4 * z, lds,
-                                                         kg, a, row, rok, z, accq);
-                __builtin_amdgcn_sched_barrier(0);
-                load_step(z + RG, slot);
-                __builtin_amdgcn_sched_barrier(0);
-            }
+        for (int cg = 0; cg < NCG; cg++) asm volatile("" : "+v"(accq[cg]));
+        __builtin_amdgcn_sched_barrier(0);
+        if (z + RG < ST) load_step(z + RG, slot);
+        __builtin_amdgcn_sched_barrier(0);
+        if (z % IT == IT - 1) {
 #pragma unroll
-            for (int cg = 0; cg < NCG; cg++) acc[cg] = q0 + m == 0 ? accq[cg] : acc[cg] + accq[cg];
+            for (int cg = 0; cg < NCG; cg++) acc[cg] = z < IT ? accq[cg] : acc[cg] + accq[cg];
         }
     }
 #pragma unroll
@@ -774,6 +779,15 @@ __global__ __launch_bounds__(KS * RTW * kWave) void k_mmvq_q6_tiled_jobs(const T
     }
 }
 
+// Steps in flight per wave of the streamed form (its ring).  Three
+// 10240x2560 products (8, 4, 1 columns), per batched launch in one run:
+// 12.80 / 12.71 us at a ring of two, 12.33 / 12.46 at three, 12.23 / 12.26
+// at four, 12.58 / 12.28 at five, 12.55 / 12.62 at six, 12.72 / 12.78 at
+// seven; a deeper ring (ten) and whole quarters refilled at once were slower
+// still.  Three 5120x5120 products: 13.10 -> 12.76 us against the rolled
+// ring of five.
+constexpr int kStreamRing = 4;
+
 // The jobs kernel in the streamed form (column-planar activations, K one
 // chunk of VKS waves of IT steps): workgroup b takes RTW row tiles of its
 // job, one wave each.
@@ -799,14 +813,14 @@ __global__ __launch_bounds__(RTW * kWave) void k_mmvq_q6_tiled_jobs_stream(const
     a.nout = jb.ncols;
     const int64_t wg = b - jb.wg0;
     switch (jb.ncols) {
-    case 1: tiled_stream_workgroup<1, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    case 2: tiled_stream_workgroup<2, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    case 3: tiled_stream_workgroup<3, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    case 4: tiled_stream_workgroup<4, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    case 5: tiled_stream_workgroup<5, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    case 6: tiled_stream_workgroup<6, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    case 7: tiled_stream_workgroup<7, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
-    default: tiled_stream_workgroup<8, RTW, VKS, IT>(jb.w, a, jb.out, wg, lds); break;
+    case 1: tiled_stream_workgroup<1, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    case 2: tiled_stream_workgroup<2, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    case 3: tiled_stream_workgroup<3, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    case 4: tiled_stream_workgroup<4, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    case 5: tiled_stream_workgroup<5, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    case 6: tiled_stream_workgroup<6, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    case 7: tiled_stream_workgroup<7, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
+    default: tiled_stream_workgroup<8, RTW, VKS, IT, kStreamRing>(jb.w, a, jb.out, wg, lds); break;
     }
 }
 
@@ -940,8 +954,8 @@ hipError_t launch_tiled_jobs_cfg(const TiledJobs<kMaxTiledJobs> &js, hipStream_t
 }
 
 // Row tiles (waves) per workgroup of the streamed form.  Three 10240x2560
-// products (8, 4, 1 columns), per launch: 12.30 us at four tiles, 13.43 at
-// two, 12.52 at eight; a ring of ten steps (RM = 2) 13.50.
+// products (8, 4, 1 columns), per launch (with a rolled ring of five steps):
+// 12.30 us at four tiles, 13.43 at two, 12.52 at eight.
 constexpr int kStreamRtw = 4;
 
 template <int VKS, int IT, int MJ>
@@ -976,9 +990,10 @@ hipError_t launch_tiled_jobs(const TiledJobs<kMaxTiledJobs> &js, hipStream_t s) 
     const int64_t need = (js.K / 128 + 4) / 5;
     // column-planar jobs whose K is exactly one chunk of four or eight waves
     // of five steps (K = 2560, 5120): the streamed form, the same bits.
-    // Three products of 8, 4 and 1 columns, per launch: 10240x2560 12.75 ->
-    // 12.30 us, 5120x5120 13.34 -> 12.95 us; at K = 1280 (two waves) the
-    // streamed form was slower (10240 rows: 7.65 -> 7.90 us), so not there.
+    // Three products of 8, 4 and 1 columns, per launch (its first, rolled
+    // ring of five): 10240x2560 12.75 -> 12.30 us, 5120x5120 13.34 -> 12.95
+    // us; at K = 1280 (two waves) the streamed form was slower (10240 rows:
+    // 7.65 -> 7.90 us), so not there.
     if constexpr (XP) {
         if (js.K == 4 * 5 * 128)
             return js.njobs <= 4 ? launch_tiled_jobs_stream_mj<4, 5, 4>(js, s)
