@@ -36,8 +36,10 @@ typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
 // Cache-policy bit of a buffer load: non-temporal.  The code planes are read
 // once per product, so they are streamed past the caches (measured ~0.1 us
 // faster per launch at eight columns than the default policy); the scales
-// and d keep the default.  (The batched product, which reads each row
-// tile's planes once per batch, measured the same with the default policy.)
+// and d keep the default.  (The batched product in its chunked form
+// measured the same with the default policy; in the streamed form, three
+// 10240x2560 products, the default policy took 13.46-13.69 against
+// 12.23-12.56 us per launch.)
 constexpr int kNonTemporal = 2;
 
 // Buffer resource for `bytes` bytes at `base` (raw, unformatted dword
@@ -954,8 +956,10 @@ hipError_t launch_tiled_jobs_cfg(const TiledJobs<kMaxTiledJobs> &js, hipStream_t
 }
 
 // Row tiles (waves) per workgroup of the streamed form.  Three 10240x2560
-// products (8, 4, 1 columns), per launch (with a rolled ring of five steps):
-// 12.30 us at four tiles, 13.43 at two, 12.52 at eight.
+// products (8, 4, 1 columns), per launch: with a rolled ring of five steps
+// 12.30 us at four tiles, 13.43 at two, 12.52 at eight; with the unrolled
+// ring of four (graph replays of 27 launches, two runs) 12.23-12.56 at
+// four, 14.07-14.14 at two, 12.72-13.17 at eight.
 constexpr int kStreamRtw = 4;
 
 template <int VKS, int IT, int MJ>
