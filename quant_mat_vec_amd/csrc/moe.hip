@@ -343,6 +343,8 @@ template <int UN, int RPL>
 __global__ __launch_bounds__(8 * kWave) void k_moe_down_tok(MoeArgs m) {
     constexpr int ROWS = 8 * RPL;
     __shared__ float ylds[8][ROWS];
+    __shared__ float wlds[8];                                // route weight of each slot
+    __shared__ int vlds[8];                                  // whether its id is in range
     const int nsb = 8 * UN;                                  // d_ff / 32
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x & (kWave - 1);
     const int r = lane >> 3, u = lane & 7;
@@ -353,7 +355,13 @@ __global__ __launch_bounds__(8 * kWave) void k_moe_down_tok(MoeArgs m) {
 #pragma unroll
     for (int k = 0; k < UN; k++) act_load(x[k], hq, (int64_t)slot * nsb + u + 8 * k);
     const int e = m.ids[slot];
-    if (e >= 0 && e < m.E) {
+    const float rw = m.route_w[slot];
+    const bool ev = e >= 0 && e < m.E;
+    if (lane == 0) {
+        wlds[wave] = rw;
+        vlds[wave] = ev ? 1 : 0;
+    }
+    if (ev) {
         // sub-blocks u + 8k of a row: with 8 * UN sub-blocks a row,
         // sub-block u + 8k lies in the row's superblock k
         Q6Planar fmt;
@@ -404,13 +412,15 @@ __global__ __launch_bounds__(8 * kWave) void k_moe_down_tok(MoeArgs m) {
         }
     }
     lds_barrier();
+    // the routed sum from LDS only: each wave put its slot's route weight
+    // and id check there with its y (reading the ids and weights here, a
+    // chain of dependent global loads after the barrier, cost 0.1-0.25 us
+    // per call at T = 1..8)
     if (threadIdx.x < ROWS) {
         const int rr = threadIdx.x;
         float acc = 0.0f;
-        for (int k = 0; k < m.topk; k++) {
-            const int sl = tk * m.topk + k, ek = m.ids[sl];
-            if (ek >= 0 && ek < m.E) acc = __builtin_fmaf(m.route_w[sl], ylds[k][rr], acc);
-        }
+        for (int k = 0; k < m.topk; k++)
+            if (vlds[k]) acc = __builtin_fmaf(wlds[k], ylds[k][rr], acc);
         m.out[(int64_t)tk * m.d_model + row0 + rr] = acc;
     }
 }
