@@ -72,43 +72,65 @@ hipError_t launch_quantize(const float *x, uint8_t *xq, int64_t K, int ncols, bo
     return hipGetLastError();
 }
 
-// Fused RMSNorm -> Q8_1: one workgroup per column.  Pass 1 sums x^2 (fp32,
-// fixed order: each thread's float4s in sequence, a 64-lane butterfly, the
-// four waves in order, so every thread holds the same sum); r =
-// 1/sqrt(sum/K + eps) (IEEE division and square root); pass 2 forms
-// y = (x*r)*gamma and quantizes it with the arithmetic of k_quantize_q8_1
-// (eight lanes per block), in the Q8_1 blocks or the column-planar layout.
-// One read of x for the sum, one (from L2) for the codes; no intermediate
-// y in memory and one launch instead of a norm pass plus a quantize pass.
+// Fused RMSNorm -> Q8_1: one 1024-thread workgroup per column.  Pass 1
+// sums x^2 (fp32, fixed order: each thread's float4s in sequence, a 64-lane
+// butterfly, the sixteen waves in order, so every thread holds the same
+// sum); r = 1/sqrt(sum/K + eps) (IEEE division and square root); pass 2
+// forms y = (x*r)*gamma and quantizes it with the arithmetic of
+// k_quantize_q8_1 (eight lanes per block), in the Q8_1 blocks or the
+// column-planar layout.  Up to K = 4096 thread t's one float4 of pass 1 is
+// the one it quantizes in pass 2 (float4 8b + i is lane i of block b), so
+// x is read once and each pass is one step; longer columns loop and read x
+// again (from L2) for the codes.  (256 threads, three steps per pass at
+// K = 2560: 3.6 us per launch of 13 columns; this form 2.9 us.)  No
+// intermediate y in memory and one launch instead of a norm pass plus a
+// quantize pass.
+constexpr int kNormThreads = 1024;
+
 template <bool PLANAR>
-__global__ __launch_bounds__(256) void k_rmsnorm_q8_1(const float *__restrict__ x, const float *__restrict__ gamma,
-                                                      float eps, uint8_t *__restrict__ xq, int64_t K) {
-    __shared__ float part[4];
-    const int64_t col = blockIdx.x, nb = K / 32;
+__global__ __launch_bounds__(kNormThreads) void k_rmsnorm_q8_1(const float *__restrict__ x,
+                                                               const float *__restrict__ gamma, float eps,
+                                                               uint8_t *__restrict__ xq, int64_t K) {
+    __shared__ float part[kNormThreads / kWave];
+    const int64_t col = blockIdx.x, nb = K / 32, n4 = K / 4;
     const float *xc = x + col * K;
     const int tid = threadIdx.x, lane = tid & 63;
+    const bool held = n4 <= kNormThreads;
+    float4 xh = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float ss = 0.0f;
-    for (int64_t i = tid; i < K / 4; i += 256) {
-        const float4 v = reinterpret_cast<const float4 *>(xc)[i];
-        ss = __builtin_fmaf(v.x, v.x, ss);
-        ss = __builtin_fmaf(v.y, v.y, ss);
-        ss = __builtin_fmaf(v.z, v.z, ss);
-        ss = __builtin_fmaf(v.w, v.w, ss);
+    if (held) {
+        if (tid < n4) {
+            xh = reinterpret_cast<const float4 *>(xc)[tid];
+            ss = __builtin_fmaf(xh.x, xh.x, ss);
+            ss = __builtin_fmaf(xh.y, xh.y, ss);
+            ss = __builtin_fmaf(xh.z, xh.z, ss);
+            ss = __builtin_fmaf(xh.w, xh.w, ss);
+        }
+    } else {
+        for (int64_t i = tid; i < n4; i += kNormThreads) {
+            const float4 v = reinterpret_cast<const float4 *>(xc)[i];
+            ss = __builtin_fmaf(v.x, v.x, ss);
+            ss = __builtin_fmaf(v.y, v.y, ss);
+            ss = __builtin_fmaf(v.z, v.z, ss);
+            ss = __builtin_fmaf(v.w, v.w, ss);
+        }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
     if (lane == 0) part[tid >> 6] = ss;
     __syncthreads();
-    ss = ((part[0] + part[1]) + part[2]) + part[3];
+    ss = part[0];
+#pragma unroll
+    for (int w = 1; w < kNormThreads / kWave; w++) ss += part[w];
     const float r = 1.0f / sqrtf(ss / (float)K + eps);
     uint8_t *c = xq + col * nb * kQ81Bytes;
     const int i = tid & 7;
-    for (int64_t b0 = 0; b0 < nb; b0 += 32) {
+    for (int64_t b0 = 0; b0 < nb; b0 += kNormThreads / 8) {
         const int64_t b = b0 + (tid >> 3);
         const bool ok = b < nb;
         float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
         if (ok) {
-            const float4 xv = reinterpret_cast<const float4 *>(xc + 32 * b)[i];
+            const float4 xv = held ? xh : reinterpret_cast<const float4 *>(xc + 32 * b)[i];
             const float4 gv = reinterpret_cast<const float4 *>(gamma + 32 * b)[i];
             v[0] = (xv.x * r) * gv.x;
             v[1] = (xv.y * r) * gv.y;
@@ -152,9 +174,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_q8_1(const float *__restrict__ 
 hipError_t launch_rmsnorm_quantize(const float *x, const float *gamma, float eps, uint8_t *xq, int64_t K, int ncols,
                                    bool planar, hipStream_t s) {
     if (planar)
-        hipLaunchKernelGGL(k_rmsnorm_q8_1<true>, dim3((unsigned)ncols), dim3(256), 0, s, x, gamma, eps, xq, K);
+        hipLaunchKernelGGL(k_rmsnorm_q8_1<true>, dim3((unsigned)ncols), dim3(kNormThreads), 0, s, x, gamma, eps, xq,
+                           K);
     else
-        hipLaunchKernelGGL(k_rmsnorm_q8_1<false>, dim3((unsigned)ncols), dim3(256), 0, s, x, gamma, eps, xq, K);
+        hipLaunchKernelGGL(k_rmsnorm_q8_1<false>, dim3((unsigned)ncols), dim3(kNormThreads), 0, s, x, gamma, eps, xq,
+                           K);
     return hipGetLastError();
 }
 
