@@ -24,6 +24,8 @@ namespace qmv {
 namespace {
 
 constexpr int kTopkThreads = 256;
+constexpr int kTopkPer = kTopkChunk / kTopkThreads;     // keys per thread of a full chunk
+static_assert(kTopkChunk % kTopkThreads == 0, "whole loads per thread");
 
 __device__ __forceinline__ uint64_t topk_key(float v, uint32_t row) {
     uint32_t b = __float_as_uint(v + 0.0f);
@@ -101,7 +103,18 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_chunks(const float *__res
     const float *o = out + (int64_t)n * rows;
     const int64_t r0 = (int64_t)c * kTopkChunk;
     const int m = (int)(rows - r0 < kTopkChunk ? rows - r0 : kTopkChunk);
-    for (int i = threadIdx.x; i < m; i += kTopkThreads) s.key[i] = topk_key(o[r0 + i], (uint32_t)(r0 + i));
+    // every load of the thread in flight before the first key is stored:
+    // unconditional loads from indices clamped into the chunk (a load per
+    // key stored as it arrived, or a branch around each load, waited for
+    // each in turn: ~13 us for the 38 chunks of a 151,936-row column)
+    float v[kTopkPer];
+#pragma unroll
+    for (int j = 0; j < kTopkPer; j++) v[j] = o[r0 + min((int)threadIdx.x + j * kTopkThreads, m - 1)];
+#pragma unroll
+    for (int j = 0; j < kTopkPer; j++) {
+        const int i = threadIdx.x + j * kTopkThreads;
+        if (i < m) s.key[i] = topk_key(v[j], (uint32_t)(r0 + i));
+    }
     __syncthreads();
     const int need = m < k ? m : k;
     select_largest(s, m, need);
@@ -114,8 +127,15 @@ __global__ __launch_bounds__(kTopkThreads) void k_topk_chunks(const float *__res
 __global__ __launch_bounds__(kTopkThreads) void k_topk_final(const uint64_t *__restrict__ cand, int k, int nchunks,
                                                              int32_t *__restrict__ idx, float *__restrict__ val) {
     __shared__ SelectLds s;
-    const int n = blockIdx.x, m = nchunks * k;
-    for (int i = threadIdx.x; i < m; i += kTopkThreads) s.key[i] = cand[(int64_t)n * m + i];
+    const int n = blockIdx.x, m = nchunks * k;          // 1 <= m <= kTopkChunk (checked by the caller)
+    uint64_t v[kTopkPer];
+#pragma unroll
+    for (int j = 0; j < kTopkPer; j++) v[j] = cand[(int64_t)n * m + min((int)threadIdx.x + j * kTopkThreads, m - 1)];
+#pragma unroll
+    for (int j = 0; j < kTopkPer; j++) {
+        const int i = threadIdx.x + j * kTopkThreads;
+        if (i < m) s.key[i] = v[j];
+    }
     __syncthreads();
     select_largest(s, m, k);
     const int t = threadIdx.x;
