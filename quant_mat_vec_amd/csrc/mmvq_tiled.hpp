@@ -841,11 +841,14 @@ __global__ __launch_bounds__(kArgmaxThreads) void k_argmax_reduce(uint64_t *__re
     const int n = blockIdx.x, t = threadIdx.x;
     const uint64_t *kc = keys + (int64_t)n * ntiles;
     const int64_t base = (int64_t)blockIdx.y * kArgmaxSpan;
+    // unconditional loads from indices clamped to the last key, all in
+    // flight at once (a conditional load each waited for the one before; a
+    // repeated key does not change the maximum)
     uint64_t v[kArgmaxLoads];
 #pragma unroll
     for (int u = 0; u < kArgmaxLoads; u++) {
         const int64_t i = base + (int64_t)u * kArgmaxThreads + t;
-        v[u] = i < ntiles ? kc[i] : 0;
+        v[u] = kc[i < ntiles ? i : ntiles - 1];
     }
     uint64_t k = 0;
 #pragma unroll
