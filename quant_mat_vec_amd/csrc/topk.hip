@@ -49,9 +49,16 @@ __device__ void select_largest(SelectLds &s, int m, int need) {
     for (int shift = 56; shift >= 0; shift -= 8) {
         s.hist[t] = 0;                                    // kTopkThreads == 256 bins
         __syncthreads();
-        for (int i = t; i < m; i += kTopkThreads) {
-            const uint64_t key = s.key[i];
-            if (key != 0 && (key & mask) == prefix) atomicAdd(&s.hist[(int)(key >> shift) & 255], 1);
+        // every LDS read of the pass issued before the first count (the
+        // array holds kTopkChunk keys; entries from m on are not counted)
+        uint64_t kv[kTopkPer];
+#pragma unroll
+        for (int j = 0; j < kTopkPer; j++) kv[j] = s.key[t + j * kTopkThreads];
+#pragma unroll
+        for (int j = 0; j < kTopkPer; j++) {
+            const uint64_t key = kv[j];
+            if (t + j * kTopkThreads < m && key != 0 && (key & mask) == prefix)
+                atomicAdd(&s.hist[(int)(key >> shift) & 255], 1);
         }
         __syncthreads();
         if (t < 64) {                                     // wave 0: bins 4t .. 4t+3, suffix sums over lanes
@@ -87,9 +94,13 @@ __device__ void select_largest(SelectLds &s, int m, int need) {
     }
     if (t == 0) s.nsel = 0;
     __syncthreads();
-    for (int i = t; i < m; i += kTopkThreads) {
-        const uint64_t key = s.key[i];
-        if (key != 0 && (key & mask) >= prefix) s.sel[atomicAdd(&s.nsel, 1)] = key;
+    uint64_t kv[kTopkPer];
+#pragma unroll
+    for (int j = 0; j < kTopkPer; j++) kv[j] = s.key[t + j * kTopkThreads];
+#pragma unroll
+    for (int j = 0; j < kTopkPer; j++) {
+        const uint64_t key = kv[j];
+        if (t + j * kTopkThreads < m && key != 0 && (key & mask) >= prefix) s.sel[atomicAdd(&s.nsel, 1)] = key;
     }
     __syncthreads();
 }
